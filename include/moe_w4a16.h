@@ -1,0 +1,275 @@
+/*
+ * moe_w4a16.h -- C ABI of the MI355X (gfx950) W4A16 routed-expert MoE library.
+ *
+ * One MoE layer (or a residual stack of them) executed from INT4 expert
+ * weights with FP16 group scales and FP16 activations:
+ *   router logits -> softmax + top-k -> group tokens by expert ->
+ *   gate/up projection + SwiGLU -> down projection -> weighted combine,
+ * plus an optional per-layer HBM expert-slot pool for partial residency,
+ * backed by an immutable pinned host copy of every expert.
+ *
+ * Sources (web pages):
+ *   "Horizon RunMap - Architecture, Results and Public Evaluation":
+ *     "Architecture invariants" (routed experts kept as INT4 with FP16 scales,
+ *     FP16 activations), "What is implemented" (weights stay compact on the
+ *     GPU), "The complete execution path" (route, then custom W4A16 kernels;
+ *     full or partial residency), "Partial-residency contract: immutable
+ *     authority and miss lifecycle" (immutable host source, H2D-only misses,
+ *     publication after complete transfer, discard eviction, capacity fixed
+ *     before admission, failure semantics).
+ *   "An expert-offloading engine, from scratch": LRU / LFU expert caches,
+ *     one contiguous blob per expert, caching never changes the output.
+ *   "F51 Nitro / Nitro-MoE", "Layer 1 - expert persistence cache": slot maps,
+ *     per-slot frequency and last-use counters, score freq*1000 - age, decay
+ *     0.75 every 2x capacity misses, ensure() = lookup, evict, H2D, slot.
+ *
+ * Conventions for every call:
+ *   - Pointers named "dev" are device (HBM) addresses on the context's device;
+ *     "host" pointers are ordinary CPU memory.  The caller owns every buffer
+ *     and stream it passes; the library owns weights, slot pools, the pinned
+ *     backing, its scratch memory, its side stream and its events.
+ *   - Compute calls are stream-ordered on the caller's `stream`
+ *     (a hipStream_t, NULL = the null stream) and return before the GPU
+ *     finishes.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failing call enqueues nothing and returns a status != MOE_OK, with text
+ *     in moe_last_error().  No exception crosses the ABI.
+ *   - Data-dependent problems found on the GPU (an expert id out of range or
+ *     repeated within a token, an expert that is not resident in the slot
+ *     pool) never cause an out-of-bounds access: the kernel substitutes a
+ *     valid id or slot, computes a meaningless result for that token and
+ *     sets a bit in a device error word, read by moe_check_device_errors().
+ *   - One host thread per context.  Calls on one context are not thread-safe.
+ *
+ * Tensor layouts (all row-major, no padding):
+ *   x     FP16  [T, H]          activations of the T tokens of a call
+ *   ids   int32 [T, k]          selected experts of each token, rank order
+ *   w     FP32  [T, k]          combine weights, same order as ids
+ *   out   FP16  [T, H]          layer output
+ *   h     FP32  [T, H]          residual stream of a stack
+ *   q     uint8 [E][3][I*H/2]   packed INT4 codes of gate [I,H], up [I,H],
+ *                               down [H,I]; row-major, element 2j of a row in
+ *                               the low nibble of byte j, 2j+1 in the high one
+ *   s     FP16  [E][3][I*H/128] scales: gate/up [I, H/128], down [H, I/128];
+ *                               W[n,k] = (q[n,k] - 8) * s[n, k/128]
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_ctx moe_ctx; /* opaque, library-owned */
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_E_ARG = 1,            /* bad pointer, index or size                      */
+  MOE_E_SHAPE = 2,          /* unsupported shape in moe_config                 */
+  MOE_E_OOM = 3,            /* device or pinned host allocation failed         */
+  MOE_E_HIP = 4,            /* a HIP runtime call failed (text has its string)  */
+  MOE_E_CAPACITY = 5,       /* slot pool smaller than a routed group           */
+  MOE_E_NOT_REGISTERED = 6, /* layer weights not registered yet                */
+  MOE_E_TRANSFER = 7,       /* a miss transfer failed before publication       */
+  MOE_E_FAULTED = 8,        /* an earlier failure after publication faulted the
+                               context; only moe_destroy, moe_last_error and
+                               moe_cache_stats still work                      */
+  MOE_E_DEVICE = 9          /* the device error word is nonzero                */
+} moe_status;
+
+typedef enum moe_policy {
+  MOE_RESIDENT_ALL = 0, /* every expert resident in HBM, no slot pool          */
+  MOE_POLICY_LRU = 1,   /* evict least recently used                           */
+  MOE_POLICY_LFU = 2,   /* evict least frequently used (count kept on eviction)*/
+  MOE_POLICY_LRU_FREQ = 3 /* evict lowest freq*1000 - age, freq decays 0.75    */
+} moe_policy;
+
+/* Flags of moe_config.flags */
+#define MOE_FLAG_ROUTER_EXACT_ALWAYS 1u /* compute every logit with the exact
+                                           integer path (the certified FP64
+                                           path is skipped); results are equal */
+#define MOE_FLAG_FORCE_GEMV 2u          /* never take the MFMA expert path     */
+#define MOE_FLAG_FORCE_MFMA 4u          /* take the MFMA path for every expert */
+
+typedef struct moe_config {
+  int32_t hidden;          /* H, multiple of 256                                  */
+  int32_t n_experts;       /* E routed experts per layer, 1..1024                 */
+  int32_t inter;           /* I expert intermediate size, multiple of 256         */
+  int32_t top_k;           /* k, 1..16, k <= E                                    */
+  int32_t renorm;          /* 1: renormalise the top-k probabilities to sum 1     */
+  int32_t n_layers;        /* routed layers held by the context, >= 1            */
+  int32_t shared_inter;    /* always-on shared expert intermediate (0 = none),
+                              multiple of 256                                     */
+  int32_t group;           /* quantisation group along K; must be 128             */
+  int32_t max_tokens;      /* largest T of any call, 1..8192                      */
+  int32_t device;          /* HIP device ordinal                                  */
+  int32_t policy;          /* moe_policy                                          */
+  int32_t slots_per_layer; /* C, slot-pool capacity per layer (policy != 0)       */
+  uint32_t flags;          /* MOE_FLAG_*                                          */
+} moe_config;
+
+typedef struct moe_cache_counters {
+  uint64_t accesses;       /* experts requested through moe_cache_ensure          */
+  uint64_t hits;
+  uint64_t misses;
+  uint64_t evictions;
+  uint64_t h2d_bytes;      /* bytes copied host -> device for misses              */
+  uint64_t d2h_bytes;      /* expert bytes copied device -> host: always 0        */
+  uint64_t failures;       /* transfers that failed                               */
+  double h2d_seconds;      /* side-stream busy time of completed miss copies,
+                              summed from events by moe_cache_stats (syncs them)  */
+} moe_cache_counters;
+
+typedef struct moe_cache_event {
+  int32_t step;            /* value of the ensure call's `step` argument          */
+  int32_t layer;
+  int32_t expert;
+  int32_t hit;             /* 1 hit, 0 miss                                       */
+  int32_t slot;            /* slot the expert occupies after the call             */
+  int32_t victim;          /* expert evicted from that slot, -1 if none           */
+} moe_cache_event;
+
+/* ---- lifetime -------------------------------------------------------------- */
+
+/* Validates `cfg`, selects cfg->device, allocates per-layer HBM expert storage
+ * (E experts, or C slots with policy != MOE_RESIDENT_ALL, plus pinned host
+ * backing for all E experts), scratch sized by max_tokens, a side stream and
+ * events.  Capacity is fixed here: with a slot pool, C < min(E, max_tokens*k)
+ * fails with MOE_E_CAPACITY (a routed group of one call could not fit).
+ * On failure *out is NULL and moe_last_error(NULL) holds the reason. */
+moe_status moe_create(const moe_config* cfg, moe_ctx** out);
+
+/* Synchronises the context's streams and frees everything it owns.  NULL is a
+ * no-op. */
+void moe_destroy(moe_ctx* ctx);
+
+/* Text of the last error on `ctx` (or of the last failed moe_create when ctx is
+ * NULL).  Valid until the next call on the same context. */
+const char* moe_last_error(const moe_ctx* ctx);
+
+/* ---- weights --------------------------------------------------------------- */
+
+/* Copies one layer's weights into the library (the caller may free its arrays
+ * on return).  router: host FP16 [E, H].  q, s: host arrays in the layout above.
+ * shared_q [3][Is*H/2], shared_s [3][Is*H/128]: host, required iff
+ * shared_inter > 0, else NULL.  The codes are re-laid in HBM (and, with a slot
+ * pool, in the pinned backing) in the device tile layout; the pinned backing
+ * is never written again for the context's lifetime.  Synchronous.
+ * With a slot pool the layer's pool starts empty.  Re-registering a layer
+ * replaces its weights (and empties its pool). */
+moe_status moe_register_layer(moe_ctx* ctx, int32_t layer, const uint16_t* router,
+                              const uint8_t* q, const uint16_t* s,
+                              const uint8_t* shared_q, const uint16_t* shared_s);
+
+/* ---- hot path ---------------------------------------------------------------- */
+
+/* Router of `layer` for T tokens (1 <= T <= max_tokens).
+ *   logit[t,e] = the FP32 value nearest (ties to even) to the exact sum
+ *                sum_i x[t,i] * router[e,i];
+ *   ids[t,:]   = the k experts with the largest logits, ordered by (logit
+ *                descending, expert id ascending);
+ *   w[t,j]     = softmax(logit[t,:])[ids[t,j]], divided by sum_j of those
+ *                when cfg.renorm.
+ * x: dev FP16 [T,H].  forced_ids: dev int32 [T,k] or NULL; when given,
+ * selection is skipped, ids = forced_ids and w is gathered at them (ids must
+ * be in range and distinct within a token, else the device error word is set).
+ * ids: dev int32 [T,k] out.  w: dev FP32 [T,k] out.  logits: dev FP32 [T,E]
+ * out, or NULL. */
+moe_status moe_route(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
+                     const int32_t* forced_ids, int32_t* ids, float* w, float* logits,
+                     void* stream);
+
+/* Routed experts of `layer` for T tokens, given their ids and weights:
+ *   out[t] = fp16( sum_{j=0}^{k-1} w[t,j] * FFN_{ids[t,j]}(x[t])
+ *                  + FFN_shared(x[t]) )       (shared term iff shared_inter)
+ *   FFN_e(x) = (silu(x Wg_e^T) * (x Wu_e^T)) Wd_e^T, silu(z) = z / (1 + e^-z),
+ * with the rank-ordered sum taken in FP32 (no atomics: the result does not
+ * depend on scheduling).  Expert weights are read as INT4 and never expanded
+ * in HBM.  With a slot pool, every expert named in ids must have been made
+ * resident by moe_cache_ensure on this layer earlier on `stream`.
+ * x: dev FP16 [T,H]; ids: dev int32 [T,k]; w: dev FP32 [T,k];
+ * out: dev FP16 [T,H] (must not alias x). */
+moe_status moe_expert_forward(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
+                              const int32_t* ids, const float* w, void* out, void* stream);
+
+/* Residual stack over layers [layer_begin, layer_end):
+ *   for l: x_l = fp16(RMSNorm(h)), RMSNorm(h) = h / sqrt(mean(h^2) + 1e-5);
+ *          route x_l (forced_ids + l*T*k when forced_ids != NULL);
+ *          h += sum_j w * FFN(x_l) (+ shared), added in FP32.
+ * h: dev FP32 [T,H], updated in place.  forced_ids: dev int32 [L,T,k] indexed
+ * by absolute layer, or NULL.  x_trace (dev FP16 [L,T,H]), ids_trace
+ * (dev int32 [L,T,k]) and w_trace (dev FP32 [L,T,k]) receive each layer's
+ * x, ids and w when non-NULL (indexed by absolute layer).  With a slot pool
+ * forced_ids is required and each layer's group must have been ensured. */
+moe_status moe_stack_forward(moe_ctx* ctx, int32_t layer_begin, int32_t layer_end, float* h,
+                             int32_t T, const int32_t* forced_ids, void* x_trace,
+                             int32_t* ids_trace, float* w_trace, void* stream);
+
+/* Synchronises `stream`, reads and clears the device error word.  Returns
+ * MOE_OK if it was zero, else MOE_E_DEVICE with *bits (if non-NULL) set:
+ * 1 = expert id out of range, 2 = expert repeated within a token,
+ * 4 = expert not resident in the slot pool. */
+moe_status moe_check_device_errors(moe_ctx* ctx, void* stream, uint32_t* bits);
+
+/* ---- expert-slot pool (partial residency) ------------------------------------ */
+
+/* ensure() of the slot pool of `layer` for one routed group.
+ * experts: host int32 [n], distinct, 0 <= e < E, n <= C.  slots: host int32
+ * [n] out: the slot each expert occupies.  step: a label copied into the event
+ * log.  Hits refresh the policy state.  Each miss evicts a victim (chosen by
+ * the policy among resident experts not in the group) or takes a free slot,
+ * then copies the expert's blob from the pinned backing into the slot with
+ * hipMemcpyAsync on the side stream, after the victim's last reader (the
+ * previous compute on `stream` that used this layer) has retired.  `stream`
+ * then waits for every copy of the group, and the expert->slot map in HBM is
+ * updated in `stream` order, so kernels enqueued on `stream` after this call
+ * see the new experts and kernels enqueued before it see the old ones.
+ * Misses of one call are serialised.  A copy that fails to enqueue leaves the
+ * pool and statistics as they were (MOE_E_TRANSFER); a failure after the map
+ * update faults the context.  With MOE_RESIDENT_ALL: slots[i] = experts[i],
+ * nothing else happens. */
+moe_status moe_cache_ensure(moe_ctx* ctx, int32_t layer, const int32_t* experts, int32_t n,
+                            int32_t* slots, int32_t step, void* stream);
+
+moe_status moe_cache_stats(moe_ctx* ctx, int32_t layer, moe_cache_counters* out);
+
+/* Copies up to `cap` events of `layer` (oldest first) into buf; *n = number
+ * copied.  The log keeps every event since the layer was registered. */
+moe_status moe_cache_event_log(const moe_ctx* ctx, int32_t layer, moe_cache_event* buf,
+                               int32_t cap, int32_t* n);
+
+/* Test hook for the failure semantics of moe_cache_ensure, for callers that
+ * test failure handling: the next call on `layer` that has misses fails
+ * mode 1: before publication (as if a copy could not be enqueued; pool, policy
+ * state and statistics stay as they were, MOE_E_TRANSFER), or mode 2: after
+ * publication (the context is faulted, MOE_E_FAULTED).  mode 0 disarms. */
+moe_status moe_debug_inject_transfer_failure(moe_ctx* ctx, int32_t layer, int32_t mode);
+
+/* ---- host-only policy engine (no device needed) --------------------------------
+ * The decision procedure moe_cache_ensure uses, exposed on its own so it can be
+ * exercised without a GPU.  Per call: the clock ticks; the group (processed in
+ * ascending id) first refreshes its hits, then fills each miss from the lowest
+ * free slot or evicts the resident expert outside the group with the smallest
+ * key -- LRU (last, id); LFU (count, last, id); LRU-FREQ
+ * (sfreq*1000 - (clock - last), id) in double, sfreq = 1 on fill, +1 per hit,
+ * all sfreq *= 0.75 after every 2*C misses.  Events are appended hits first,
+ * then misses, each in ascending id. */
+typedef struct moe_policy_engine moe_policy_engine;
+
+moe_policy_engine* moe_policy_new(int32_t policy, int32_t n_experts, int32_t capacity,
+                                  int32_t layer);
+void moe_policy_free(moe_policy_engine* p);
+/* Returns MOE_OK, MOE_E_ARG (bad id, repeated id) or MOE_E_CAPACITY (n > C).
+ * slots [n] out in the order of `experts`; events appended to the engine's log. */
+moe_status moe_policy_access(moe_policy_engine* p, const int32_t* experts, int32_t n,
+                             int32_t step, int32_t* slots);
+int32_t moe_policy_event_count(const moe_policy_engine* p);
+int32_t moe_policy_events(const moe_policy_engine* p, moe_cache_event* buf, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_W4A16_H */

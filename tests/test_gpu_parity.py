@@ -1,0 +1,197 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: routing indices and cache decisions bit-exact; router logits bit-exact
+(both sides compute the FP32 value nearest to the exact dot product); combine
+weights within 1e-5 relative; layer outputs within relative L2 2e-3 and
+max-abs 5e-2 of the float64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from fixtures import moe_inputs as fx
+from oracle import moe_oracle as ora
+
+from gpu_util import assert_close, gpu_layer, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+SMALL = fx.MoEShape(hidden=256, n_experts=16, inter=256, top_k=4, renorm=False)
+SMALL_SHARED = fx.MoEShape(hidden=512, n_experts=32, inter=256, top_k=3, renorm=True, shared_inter=512)
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import w4a16_routed_expert_router_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def _ctx(m, shape, n_layers=1, max_tokens=64, **kw):
+    return m.MoEContext(shape, n_layers=n_layers, max_tokens=max_tokens, **kw)
+
+
+def _check_route(ctx, wts, shape, x, forced=None):
+    ids, w, lg = ctx.route(0, to_gpu(x), forced_ids=None if forced is None else to_gpu(forced),
+                           want_logits=True)
+    torch.cuda.synchronize()
+    o_ids, o_w, o_lg = ora.route(x, wts["router"], shape.top_k, shape.renorm, forced)
+    if forced is None:
+        np.testing.assert_array_equal(lg.cpu().numpy().view(np.uint32), o_lg.view(np.uint32))
+    np.testing.assert_array_equal(ids.cpu().numpy(), o_ids)
+    np.testing.assert_allclose(w.cpu().numpy(), o_w, rtol=1e-5, atol=1e-7)
+    return ids, w
+
+
+@pytest.mark.parametrize("T", [1, 5, 37])
+def test_route_small(moe, T):
+    say(f"test_route_small T={T}")
+    wts = gpu_layer(SMALL, "gpu-small", 0)
+    ctx = _ctx(moe, SMALL)
+    ctx.register_layer(0, wts)
+    x = fx.activations(("route-small", T), T, SMALL.hidden).numpy()
+    _check_route(ctx, wts, SMALL, x)
+    assert ctx.check_device_errors() == 0
+
+
+def test_route_ties_pick_lowest_id(moe):
+    say("test_route_ties_pick_lowest_id")
+    wts = gpu_layer(SMALL, "gpu-ties", 0)
+    wts["router"][9] = wts["router"][2]
+    wts["router"][12] = wts["router"][2]
+    ctx = _ctx(moe, SMALL)
+    ctx.register_layer(0, wts)
+    x = np.sign(wts["router"][2:3].astype(np.float32)).astype(np.float16).repeat(3, 0)
+    ids, _ = _check_route(ctx, wts, SMALL, x)
+    assert ids.cpu().numpy()[0, :3].tolist() == [2, 9, 12]
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_route_olmoe_qwen_shapes(moe, flags):
+    say(f"test_route_olmoe_qwen_shapes flags={flags}")
+    for shape, T in ((fx.OLMOE, 64), (fx.QWEN_NEXT, 16)):
+        router = fx.router_only(shape, "gpu-route", 0, device="cuda").cpu().numpy()
+        wts = {"router": router}
+        ctx = moe.MoEContext(shape, n_layers=1, max_tokens=T, flags=flags)
+        # router-only registration: zero experts (never run here)
+        E, H, I = shape.n_experts, shape.hidden, shape.inter
+        full = {"router": router, "q": np.zeros((E, 3, I * H // 2), np.uint8),
+                "s": np.zeros((E, 3, I * H // 128), np.float16)}
+        if shape.shared_inter:
+            full["shared_q"] = np.zeros((3, shape.shared_inter * H // 2), np.uint8)
+            full["shared_s"] = np.zeros((3, shape.shared_inter * H // 128), np.float16)
+        ctx.register_layer(0, full)
+        x = fx.activations(("route-shapes", T), T, H).numpy()
+        ids, w = _check_route(ctx, wts, shape, x)
+        if shape.renorm:
+            np.testing.assert_allclose(w.sum(1).cpu().numpy(), 1.0, rtol=1e-5)
+        ctx.close()
+
+
+def test_route_wide_range_inputs_exact(moe):
+    """Inputs spanning FP16 subnormals to large values stress the exact tier."""
+    say("test_route_wide_range_inputs_exact")
+    rng = np.random.default_rng(3)
+    wts = gpu_layer(SMALL, "gpu-wide", 0)
+    bits = rng.integers(0, 1 << 16, size=(8, SMALL.hidden), dtype=np.uint16)
+    x = bits.view(np.float16)
+    x = np.where(np.isfinite(x), x, np.float16(0.5)).astype(np.float16)
+    x = np.clip(x, -2.0, 2.0).astype(np.float16)   # keep logits finite
+    wts["router"] = np.where(np.arange(SMALL.hidden) % 3 == 0, wts["router"] * np.float16(1e-3),
+                             wts["router"]).astype(np.float16)
+    ctx = _ctx(moe, SMALL)
+    ctx.register_layer(0, wts)
+    _check_route(ctx, wts, SMALL, x)
+
+
+def test_route_forced_ids_gather_softmax(moe):
+    say("test_route_forced_ids_gather_softmax")
+    wts = gpu_layer(SMALL, "gpu-forced", 0)
+    ctx = _ctx(moe, SMALL)
+    ctx.register_layer(0, wts)
+    T = 9
+    x = fx.activations(("forced",), T, SMALL.hidden).numpy()
+    rng = np.random.default_rng(0)
+    forced = np.stack([np.sort(rng.choice(SMALL.n_experts, SMALL.top_k, replace=False))
+                       for _ in range(T)]).astype(np.int32)
+    _check_route(ctx, wts, SMALL, x, forced)
+    assert ctx.check_device_errors() == 0
+
+
+def test_route_forced_bad_ids_set_error_word(moe):
+    say("test_route_forced_bad_ids_set_error_word")
+    wts = gpu_layer(SMALL, "gpu-forced", 0)
+    ctx = _ctx(moe, SMALL)
+    ctx.register_layer(0, wts)
+    x = fx.activations(("forced-bad",), 2, SMALL.hidden).cuda()
+    forced = torch.tensor([[0, 1, 2, 99], [3, 3, 4, 5]], dtype=torch.int32, device="cuda")
+    ids, _ = ctx.route(0, x, forced_ids=forced)
+    bits = ctx.check_device_errors()
+    assert bits & 1 and bits & 2
+    got = ids.cpu().numpy()
+    assert got.min() >= 0 and got.max() < SMALL.n_experts
+    assert ctx.check_device_errors() == 0      # cleared
+
+
+def _layer_case(moe, shape, cfg, T, flags=0, wts=None):
+    wts = gpu_layer(shape, cfg, 0) if wts is None else wts
+    ctx = moe.MoEContext(shape, n_layers=1, max_tokens=max(T, 1), flags=flags)
+    ctx.register_layer(0, wts)
+    x = fx.activations((cfg, "x", T), T, shape.hidden).numpy()
+    xg = to_gpu(x)
+    ids, w = ctx.route(0, xg)
+    out = ctx.expert_forward(0, xg, ids, w)
+    torch.cuda.synchronize()
+    assert ctx.check_device_errors() == 0
+    ref = ora.moe_layer(x, wts, shape)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref["ids"])
+    assert_close(out.float().cpu().numpy(), ref["out"], f"{cfg} T={T}")
+    ctx.close()
+    return wts
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 64])
+def test_layer_small(moe, T):
+    say(f"test_layer_small T={T}")
+    _layer_case(moe, SMALL, "gpu-layer-small", T)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_layer_small_shared_renorm(moe, T):
+    say(f"test_layer_small_shared_renorm T={T}")
+    _layer_case(moe, SMALL_SHARED, "gpu-layer-shared", T)
+
+
+@pytest.fixture(scope="module")
+def olmoe_layer():
+    return gpu_layer(fx.OLMOE, "olmoe-layer", 0)
+
+
+@pytest.mark.parametrize("T", [4, 64, 512])
+def test_layer_olmoe(moe, olmoe_layer, T):
+    """OLMoE-shaped layer: decode T=4, batch-64 decode, 512-token prefill."""
+    say(f"test_layer_olmoe T={T}")
+    _layer_case(moe, fx.OLMOE, "olmoe-layer", T, wts=olmoe_layer)
+
+
+def test_expert_forward_identical_experts_scale(moe):
+    """All experts equal: out = (sum_j w) * FFN(x) on the GPU as well."""
+    say("test_expert_forward_identical_experts_scale")
+    wts = gpu_layer(SMALL, "gpu-ident", 0)
+    for key in ("q", "s"):
+        wts[key] = np.repeat(wts[key][:1], SMALL.n_experts, axis=0)
+    _layer_case(moe, SMALL, "gpu-ident", 5, wts=wts)
+
+
+def test_expert_forward_bad_ids_are_contained(moe):
+    say("test_expert_forward_bad_ids_are_contained")
+    wts = gpu_layer(SMALL, "gpu-badids", 0)
+    ctx = _ctx(moe, SMALL)
+    ctx.register_layer(0, wts)
+    x = fx.activations(("badids",), 3, SMALL.hidden).cuda()
+    ids = torch.tensor([[0, 1, 2, 3], [5, 5, 6, 7], [1, 2, 3, -4]], dtype=torch.int32, device="cuda")
+    w = torch.full((3, 4), 0.25, dtype=torch.float32, device="cuda")
+    out = ctx.expert_forward(0, x, ids, w)
+    bits = ctx.check_device_errors()
+    assert bits & 1 and bits & 2
+    assert torch.isfinite(out.float()).all()

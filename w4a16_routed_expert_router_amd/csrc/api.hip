@@ -1,0 +1,558 @@
+// C ABI of the W4A16 routed-expert MoE library: context, weight registration,
+// dispatch of the hot path and the expert-slot pool transport.
+//
+// Expert-slot pool ("Horizon RunMap", "Partial-residency contract: immutable
+// authority and miss lifecycle"; "F51 Nitro / Nitro-MoE", "Layer 1 - expert
+// persistence cache"):
+//   - every expert of a pooled layer lives in pinned host memory that is
+//     written once at registration and never again (immutable authority);
+//   - a miss copies one contiguous expert blob host -> device on a side stream
+//     (H2D only; eviction discards the device copy, nothing is written back);
+//   - the side stream first waits for the layer's "retired" event, recorded
+//     after the last compute that read the layer's slots, so a victim slot is
+//     not overwritten while an earlier kernel may still read it;
+//   - the caller's stream waits for the "ready" event of the call's copies and
+//     only then runs the small kernel that writes the expert -> slot map in HBM
+//     (publication after complete transfer, in stream order);
+//   - capacity is fixed at creation; a routed group larger than it fails.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <memory>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/moe_w4a16.h"
+#include "launch.hpp"
+#include "policy.hpp"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_create_error;
+
+struct LayerState {
+  bool registered = false;
+  uint16_t* router = nullptr;  // dev [E,H] fp16
+  uint8_t* store = nullptr;    // dev: E blobs (resident) or C slot blobs (pool)
+  uint8_t* shared = nullptr;   // dev: shared-expert blob
+  int32_t* map = nullptr;      // dev [E]: expert -> slot, -1 = not resident
+  uint8_t* backing = nullptr;  // pinned host [E blobs] (pool only)
+  std::unique_ptr<PolicyEngine> policy;
+  hipEvent_t retired = nullptr;
+  hipEvent_t ready = nullptr;
+  moe_cache_counters stats{};
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> timing;
+  int inject = 0;  // test hook: 1 fail before publication, 2 fail after it
+};
+
+}  // namespace
+
+struct moe_ctx {
+  moe_config cfg{};
+  BlobLayout lay{}, shared_lay{};
+  std::vector<LayerState> layers;
+  float* logits = nullptr;
+  int32_t* ids = nullptr;
+  float* w = nullptr;
+  int32_t* ids_s = nullptr;
+  ActiveExpert* active = nullptr;
+  int32_t* n_active = nullptr;
+  int32_t* perm_tok = nullptr;
+  int32_t* pos_of = nullptr;
+  uint16_t* hbuf = nullptr;
+  uint16_t* hshared = nullptr;
+  float* ybuf = nullptr;
+  float* yshared = nullptr;
+  uint16_t* xbuf = nullptr;
+  uint32_t* err = nullptr;
+  hipStream_t side = nullptr;
+  std::string last_error;
+  bool faulted = false;
+};
+
+namespace {
+
+moe_status fail(moe_ctx* c, moe_status st, const std::string& msg) {
+  if (c)
+    c->last_error = msg;
+  else
+    g_create_error = msg;
+  return st;
+}
+
+#define HIPCHK(ctx, call)                                                           \
+  do {                                                                              \
+    hipError_t e_ = (call);                                                         \
+    if (e_ != hipSuccess)                                                           \
+      return fail(ctx, MOE_E_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+bool valid_dim(int v) { return v >= 256 && v <= 2048 && v % 256 == 0; }
+
+// Canonical packing has k0..k7 of a row in nibbles 0..7 of a little-endian
+// word; the device layout puts the even k in nibbles 0..3 and the odd k in
+// nibbles 4..7 (see dequant8 in common.hpp).
+inline uint32_t compress_low_nibbles(uint32_t v) {
+  v &= 0x0F0F0F0Fu;
+  v = (v | (v >> 4)) & 0x00FF00FFu;
+  v = (v | (v >> 8)) & 0x0000FFFFu;
+  return v;
+}
+inline uint32_t to_device_word(uint32_t c) {
+  return compress_low_nibbles(c) | (compress_low_nibbles(c >> 4) << 16);
+}
+
+// One expert's canonical (codes [3][cb], scales [3][sc]) -> device blob bytes.
+void repack_expert(const uint8_t* q, const uint16_t* s, int64_t cb, int64_t sc, uint8_t* dst) {
+  for (int m = 0; m < 3; ++m) {
+    const uint8_t* src = q + m * cb;
+    uint8_t* d = dst + m * cb;
+    for (int64_t i = 0; i < cb; i += 4) {
+      uint32_t w;
+      memcpy(&w, src + i, 4);
+      w = to_device_word(w);
+      memcpy(d + i, &w, 4);
+    }
+  }
+  memcpy(dst + 3 * cb, s, 3 * sc * sizeof(uint16_t));
+}
+
+// Repack E experts with a few host threads.
+void repack_many(const uint8_t* q, const uint16_t* s, int n, int64_t cb, int64_t sc,
+                 uint8_t* dst, int64_t blob) {
+  unsigned nt = std::thread::hardware_concurrency();
+  nt = nt == 0 ? 1 : (nt > 16 ? 16 : nt);
+  if ((int64_t)n * blob < (64ll << 20)) nt = 1;
+  std::vector<std::thread> th;
+  for (unsigned t = 0; t < nt; ++t)
+    th.emplace_back([=] {
+      for (int e = (int)t; e < n; e += (int)nt)
+        repack_expert(q + (int64_t)e * 3 * cb, s + (int64_t)e * 3 * sc, cb, sc, dst + e * blob);
+    });
+  for (auto& x : th) x.join();
+}
+
+moe_status check_ctx(moe_ctx* c) {
+  if (!c) return MOE_E_ARG;
+  if (c->faulted) return fail(c, MOE_E_FAULTED, "context is faulted");
+  return MOE_OK;
+}
+
+moe_status check_layer(moe_ctx* c, int layer) {
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, MOE_E_ARG, "layer index out of range");
+  if (!c->layers[layer].registered) return fail(c, MOE_E_NOT_REGISTERED, "layer not registered");
+  return MOE_OK;
+}
+
+bool pooled(const moe_ctx* c) { return c->cfg.policy != MOE_RESIDENT_ALL; }
+
+int max_active(const moe_ctx* c, int T) {
+  const int64_t p = (int64_t)T * c->cfg.top_k;
+  return (int)(p < c->cfg.n_experts ? p : c->cfg.n_experts);
+}
+
+// group -> gate/up -> down (routed and shared) -> combine into out or resid.
+moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const int32_t* ids,
+                       const float* w, uint16_t* out, float* resid, hipStream_t s) {
+  LayerState& L = c->layers[layer];
+  const moe_config& g = c->cfg;
+  GroupArgs ga{ids, T, g.top_k, g.n_experts, L.map, c->ids_s, c->active, c->n_active,
+               c->perm_tok, c->pos_of, c->err};
+  launch_group(ga, s);
+  ExpertArgs ea{};
+  ea.blobs = L.store;
+  ea.blob_stride = c->lay.total();
+  ea.lay = c->lay;
+  ea.active = c->active;
+  ea.n_active = c->n_active;
+  ea.max_active = max_active(c, T);
+  ea.H = g.hidden;
+  ea.I = g.inter;
+  ea.x = x;
+  ea.perm_tok = c->perm_tok;
+  ea.hbuf = c->hbuf;
+  ea.ybuf = c->ybuf;
+  launch_gateup_gemv(ea, s);
+  launch_down_gemv(ea, s);
+  if (g.shared_inter) {
+    ExpertArgs sa = ea;
+    sa.lay = c->shared_lay;
+    sa.fixed_blob = L.shared;
+    sa.fixed_count = T;
+    sa.fixed_offset = 0;
+    sa.I = g.shared_inter;
+    sa.hbuf = c->hshared;
+    sa.ybuf = c->yshared;
+    launch_gateup_gemv(sa, s);
+    launch_down_gemv(sa, s);
+  }
+  CombineArgs ca{c->ybuf, g.shared_inter ? c->yshared : nullptr, c->pos_of, w, T, g.top_k,
+                 g.hidden, out, resid};
+  launch_combine(ca, s);
+  if (pooled(c)) HIPCHK(c, hipEventRecord(L.retired, s));
+  HIPCHK(c, hipGetLastError());
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(const moe_ctx* ctx) {
+  return ctx ? ctx->last_error.c_str() : g_create_error.c_str();
+}
+
+moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
+  if (!out) return fail(nullptr, MOE_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (!cfg) return fail(nullptr, MOE_E_ARG, "cfg is NULL");
+  const moe_config g = *cfg;
+  if (!valid_dim(g.hidden) || !valid_dim(g.inter) || (g.shared_inter && !valid_dim(g.shared_inter)))
+    return fail(nullptr, MOE_E_SHAPE, "hidden/inter/shared_inter must be multiples of 256 in [256, 2048]");
+  if (g.n_experts < 1 || g.n_experts > 1024) return fail(nullptr, MOE_E_SHAPE, "n_experts must be in [1, 1024]");
+  if (g.top_k < 1 || g.top_k > 16 || g.top_k > g.n_experts) return fail(nullptr, MOE_E_SHAPE, "top_k must be in [1, min(16, E)]");
+  if (g.group != 128) return fail(nullptr, MOE_E_SHAPE, "group must be 128");
+  if (g.n_layers < 1) return fail(nullptr, MOE_E_SHAPE, "n_layers must be >= 1");
+  if (g.max_tokens < 1 || g.max_tokens > 8192) return fail(nullptr, MOE_E_SHAPE, "max_tokens must be in [1, 8192]");
+  if (g.policy < 0 || g.policy > 3) return fail(nullptr, MOE_E_ARG, "unknown policy");
+  if (g.policy != MOE_RESIDENT_ALL) {
+    const int64_t need = std::min<int64_t>(g.n_experts, (int64_t)g.max_tokens * g.top_k);
+    if (g.slots_per_layer < need || g.slots_per_layer > g.n_experts)
+      return fail(nullptr, MOE_E_CAPACITY,
+                  "slots_per_layer must be >= min(E, max_tokens*k) and <= E");
+  }
+  std::unique_ptr<moe_ctx> c(new moe_ctx());
+  c->cfg = g;
+  const int64_t cb = (int64_t)g.inter * g.hidden / 2, sc = (int64_t)g.inter * g.hidden / 128;
+  c->lay = BlobLayout{cb, sc * 2};
+  const int64_t scb = (int64_t)g.shared_inter * g.hidden / 2, ssc = (int64_t)g.shared_inter * g.hidden / 128;
+  c->shared_lay = BlobLayout{scb, ssc * 2};
+  hipError_t e = hipSetDevice(g.device);
+  if (e != hipSuccess) return fail(nullptr, MOE_E_HIP, std::string("hipSetDevice: ") + hipGetErrorString(e));
+
+  auto dalloc = [&](void** p, size_t bytes) -> bool {
+    if (hipMalloc(p, bytes < 256 ? 256 : bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    return true;
+  };
+  c->layers.resize(g.n_layers);
+  const int64_t blob = c->lay.total();
+  const int nslots = g.policy == MOE_RESIDENT_ALL ? g.n_experts : g.slots_per_layer;
+  bool ok = true;
+  for (int l = 0; l < g.n_layers && ok; ++l) {
+    LayerState& L = c->layers[l];
+    ok = ok && dalloc((void**)&L.router, (size_t)g.n_experts * g.hidden * 2);
+    ok = ok && dalloc((void**)&L.store, (size_t)nslots * blob);
+    ok = ok && dalloc((void**)&L.map, (size_t)g.n_experts * 4);
+    if (g.shared_inter) ok = ok && dalloc((void**)&L.shared, (size_t)c->shared_lay.total());
+    if (ok && g.policy != MOE_RESIDENT_ALL) {
+      if (hipHostMalloc((void**)&L.backing, (size_t)g.n_experts * blob, hipHostMallocDefault) != hipSuccess) {
+        (void)hipGetLastError();
+        L.backing = nullptr;
+        ok = false;
+      }
+    }
+    if (ok) {
+      if (hipEventCreateWithFlags(&L.retired, hipEventDisableTiming) != hipSuccess ||
+          hipEventCreateWithFlags(&L.ready, hipEventDisableTiming) != hipSuccess)
+        ok = false;
+    }
+  }
+  const int64_t P = (int64_t)g.max_tokens * g.top_k;
+  const int Imax = g.inter;
+  ok = ok && dalloc((void**)&c->logits, (size_t)g.max_tokens * g.n_experts * 4);
+  ok = ok && dalloc((void**)&c->ids, (size_t)P * 4);
+  ok = ok && dalloc((void**)&c->w, (size_t)P * 4);
+  ok = ok && dalloc((void**)&c->ids_s, (size_t)P * 4);
+  ok = ok && dalloc((void**)&c->active, (size_t)g.n_experts * sizeof(ActiveExpert));
+  ok = ok && dalloc((void**)&c->n_active, 4);
+  ok = ok && dalloc((void**)&c->perm_tok, (size_t)P * 4);
+  ok = ok && dalloc((void**)&c->pos_of, (size_t)P * 4);
+  ok = ok && dalloc((void**)&c->hbuf, (size_t)P * Imax * 2);
+  ok = ok && dalloc((void**)&c->ybuf, (size_t)P * g.hidden * 4);
+  ok = ok && dalloc((void**)&c->xbuf, (size_t)g.max_tokens * g.hidden * 2);
+  ok = ok && dalloc((void**)&c->err, 4);
+  if (g.shared_inter) {
+    ok = ok && dalloc((void**)&c->hshared, (size_t)g.max_tokens * g.shared_inter * 2);
+    ok = ok && dalloc((void**)&c->yshared, (size_t)g.max_tokens * g.hidden * 4);
+  }
+  if (ok && hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess) ok = false;
+  if (ok) {
+    const uint32_t zero = 0;
+    ok = hipMemcpy(c->err, &zero, 4, hipMemcpyHostToDevice) == hipSuccess;
+  }
+  if (!ok) {
+    moe_destroy(c.release());
+    return fail(nullptr, MOE_E_OOM, "device or pinned allocation failed");
+  }
+  *out = c.release();
+  return MOE_OK;
+}
+
+void moe_destroy(moe_ctx* c) {
+  if (!c) return;
+  (void)hipSetDevice(c->cfg.device);
+  (void)hipDeviceSynchronize();
+  for (LayerState& L : c->layers) {
+    (void)hipFree(L.router);
+    (void)hipFree(L.store);
+    (void)hipFree(L.map);
+    (void)hipFree(L.shared);
+    if (L.backing) (void)hipHostFree(L.backing);
+    if (L.retired) (void)hipEventDestroy(L.retired);
+    if (L.ready) (void)hipEventDestroy(L.ready);
+    for (auto& p : L.timing) {
+      (void)hipEventDestroy(p.first);
+      (void)hipEventDestroy(p.second);
+    }
+  }
+  void* bufs[] = {c->logits, c->ids,  c->w,    c->ids_s,   c->active,  c->n_active, c->perm_tok,
+                  c->pos_of, c->hbuf, c->ybuf, c->xbuf,    c->err,     c->hshared,  c->yshared};
+  for (void* p : bufs) (void)hipFree(p);
+  if (c->side) (void)hipStreamDestroy(c->side);
+  delete c;
+}
+
+moe_status moe_register_layer(moe_ctx* c, int32_t layer, const uint16_t* router, const uint8_t* q,
+                              const uint16_t* s, const uint8_t* shared_q, const uint16_t* shared_s) {
+  if (moe_status st = check_ctx(c)) return st;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, MOE_E_ARG, "layer index out of range");
+  if (!router || !q || !s) return fail(c, MOE_E_ARG, "router, q and s are required");
+  const moe_config& g = c->cfg;
+  if (g.shared_inter && (!shared_q || !shared_s)) return fail(c, MOE_E_ARG, "shared expert weights required");
+  if (!g.shared_inter && (shared_q || shared_s)) return fail(c, MOE_E_ARG, "no shared expert configured");
+  HIPCHK(c, hipSetDevice(g.device));
+  HIPCHK(c, hipDeviceSynchronize());
+  LayerState& L = c->layers[layer];
+  const int64_t cb = c->lay.code_bytes, sc = c->lay.scale_bytes / 2, blob = c->lay.total();
+  HIPCHK(c, hipMemcpy(L.router, router, (size_t)g.n_experts * g.hidden * 2, hipMemcpyHostToDevice));
+  std::vector<int32_t> map(g.n_experts);
+  if (pooled(c)) {
+    repack_many(q, s, g.n_experts, cb, sc, L.backing, blob);
+    for (int e = 0; e < g.n_experts; ++e) map[e] = -1;
+    L.policy.reset(new PolicyEngine(g.policy, g.n_experts, g.slots_per_layer, layer));
+    L.stats = moe_cache_counters{};
+  } else {
+    // stage in chunks of experts through pinned memory
+    const int chunk = 16;
+    uint8_t* stage = nullptr;
+    HIPCHK(c, hipHostMalloc((void**)&stage, (size_t)chunk * blob, hipHostMallocDefault));
+    hipError_t err = hipSuccess;
+    for (int e0 = 0; e0 < g.n_experts && err == hipSuccess; e0 += chunk) {
+      const int n = std::min(chunk, g.n_experts - e0);
+      repack_many(q + (int64_t)e0 * 3 * cb, s + (int64_t)e0 * 3 * sc, n, cb, sc, stage, blob);
+      err = hipMemcpy(L.store + (int64_t)e0 * blob, stage, (size_t)n * blob, hipMemcpyHostToDevice);
+    }
+    (void)hipHostFree(stage);
+    if (err != hipSuccess) return fail(c, MOE_E_HIP, std::string("hipMemcpy: ") + hipGetErrorString(err));
+    for (int e = 0; e < g.n_experts; ++e) map[e] = e;
+  }
+  HIPCHK(c, hipMemcpy(L.map, map.data(), map.size() * 4, hipMemcpyHostToDevice));
+  if (g.shared_inter) {
+    const int64_t scb = c->shared_lay.code_bytes, ssc = c->shared_lay.scale_bytes / 2;
+    std::vector<uint8_t> tmp((size_t)c->shared_lay.total());
+    repack_expert(shared_q, shared_s, scb, ssc, tmp.data());
+    HIPCHK(c, hipMemcpy(L.shared, tmp.data(), tmp.size(), hipMemcpyHostToDevice));
+  }
+  L.registered = true;
+  return MOE_OK;
+}
+
+moe_status moe_route(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* forced_ids,
+                     int32_t* ids, float* w, float* logits, void* stream) {
+  if (moe_status st = check_ctx(c)) return st;
+  if (moe_status st = check_layer(c, layer)) return st;
+  if (!x || !ids || !w) return fail(c, MOE_E_ARG, "x, ids and w are required");
+  if (T < 1 || T > c->cfg.max_tokens) return fail(c, MOE_E_ARG, "T out of range [1, max_tokens]");
+  const moe_config& g = c->cfg;
+  RouterArgs ra{(const uint16_t*)x, c->layers[layer].router, T, g.n_experts, g.hidden, g.top_k,
+                g.renorm, logits ? logits : c->logits, forced_ids, ids, w, c->err,
+                (int)(g.flags & MOE_FLAG_ROUTER_EXACT_ALWAYS)};
+  launch_router(ra, (hipStream_t)stream);
+  HIPCHK(c, hipGetLastError());
+  return MOE_OK;
+}
+
+moe_status moe_expert_forward(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* ids,
+                              const float* w, void* out, void* stream) {
+  if (moe_status st = check_ctx(c)) return st;
+  if (moe_status st = check_layer(c, layer)) return st;
+  if (!x || !ids || !w || !out) return fail(c, MOE_E_ARG, "x, ids, w and out are required");
+  if (x == out) return fail(c, MOE_E_ARG, "out must not alias x");
+  if (T < 1 || T > c->cfg.max_tokens) return fail(c, MOE_E_ARG, "T out of range [1, max_tokens]");
+  return run_experts(c, layer, (const uint16_t*)x, T, ids, w, (uint16_t*)out, nullptr,
+                     (hipStream_t)stream);
+}
+
+moe_status moe_stack_forward(moe_ctx* c, int32_t layer_begin, int32_t layer_end, float* h, int32_t T,
+                             const int32_t* forced_ids, void* x_trace, int32_t* ids_trace,
+                             float* w_trace, void* stream) {
+  if (moe_status st = check_ctx(c)) return st;
+  const moe_config& g = c->cfg;
+  if (layer_begin < 0 || layer_end > g.n_layers || layer_begin >= layer_end)
+    return fail(c, MOE_E_ARG, "bad layer range");
+  for (int l = layer_begin; l < layer_end; ++l)
+    if (moe_status st = check_layer(c, l)) return st;
+  if (!h) return fail(c, MOE_E_ARG, "h is required");
+  if (T < 1 || T > g.max_tokens) return fail(c, MOE_E_ARG, "T out of range [1, max_tokens]");
+  if (pooled(c) && !forced_ids) return fail(c, MOE_E_ARG, "a slot pool needs forced_ids");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t tk = (int64_t)T * g.top_k, th = (int64_t)T * g.hidden;
+  for (int l = layer_begin; l < layer_end; ++l) {
+    uint16_t* x = x_trace ? (uint16_t*)x_trace + l * th : c->xbuf;
+    int32_t* ids = ids_trace ? ids_trace + l * tk : c->ids;
+    float* w = w_trace ? w_trace + l * tk : c->w;
+    launch_rmsnorm(h, T, g.hidden, 1e-5f, x, s);
+    RouterArgs ra{x, c->layers[l].router, T, g.n_experts, g.hidden, g.top_k, g.renorm, c->logits,
+                  forced_ids ? forced_ids + l * tk : nullptr, ids, w, c->err,
+                  (int)(g.flags & MOE_FLAG_ROUTER_EXACT_ALWAYS)};
+    launch_router(ra, s);
+    if (moe_status st = run_experts(c, l, x, T, ids, w, nullptr, h, s)) return st;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_check_device_errors(moe_ctx* c, void* stream, uint32_t* bits) {
+  if (!c) return MOE_E_ARG;
+  HIPCHK(c, hipStreamSynchronize((hipStream_t)stream));
+  uint32_t v = 0;
+  const uint32_t zero = 0;
+  HIPCHK(c, hipMemcpy(&v, c->err, 4, hipMemcpyDeviceToHost));
+  HIPCHK(c, hipMemcpy(c->err, &zero, 4, hipMemcpyHostToDevice));
+  if (bits) *bits = v;
+  if (v) return fail(c, MOE_E_DEVICE, "device error word " + std::to_string(v));
+  return MOE_OK;
+}
+
+moe_status moe_cache_ensure(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n,
+                            int32_t* slots, int32_t step, void* stream) {
+  if (moe_status st = check_ctx(c)) return st;
+  if (moe_status st = check_layer(c, layer)) return st;
+  if (n < 0 || (n > 0 && (!experts || !slots))) return fail(c, MOE_E_ARG, "bad experts/slots");
+  const moe_config& g = c->cfg;
+  for (int i = 0; i < n; ++i)
+    if (experts[i] < 0 || experts[i] >= g.n_experts) return fail(c, MOE_E_ARG, "expert id out of range");
+  if (!pooled(c)) {
+    for (int i = 0; i < n; ++i) slots[i] = experts[i];
+    return MOE_OK;
+  }
+  LayerState& L = c->layers[layer];
+  if (n > g.slots_per_layer) return fail(c, MOE_E_CAPACITY, "routed group larger than the slot pool");
+  hipStream_t s = (hipStream_t)stream;
+  const PolicyEngine saved = *L.policy;
+  std::vector<PolicyEngine::Decision> dec;
+  const int rc = L.policy->access(experts, n, step, dec);
+  if (rc == 1) return fail(c, MOE_E_ARG, "repeated expert in group");
+  if (rc == 2) return fail(c, MOE_E_CAPACITY, "routed group larger than the slot pool");
+  const int64_t blob = c->lay.total();
+  int nmiss = 0, nevict = 0;
+  for (const auto& d : dec)
+    if (!d.hit) {
+      ++nmiss;
+      if (d.victim >= 0) ++nevict;
+    }
+  if (nmiss > 0) {
+    // transport: side stream waits for the last reader of this layer's slots
+    bool good = L.inject != 1;
+    hipEvent_t t0 = nullptr, t1 = nullptr;
+    good = good && hipEventCreate(&t0) == hipSuccess && hipEventCreate(&t1) == hipSuccess;
+    good = good && hipStreamWaitEvent(c->side, L.retired, 0) == hipSuccess;
+    good = good && hipEventRecord(t0, c->side) == hipSuccess;
+    for (const auto& d : dec) {
+      if (d.hit || !good) continue;
+      good = hipMemcpyAsync(L.store + (int64_t)d.slot * blob, L.backing + (int64_t)d.expert * blob,
+                            (size_t)blob, hipMemcpyHostToDevice, c->side) == hipSuccess;
+    }
+    good = good && hipEventRecord(t1, c->side) == hipSuccess;
+    good = good && hipEventRecord(L.ready, c->side) == hipSuccess;
+    good = good && hipStreamWaitEvent(s, L.ready, 0) == hipSuccess;
+    if (!good) {
+      (void)hipGetLastError();
+      if (t0) (void)hipEventDestroy(t0);
+      if (t1) (void)hipEventDestroy(t1);
+      *L.policy = saved;  // the old generation stays authoritative
+      L.inject = 0;
+      L.stats.failures += 1;
+      return fail(c, MOE_E_TRANSFER, "miss transfer failed before publication");
+    }
+    L.timing.emplace_back(t0, t1);
+    // publication in stream order, after the copies
+    PublishArgs pa{};
+    pa.map = L.map;
+    for (const auto& d : dec) {
+      if (d.hit) continue;
+      if (d.victim >= 0) {
+        if (pa.n == kMaxPublish) {
+          launch_publish(pa, s);
+          pa.n = 0;
+        }
+        pa.u[pa.n++] = PublishUpdate{d.victim, -1};
+      }
+      if (pa.n == kMaxPublish) {
+        launch_publish(pa, s);
+        pa.n = 0;
+      }
+      pa.u[pa.n++] = PublishUpdate{d.expert, d.slot};
+    }
+    if (pa.n) launch_publish(pa, s);
+    if (hipGetLastError() != hipSuccess || L.inject == 2) {
+      c->faulted = true;
+      L.inject = 0;
+      L.stats.failures += 1;
+      return fail(c, MOE_E_FAULTED, "failure after publication: context faulted");
+    }
+  }
+  L.stats.accesses += n;
+  L.stats.hits += n - nmiss;
+  L.stats.misses += nmiss;
+  L.stats.evictions += nevict;
+  L.stats.h2d_bytes += (uint64_t)nmiss * blob;
+  for (int i = 0; i < n; ++i) slots[i] = L.policy->slot_of(experts[i]);
+  return MOE_OK;
+}
+
+moe_status moe_cache_stats(moe_ctx* c, int32_t layer, moe_cache_counters* out) {
+  if (!c || !out) return MOE_E_ARG;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, MOE_E_ARG, "layer index out of range");
+  LayerState& L = c->layers[layer];
+  for (auto& p : L.timing) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(p.second) == hipSuccess && hipEventElapsedTime(&ms, p.first, p.second) == hipSuccess)
+      L.stats.h2d_seconds += ms * 1e-3;
+    (void)hipEventDestroy(p.first);
+    (void)hipEventDestroy(p.second);
+  }
+  L.timing.clear();
+  *out = L.stats;
+  return MOE_OK;
+}
+
+moe_status moe_cache_event_log(const moe_ctx* c, int32_t layer, moe_cache_event* buf, int32_t cap,
+                               int32_t* n) {
+  if (!c || !n) return MOE_E_ARG;
+  if (layer < 0 || layer >= c->cfg.n_layers) return MOE_E_ARG;
+  const LayerState& L = c->layers[layer];
+  *n = 0;
+  if (!L.policy) return MOE_OK;
+  const auto& lg = L.policy->log();
+  const int32_t m = std::min<int32_t>(cap < 0 ? 0 : cap, (int32_t)lg.size());
+  if (m > 0 && !buf) return MOE_E_ARG;
+  for (int32_t i = 0; i < m; ++i) buf[i] = lg[i];
+  *n = m;
+  return MOE_OK;
+}
+
+moe_status moe_debug_inject_transfer_failure(moe_ctx* c, int32_t layer, int32_t mode) {
+  if (!c) return MOE_E_ARG;
+  if (layer < 0 || layer >= c->cfg.n_layers || mode < 0 || mode > 2)
+    return fail(c, MOE_E_ARG, "bad layer or mode");
+  c->layers[layer].inject = mode;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Device-side helpers shared by the HIP kernels of the W4A16 MoE library.
+// gfx950 only: 64-lane wavefronts, v_dot2_f32_f16, packed FP16 arithmetic.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 128;  // INT4 quantisation group along K
+
+// Device error word bits (see moe_check_device_errors).
+constexpr uint32_t kErrBadId = 1u;
+constexpr uint32_t kErrDupId = 2u;
+constexpr uint32_t kErrNotResident = 4u;
+
+// One active expert of a call, produced by the grouping kernel.
+struct ActiveExpert {
+  int32_t expert;  // routed expert id
+  int32_t slot;    // index of its blob in the layer's expert storage
+  int32_t count;   // tokens routed to it
+  int32_t offset;  // first position of its tokens in the sorted order
+};
+
+// Byte offsets of the parts of one expert blob in HBM (device layout):
+//   [gate codes I*H/2][up codes I*H/2][down codes H*I/2]
+//   [gate scales I*H/128 fp16][up scales][down scales]
+struct BlobLayout {
+  int64_t code_bytes;   // one matrix
+  int64_t scale_bytes;  // one matrix
+  __host__ __device__ int64_t codes(int m) const { return m * code_bytes; }
+  __host__ __device__ int64_t scales(int m) const { return 3 * code_bytes + m * scale_bytes; }
+  __host__ __device__ int64_t total() const { return 3 * (code_bytes + scale_bytes); }
+};
+
+// ---- INT4 -> FP16 --------------------------------------------------------------
+// Device code layout: within each 32-bit word holding k0..k7 of a row, nibble
+// position p holds k[perm(p)] with positions (0,4,1,5,2,6,3,7) <- (k0..k7), so
+// that masking with 0x000F000F / 0x00F000F0 yields the pairs (k0,k1), (k2,k3)
+// and after an 8-bit shift (k4,k5), (k6,k7).  OR-ing a nibble into the FP16
+// pattern 0x6400 (= 1024, ulp 1) gives 1024 + q exactly; a nibble in bits 4..7
+// gives 1024 + 16q.  Both are turned into q - 8 exactly.
+__device__ __forceinline__ void dequant8(uint32_t d, h2 out[4]) {
+  const uint32_t d8 = d >> 8;
+  const h2 lo0 = __builtin_bit_cast(h2, (d & 0x000F000Fu) | 0x64006400u);
+  const h2 hi0 = __builtin_bit_cast(h2, (d & 0x00F000F0u) | 0x64006400u);
+  const h2 lo1 = __builtin_bit_cast(h2, (d8 & 0x000F000Fu) | 0x64006400u);
+  const h2 hi1 = __builtin_bit_cast(h2, (d8 & 0x00F000F0u) | 0x64006400u);
+  const h2 k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const h2 k16th = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const h2 km72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  out[0] = lo0 - k1032;
+  out[1] = hi0 * k16th + km72;
+  out[2] = lo1 - k1032;
+  out[3] = hi1 * k16th + km72;
+}
+
+__device__ __forceinline__ float dot2(h2 a, h2 b, float c) {
+  return __builtin_amdgcn_fdot2(a, b, c, false);
+}
+
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// ---- wave reductions -------------------------------------------------------------
+__device__ __forceinline__ float wave_sum_xor(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ void atomic_or_err(uint32_t* err, uint32_t bits) {
+  if (err) atomicOr(err, bits);
+}
+
+}  // namespace moe

@@ -1,0 +1,81 @@
+// Internal launcher interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace moe {
+
+struct RouterArgs {
+  const uint16_t* x;      // [T,H] fp16
+  const uint16_t* wr;     // [E,H] fp16
+  int T, E, H, k, renorm;
+  float* logits;          // [T,E] fp32 out
+  const int32_t* forced;  // [T,k] or null
+  int32_t* ids;           // [T,k] out
+  float* w;               // [T,k] out
+  uint32_t* err;
+  int exact_always;
+};
+void launch_router(const RouterArgs& a, hipStream_t stream);
+
+struct GroupArgs {
+  const int32_t* ids_in;    // [T,k] caller ids
+  int T, k, E;
+  const int32_t* slot_map;  // [E] expert -> slot, or null (identity)
+  int32_t* ids_s;           // [T,k] validated ids
+  ActiveExpert* active;     // [E]
+  int32_t* n_active;        // [1]
+  int32_t* perm_tok;        // [T*k] token at sorted position
+  int32_t* pos_of;          // [T*k] sorted position of pair t*k+j
+  uint32_t* err;
+};
+void launch_group(const GroupArgs& a, hipStream_t stream);
+
+struct ExpertArgs {
+  const uint8_t* blobs;       // expert storage of the layer (slot-indexed)
+  int64_t blob_stride;        // bytes per slot
+  BlobLayout lay;             // offsets inside one blob (for this expert kind)
+  const ActiveExpert* active; // routed mode: active list from the grouping
+  const int32_t* n_active;
+  int max_active;             // upper bound of *n_active (sizes the grid)
+  const uint8_t* fixed_blob;  // shared-expert mode: its blob (then active unused)
+  int fixed_count;            // shared-expert mode: tokens (= T)
+  int fixed_offset;           // shared-expert mode: first position
+  int H, I;
+  const uint16_t* x;          // [T,H] fp16 (gate/up input)
+  const int32_t* perm_tok;    // token at each sorted position (routed mode)
+  uint16_t* hbuf;             // [positions, I] fp16
+  float* ybuf;                // [positions, H] fp32
+};
+void launch_gateup_gemv(const ExpertArgs& a, hipStream_t stream);
+void launch_down_gemv(const ExpertArgs& a, hipStream_t stream);
+
+struct CombineArgs {
+  const float* ybuf;          // [P, H] routed outputs by sorted position
+  const float* yshared;       // [T, H] shared-expert output or null
+  const int32_t* pos_of;      // [T*k]
+  const float* w;             // [T*k]
+  int T, k, H;
+  uint16_t* out;              // [T,H] fp16 (if resid == null)
+  float* resid;               // [T,H] fp32: resid += combined (stack mode)
+};
+void launch_combine(const CombineArgs& a, hipStream_t stream);
+
+void launch_rmsnorm(const float* h, int T, int H, float eps, uint16_t* x, hipStream_t stream);
+
+struct PublishUpdate {
+  int32_t expert;
+  int32_t slot;  // -1 = evicted
+};
+constexpr int kMaxPublish = 64;
+struct PublishArgs {
+  int32_t* map;
+  int n;
+  PublishUpdate u[kMaxPublish];
+};
+void launch_publish(const PublishArgs& a, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,158 @@
+// Host-side decision procedure of the expert-slot pool (no HIP dependency).
+//
+// The pool keeps C slots per routed layer.  A routed group whose experts are all
+// resident reads existing copies; each miss takes a free slot or evicts a
+// resident expert outside the group, discarding its GPU copy ("Horizon RunMap",
+// "Partial-residency contract: immutable authority and miss lifecycle").
+// Victim rules: least recently used / least frequently used ("An
+// expert-offloading engine, from scratch", "Terms used here", "What the numbers
+// say"), and the score frequency*1000 - age with frequencies scaled by 0.75
+// after every 2*capacity misses ("F51 Nitro / Nitro-MoE", "Layer 1 - expert
+// persistence cache").
+//
+// Details the pages leave open, as implemented:
+//   - one clock tick per access call (one routed group);
+//   - the group is processed in ascending expert id, every hit first, then every
+//     miss; a miss takes the lowest-index free slot, else the victim with the
+//     smallest key among resident experts not in the group;
+//   - keys: LRU (last, id); LFU (count, last, id) with count = number of calls
+//     that named the expert, kept across evictions; LRU-FREQ
+//     (sfreq*1000 - (clock - last), id) in double, sfreq = 1 on fill and +1 per
+//     hit, all sfreq *= 0.75 right after the miss that completes each 2*C.
+#include "policy.hpp"
+
+#include <algorithm>
+
+namespace moe {
+
+PolicyEngine::PolicyEngine(int policy, int n_experts, int capacity, int layer)
+    : policy_(policy), E_(n_experts), C_(capacity), layer_(layer),
+      slot_of_(n_experts, -1), expert_in_(capacity, -1), last_(n_experts, 0),
+      count_(n_experts, 0), sfreq_(capacity, 0.0) {}
+
+#pragma clang fp contract(off)
+static inline double freq_score(double sfreq, int64_t clock, int64_t last) {
+  const double a = sfreq * 1000.0;
+  const double b = (double)(clock - last);
+  return a - b;
+}
+
+bool PolicyEngine::less_key(int a, int b) const {
+  // true when expert a is a better victim than expert b
+  switch (policy_) {
+    case 1:  // LRU
+      if (last_[a] != last_[b]) return last_[a] < last_[b];
+      return a < b;
+    case 2:  // LFU
+      if (count_[a] != count_[b]) return count_[a] < count_[b];
+      if (last_[a] != last_[b]) return last_[a] < last_[b];
+      return a < b;
+    default: {  // LRU-FREQ
+      const double sa = freq_score(sfreq_[slot_of_[a]], clock_, last_[a]);
+      const double sb = freq_score(sfreq_[slot_of_[b]], clock_, last_[b]);
+      if (sa != sb) return sa < sb;
+      return a < b;
+    }
+  }
+}
+
+int PolicyEngine::access(const int32_t* experts, int n, int step, std::vector<Decision>& out) {
+  out.clear();
+  if (n < 0) return 1;
+  if (n > C_) return 2;
+  std::vector<int32_t> g(experts, experts + n);
+  for (int e : g)
+    if (e < 0 || e >= E_) return 1;
+  std::sort(g.begin(), g.end());
+  for (int i = 1; i < n; ++i)
+    if (g[i] == g[i - 1]) return 1;
+  std::vector<char> in_group(E_, 0);
+  for (int e : g) in_group[e] = 1;
+
+  ++clock_;
+  std::vector<char> hit(n, 0);
+  for (int i = 0; i < n; ++i) {
+    const int e = g[i];
+    const int s = slot_of_[e];
+    if (s < 0) continue;
+    hit[i] = 1;
+    last_[e] = clock_;
+    count_[e] += 1;
+    sfreq_[s] += 1.0;
+    ++hits_;
+    out.push_back(Decision{e, s, -1, true});
+  }
+  for (int i = 0; i < n; ++i) {
+    if (hit[i]) continue;
+    const int e = g[i];
+    int slot = -1, victim = -1;
+    for (int s = 0; s < C_; ++s)
+      if (expert_in_[s] < 0) {
+        slot = s;
+        break;
+      }
+    if (slot < 0) {
+      for (int s = 0; s < C_; ++s) {
+        const int x = expert_in_[s];
+        if (in_group[x]) continue;
+        if (victim < 0 || less_key(x, victim)) victim = x;
+      }
+      slot = slot_of_[victim];
+      slot_of_[victim] = -1;
+    }
+    expert_in_[slot] = e;
+    slot_of_[e] = slot;
+    last_[e] = clock_;
+    count_[e] += 1;
+    sfreq_[slot] = 1.0;
+    ++misses_;
+    out.push_back(Decision{e, slot, victim, false});
+    if (policy_ == 3 && misses_ % (2 * (int64_t)C_) == 0)
+      for (double& f : sfreq_) f *= 0.75;
+  }
+  for (const Decision& d : out)
+    log_.push_back(moe_cache_event{step, layer_, d.expert, d.hit ? 1 : 0, d.slot, d.victim});
+  return 0;
+}
+
+}  // namespace moe
+
+// ---- C ABI of the host-only engine ---------------------------------------------
+struct moe_policy_engine {
+  moe::PolicyEngine eng;
+};
+
+extern "C" {
+
+moe_policy_engine* moe_policy_new(int32_t policy, int32_t n_experts, int32_t capacity,
+                                  int32_t layer) {
+  if (policy < 1 || policy > 3 || n_experts < 1 || capacity < 1) return nullptr;
+  return new moe_policy_engine{moe::PolicyEngine(policy, n_experts, capacity, layer)};
+}
+
+void moe_policy_free(moe_policy_engine* p) { delete p; }
+
+moe_status moe_policy_access(moe_policy_engine* p, const int32_t* experts, int32_t n,
+                             int32_t step, int32_t* slots) {
+  if (!p || (n > 0 && (!experts || !slots))) return MOE_E_ARG;
+  std::vector<moe::PolicyEngine::Decision> d;
+  const int rc = p->eng.access(experts, n, step, d);
+  if (rc == 1) return MOE_E_ARG;
+  if (rc == 2) return MOE_E_CAPACITY;
+  for (int i = 0; i < n; ++i) slots[i] = p->eng.slot_of(experts[i]);
+  return MOE_OK;
+}
+
+int32_t moe_policy_event_count(const moe_policy_engine* p) {
+  return p ? (int32_t)p->eng.log().size() : 0;
+}
+
+int32_t moe_policy_events(const moe_policy_engine* p, moe_cache_event* buf, int32_t cap) {
+  if (!p || !buf || cap <= 0) return 0;
+  const auto& lg = p->eng.log();
+  const int32_t n = std::min<int32_t>(cap, (int32_t)lg.size());
+  std::copy(lg.begin(), lg.begin() + n, buf);
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Slot-pool decision engine (host only, no HIP dependency).
+#pragma once
+
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/moe_w4a16.h"
+
+namespace moe {
+
+class PolicyEngine {
+ public:
+  struct Decision {
+    int32_t expert;
+    int32_t slot;
+    int32_t victim;  // -1 if none
+    bool hit;
+  };
+
+  PolicyEngine(int policy, int n_experts, int capacity, int layer);
+
+  // One routed group.  Returns 0 on success, 1 for a bad or repeated id,
+  // 2 when n exceeds the capacity; on failure nothing changes.  `out` gets
+  // the decisions in event order (hits ascending, then misses ascending).
+  int access(const int32_t* experts, int n, int step, std::vector<Decision>& out);
+
+  int32_t slot_of(int e) const { return slot_of_[e]; }
+  const std::vector<moe_cache_event>& log() const { return log_; }
+  int64_t hits() const { return hits_; }
+  int64_t misses() const { return misses_; }
+  int capacity() const { return C_; }
+
+ private:
+  bool less_key(int a, int b) const;
+
+  int policy_, E_, C_, layer_;
+  int64_t clock_ = 0, misses_ = 0, hits_ = 0;
+  std::vector<int32_t> slot_of_;    // expert -> slot or -1
+  std::vector<int32_t> expert_in_;  // slot -> expert or -1
+  std::vector<int64_t> last_;       // expert -> clock of last use
+  std::vector<int64_t> count_;      // expert -> calls that named it
+  std::vector<double> sfreq_;       // slot -> LRU-FREQ frequency
+  std::vector<moe_cache_event> log_;
+};
+
+}  // namespace moe
