@@ -93,6 +93,8 @@ typedef enum moe_policy {
                                            path is skipped); results are equal */
 #define MOE_FLAG_FORCE_GEMV 2u          /* never take the MFMA expert path     */
 #define MOE_FLAG_FORCE_MFMA 4u          /* take the MFMA path for every expert */
+#define MOE_FLAG_NO_FUSED 8u            /* stacks: never take the fused one-launch
+                                           decode path (use per-layer kernels)  */
 
 typedef struct moe_config {
   int32_t hidden;          /* H, multiple of 256                                  */
@@ -203,7 +205,11 @@ moe_status moe_expert_forward(moe_ctx* ctx, int32_t layer, const void* x, int32_
  * by absolute layer, or NULL.  x_trace (dev FP16 [L,T,H]), ids_trace
  * (dev int32 [L,T,k]) and w_trace (dev FP32 [L,T,k]) receive each layer's
  * x, ids and w when non-NULL (indexed by absolute layer).  With a slot pool
- * forced_ids is required and each layer's group must have been ensured. */
+ * forced_ids is required and each layer's group must have been ensured.
+ * Small batches (T <= 8, T*k <= 64, T*E <= 4096, H = 2048, I in {512, 1024},
+ * shared_inter in {0, I}) run as one persistent kernel per call; others run
+ * the per-layer kernels.  Both give results within the stated tolerance and
+ * each is deterministic. */
 moe_status moe_stack_forward(moe_ctx* ctx, int32_t layer_begin, int32_t layer_end, float* h,
                              int32_t T, const int32_t* forced_ids, void* x_trace,
                              int32_t* ids_trace, float* w_trace, void* stream);
@@ -211,8 +217,20 @@ moe_status moe_stack_forward(moe_ctx* ctx, int32_t layer_begin, int32_t layer_en
 /* Synchronises `stream`, reads and clears the device error word.  Returns
  * MOE_OK if it was zero, else MOE_E_DEVICE with *bits (if non-NULL) set:
  * 1 = expert id out of range, 2 = expert repeated within a token,
- * 4 = expert not resident in the slot pool. */
+ * 4 = expert not resident in the slot pool, 8 = a grid barrier of the fused
+ * decode path timed out (its results are then meaningless). */
 moe_status moe_check_device_errors(moe_ctx* ctx, void* stream, uint32_t* bits);
+
+/* ---- instrumentation -------------------------------------------------------------
+ * Kernel timer: while enabled for a kernel kind, every launch of that kind is
+ * bracketed by a HIP event pair recorded on the stream it is launched on.
+ * Kinds: 0 router logits, 1 top-k, 2 grouping, 3 gate/up + SwiGLU,
+ * 4 down projection, 5 combine, 6 RMSNorm, 7 fused decode (whole stack call).
+ * kind = -1 disables.
+ * moe_timer_read synchronises the recorded events, returns the summed
+ * elapsed milliseconds and the number of launches, and resets both. */
+moe_status moe_timer_enable(moe_ctx* ctx, int32_t kind);
+moe_status moe_timer_read(moe_ctx* ctx, double* total_ms, int64_t* launches);
 
 /* ---- expert-slot pool (partial residency) ------------------------------------ */
 

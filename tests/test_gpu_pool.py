@@ -1,0 +1,163 @@
+"""Partial residency: an HBM expert-slot pool per layer backed by pinned host
+memory.  Outputs must be bit-identical to full residency; hit/miss/eviction
+sequences must equal the oracle's decisions; counters must add up."""
+import numpy as np
+import pytest
+import torch
+
+from fixtures import moe_inputs as fx
+from oracle import moe_oracle as ora
+
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+L = 16
+STEPS = 256
+POLICY_ORACLE = {"lru": ora.LRU, "lfu": ora.LFU, "lru_freq": ora.LRU_FREQ}
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import w4a16_routed_expert_router_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def olmoe_layers():
+    return [{k: v.cpu().numpy() for k, v in
+             fx.layer_weights(fx.OLMOE, "pool-olmoe", l, device="cuda", batched=True).items()}
+            for l in range(L)]
+
+
+@pytest.fixture(scope="module")
+def trace():
+    return fx.zipf_trace("pool-zipf", STEPS, L, fx.OLMOE.n_experts, fx.OLMOE.top_k, s=1.1)
+
+
+@pytest.fixture(scope="module")
+def h0s():
+    return torch.stack([fx.activations(("pool-h0", i), 1, fx.OLMOE.hidden, device="cuda").float()
+                        for i in range(32)])
+
+
+def _ctx(moe, layers, **kw):
+    ctx = moe.MoEContext(fx.OLMOE, n_layers=L, max_tokens=1, **kw)
+    for l, w in enumerate(layers):
+        ctx.register_layer(l, w)
+    return ctx
+
+
+def _run(ctx, trace, h0s, pooled, steps=STEPS, flags_check=True):
+    outs = []
+    ftr = torch.from_numpy(trace[:, :, None, :].copy()).cuda()     # [S, L, 1, k]
+    for s in range(steps):
+        if pooled:
+            for l in range(L):
+                ctx.cache_ensure(l, trace[s, l], step=s)
+        h = h0s[s % len(h0s)].clone()
+        ctx.stack_forward(h, forced_ids=ftr[s])
+        outs.append(h)
+    torch.cuda.synchronize()
+    if flags_check:
+        assert ctx.check_device_errors() == 0
+    return torch.stack(outs)
+
+
+@pytest.fixture(scope="module")
+def resident_out(moe, olmoe_layers, trace, h0s):
+    ctx = _ctx(moe, olmoe_layers)
+    out = _run(ctx, trace, h0s, pooled=False)
+    ctx.close()
+    return out
+
+
+@pytest.mark.parametrize("policy,C", [("lru", 16), ("lfu", 16), ("lfu", 32), ("lru", 48),
+                                      ("lru_freq", 16)])
+def test_pool_bit_identical_and_decisions_match_oracle(moe, olmoe_layers, trace, h0s,
+                                                       resident_out, policy, C):
+    say(f"test_pool policy={policy} C={C}")
+    ctx = _ctx(moe, olmoe_layers, policy=policy, slots=C)
+    out = _run(ctx, trace, h0s, pooled=True)
+    assert torch.equal(out, resident_out), "cache changed the output"
+    blob = fx.OLMOE.blob_bytes
+    hit_rates = []
+    for l in range(L):
+        sim = ora.CacheSim(POLICY_ORACLE[policy], fx.OLMOE.n_experts, C, layer=l)
+        for s in range(STEPS):
+            sim.ensure(trace[s, l].tolist(), s)
+        assert ctx.cache_events(l) == [e.as_tuple() for e in sim.events], f"layer {l}"
+        st = ctx.cache_stats(l)
+        assert st["accesses"] == STEPS * fx.OLMOE.top_k
+        assert st["hits"] + st["misses"] == st["accesses"] and st["hits"] == sim.hits
+        assert st["misses"] == sim.misses and st["h2d_bytes"] == sim.misses * blob
+        assert st["evictions"] == sum(1 for e in sim.events if e.victim >= 0)
+        assert st["d2h_bytes"] == 0 and st["failures"] == 0
+        assert st["h2d_seconds"] > 0
+        hit_rates.append(st["hits"] / st["accesses"])
+    say(f"  mean hit rate {np.mean(hit_rates):.3f}")
+    ctx.close()
+
+
+def test_pool_transfer_failure_before_publication_keeps_state(moe, olmoe_layers, trace, h0s,
+                                                              resident_out):
+    say("test_pool_transfer_failure_before_publication_keeps_state")
+    ctx = _ctx(moe, olmoe_layers, policy="lfu", slots=16)
+    _run(ctx, trace, h0s, pooled=True, steps=10)
+    before = ctx.cache_events(3), ctx.cache_stats(3)
+    # a group of experts that are not resident after those 10 steps (all misses)
+    sim = ora.CacheSim(ora.LFU, fx.OLMOE.n_experts, 16, layer=3)
+    for s in range(10):
+        sim.ensure(trace[s, 3].tolist(), s)
+    miss_group = np.array([e for e in range(fx.OLMOE.n_experts) if e not in sim.slot_of][:8],
+                          dtype=np.int32)
+    ctx.inject_transfer_failure(3, 1)
+    with pytest.raises(moe.MoEError) as ei:
+        ctx.cache_ensure(3, miss_group, step=99)
+    assert ei.value.status == 7          # MOE_E_TRANSFER
+    after = ctx.cache_events(3), ctx.cache_stats(3)
+    assert after[0] == before[0]
+    assert after[1]["misses"] == before[1]["misses"] and after[1]["failures"] == 1
+    # the context keeps working and stays exact
+    ctx.cache_ensure(3, miss_group, step=99)
+    ctx.close()
+
+
+def test_pool_failure_after_publication_faults_context(moe, olmoe_layers):
+    say("test_pool_failure_after_publication_faults_context")
+    ctx = _ctx(moe, olmoe_layers, policy="lru", slots=16)
+    ctx.inject_transfer_failure(0, 2)
+    with pytest.raises(moe.MoEError) as ei:
+        ctx.cache_ensure(0, np.arange(8, dtype=np.int32))
+    assert ei.value.status == 8          # MOE_E_FAULTED
+    with pytest.raises(moe.MoEError):
+        ctx.cache_ensure(0, np.arange(8, dtype=np.int32))
+    assert ctx.cache_stats(0)["failures"] == 1     # stats still readable
+    ctx.close()
+
+
+def test_pool_capacity_and_residency_errors(moe, olmoe_layers):
+    say("test_pool_capacity_and_residency_errors")
+    with pytest.raises(moe.MoEError) as ei:
+        moe.MoEContext(fx.OLMOE, n_layers=1, max_tokens=4, policy="lru", slots=16)  # 4*8 > 16
+    assert ei.value.status == 5
+    ctx = _ctx(moe, olmoe_layers, policy="lru", slots=16)
+    with pytest.raises(moe.MoEError) as ei:
+        ctx.cache_ensure(0, np.arange(17, dtype=np.int32))
+    assert ei.value.status == 5
+    # running experts that were never made resident is contained and reported
+    h = torch.zeros((1, fx.OLMOE.hidden), dtype=torch.float32, device="cuda")
+    h[0, 0] = 1.0
+    forced = torch.arange(8, dtype=torch.int32, device="cuda").reshape(1, 1, 8).repeat(L, 1, 1)
+    ctx.stack_forward(h, forced_ids=forced)
+    bits = ctx.check_device_errors()
+    assert bits & 4
+    ctx.close()
+
+
+def test_pool_resident_all_ensure_is_identity(moe, olmoe_layers):
+    ctx = _ctx(moe, olmoe_layers[:1] * L)
+    g = np.array([5, 1, 9], dtype=np.int32)
+    assert ctx.cache_ensure(0, g).tolist() == [5, 1, 9]
+    assert ctx.cache_events(0) == []
+    ctx.close()

@@ -14,7 +14,7 @@ import torch
 
 from . import capi
 from .capi import (MOE_FLAG_FORCE_GEMV, MOE_FLAG_FORCE_MFMA,  # noqa: F401
-                   MOE_FLAG_ROUTER_EXACT_ALWAYS, MOE_POLICY_LFU, MOE_POLICY_LRU,
+                   MOE_FLAG_NO_FUSED, MOE_FLAG_ROUTER_EXACT_ALWAYS, MOE_POLICY_LFU, MOE_POLICY_LRU,
                    MOE_POLICY_LRU_FREQ, MOE_RESIDENT_ALL, MoEError)
 
 _lib = capi.load()
@@ -180,6 +180,18 @@ class MoEContext:
         buf = (capi.moe_cache_event * cap)()
         self._check(_lib.moe_cache_event_log(self._h, layer, buf, cap, C.byref(n)))
         return [buf[i].as_tuple() for i in range(n.value)]
+
+    KERNEL_KINDS = {"logits": 0, "topk": 1, "group": 2, "gateup": 3, "down": 4, "combine": 5,
+                    "rmsnorm": 6, "fused": 7}
+
+    def timer_enable(self, kind):
+        self._check(_lib.moe_timer_enable(self._h, -1 if kind is None else self.KERNEL_KINDS[kind]))
+
+    def timer_read(self):
+        ms = C.c_double(0.0)
+        n = C.c_int64(0)
+        self._check(_lib.moe_timer_read(self._h, C.byref(ms), C.byref(n)))
+        return ms.value, n.value
 
     def inject_transfer_failure(self, layer, mode):
         self._check(_lib.moe_debug_inject_transfer_failure(self._h, layer, mode))

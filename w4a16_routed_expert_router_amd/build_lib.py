@@ -1,6 +1,6 @@
 """Compile the HIP library libmoe_w4a16.so for gfx950 (in-tree).
 
-Usage: python -m w4a16_routed_expert_router_amd.build_lib
+Usage: python w4a16_routed_expert_router_amd/build_lib.py  (or __graft_entry__.build())
 """
 from __future__ import annotations
 
@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_w4a16.so")
 
-SOURCES = ["api.hip", "router.hip", "group.hip", "expert_gemv.hip", "expert_mfma.hip", "policy.cpp"]
+SOURCES = ["api.hip", "router.hip", "group.hip", "expert_gemv.hip", "decode_fused.hip", "policy.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

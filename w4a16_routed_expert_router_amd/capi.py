@@ -22,6 +22,7 @@ MOE_RESIDENT_ALL, MOE_POLICY_LRU, MOE_POLICY_LFU, MOE_POLICY_LRU_FREQ = 0, 1, 2,
 MOE_FLAG_ROUTER_EXACT_ALWAYS = 1
 MOE_FLAG_FORCE_GEMV = 2
 MOE_FLAG_FORCE_MFMA = 4
+MOE_FLAG_NO_FUSED = 8
 
 
 class moe_config(C.Structure):
@@ -62,6 +63,8 @@ SIGNATURES = {
     "moe_cache_stats": (_I, [_P, _I, C.POINTER(moe_cache_counters)]),
     "moe_cache_event_log": (_I, [_P, _I, C.POINTER(moe_cache_event), _I, C.POINTER(_I)]),
     "moe_debug_inject_transfer_failure": (_I, [_P, _I, _I]),
+    "moe_timer_enable": (_I, [_P, _I]),
+    "moe_timer_read": (_I, [_P, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
     "moe_policy_new": (_P, [_I, _I, _I, _I]),
     "moe_policy_free": (None, [_P]),
     "moe_policy_access": (_I, [_P, _P, _I, _I, _P]),
@@ -83,7 +86,7 @@ def load() -> C.CDLL:
         if not os.path.exists(_LIB_PATH):
             raise ImportError(
                 f"{_LIB_PATH} is missing: build it with "
-                "`python -m w4a16_routed_expert_router_amd.build_lib`")
+                "`python w4a16_routed_expert_router_amd/build_lib.py`")
         lib = C.CDLL(_LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)

@@ -71,6 +71,15 @@ struct moe_ctx {
   hipStream_t side = nullptr;
   std::string last_error;
   bool faulted = false;
+  // fused decode path
+  std::vector<FusedLayer> hlayers;
+  FusedLayer* dlayers = nullptr;
+  uint32_t* flags = nullptr;
+  int grid = 0;
+  // kernel timer
+  int timer_kind = -1;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> timer_events;
+  size_t timer_used = 0;
 };
 
 namespace {
@@ -149,9 +158,52 @@ moe_status check_layer(moe_ctx* c, int layer) {
 
 bool pooled(const moe_ctx* c) { return c->cfg.policy != MOE_RESIDENT_ALL; }
 
+enum KernelKind {
+  kKindLogits = 0, kKindTopk, kKindGroup, kKindGateUp, kKindDown, kKindCombine, kKindNorm, kKindFused
+};
+
+bool fused_eligible(const moe_ctx* c, int T) {
+  const moe_config& g = c->cfg;
+  if (g.flags & MOE_FLAG_NO_FUSED) return false;
+  if (T > kFMaxT || T * g.top_k > kFMaxP || T * g.n_experts > kFMaxTE) return false;
+  if (((g.n_experts + 63) / 64) * g.top_k > kFMaxCand) return false;
+  if (g.shared_inter != 0 && g.shared_inter != g.inter) return false;
+  return c->grid > 0 && fused_supported(g.hidden, g.inter);
+}
+
+// Brackets one launch with a recorded event pair when the timer is on for `kind`.
+struct ScopedTimer {
+  moe_ctx* c;
+  hipStream_t s;
+  hipEvent_t stop = nullptr;
+  ScopedTimer(moe_ctx* ctx, int kind, hipStream_t stream) : c(ctx), s(stream) {
+    if (c->timer_kind != kind) return;
+    if (c->timer_used == c->timer_events.size()) {
+      hipEvent_t a = nullptr, b = nullptr;
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
+      c->timer_events.emplace_back(a, b);
+    }
+    auto& p = c->timer_events[c->timer_used++];
+    (void)hipEventRecord(p.first, s);
+    stop = p.second;
+  }
+  ~ScopedTimer() {
+    if (stop) (void)hipEventRecord(stop, s);
+  }
+};
+
 int max_active(const moe_ctx* c, int T) {
   const int64_t p = (int64_t)T * c->cfg.top_k;
   return (int)(p < c->cfg.n_experts ? p : c->cfg.n_experts);
+}
+
+void run_router(moe_ctx* c, const RouterArgs& ra, hipStream_t s) {
+  {
+    ScopedTimer tm(c, kKindLogits, s);
+    launch_router_logits(ra, s);
+  }
+  ScopedTimer tm(c, kKindTopk, s);
+  launch_router_topk(ra, s);
 }
 
 // group -> gate/up -> down (routed and shared) -> combine into out or resid.
@@ -161,7 +213,10 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   const moe_config& g = c->cfg;
   GroupArgs ga{ids, T, g.top_k, g.n_experts, L.map, c->ids_s, c->active, c->n_active,
                c->perm_tok, c->pos_of, c->err};
-  launch_group(ga, s);
+  {
+    ScopedTimer tm(c, kKindGroup, s);
+    launch_group(ga, s);
+  }
   ExpertArgs ea{};
   ea.blobs = L.store;
   ea.blob_stride = c->lay.total();
@@ -175,8 +230,14 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   ea.perm_tok = c->perm_tok;
   ea.hbuf = c->hbuf;
   ea.ybuf = c->ybuf;
-  launch_gateup_gemv(ea, s);
-  launch_down_gemv(ea, s);
+  {
+    ScopedTimer tm(c, kKindGateUp, s);
+    launch_gateup_gemv(ea, s);
+  }
+  {
+    ScopedTimer tm(c, kKindDown, s);
+    launch_down_gemv(ea, s);
+  }
   if (g.shared_inter) {
     ExpertArgs sa = ea;
     sa.lay = c->shared_lay;
@@ -191,7 +252,10 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   }
   CombineArgs ca{c->ybuf, g.shared_inter ? c->yshared : nullptr, c->pos_of, w, T, g.top_k,
                  g.hidden, out, resid};
-  launch_combine(ca, s);
+  {
+    ScopedTimer tm(c, kKindCombine, s);
+    launch_combine(ca, s);
+  }
   if (pooled(c)) HIPCHK(c, hipEventRecord(L.retired, s));
   HIPCHK(c, hipGetLastError());
   return MOE_OK;
@@ -273,7 +337,17 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ok = ok && dalloc((void**)&c->n_active, 4);
   ok = ok && dalloc((void**)&c->perm_tok, (size_t)P * 4);
   ok = ok && dalloc((void**)&c->pos_of, (size_t)P * 4);
-  ok = ok && dalloc((void**)&c->hbuf, (size_t)P * Imax * 2);
+  // rows: routed (token, rank) pairs, then the shared expert's tokens
+  ok = ok && dalloc((void**)&c->hbuf, (size_t)(P + g.max_tokens) * std::max(Imax, g.shared_inter) * 2);
+  ok = ok && dalloc((void**)&c->dlayers, (size_t)g.n_layers * sizeof(FusedLayer));
+  c->hlayers.assign(g.n_layers, FusedLayer{nullptr, nullptr, nullptr, nullptr});
+  {
+    int ncu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, g.device) != hipSuccess) ncu = 0;
+    c->grid = ncu;
+    ok = ok && dalloc((void**)&c->flags, (size_t)std::max(ncu, 1) * 4);
+    if (ok) ok = hipMemset(c->flags, 0, (size_t)std::max(ncu, 1) * 4) == hipSuccess;
+  }
   ok = ok && dalloc((void**)&c->ybuf, (size_t)P * g.hidden * 4);
   ok = ok && dalloc((void**)&c->xbuf, (size_t)g.max_tokens * g.hidden * 2);
   ok = ok && dalloc((void**)&c->err, 4);
@@ -312,9 +386,14 @@ void moe_destroy(moe_ctx* c) {
     }
   }
   void* bufs[] = {c->logits, c->ids,  c->w,    c->ids_s,   c->active,  c->n_active, c->perm_tok,
-                  c->pos_of, c->hbuf, c->ybuf, c->xbuf,    c->err,     c->hshared,  c->yshared};
+                  c->pos_of, c->hbuf, c->ybuf, c->xbuf,    c->err,     c->hshared,  c->yshared,
+                  c->dlayers, c->flags};
   for (void* p : bufs) (void)hipFree(p);
   if (c->side) (void)hipStreamDestroy(c->side);
+  for (auto& p : c->timer_events) {
+    (void)hipEventDestroy(p.first);
+    (void)hipEventDestroy(p.second);
+  }
   delete c;
 }
 
@@ -359,6 +438,8 @@ moe_status moe_register_layer(moe_ctx* c, int32_t layer, const uint16_t* router,
     repack_expert(shared_q, shared_s, scb, ssc, tmp.data());
     HIPCHK(c, hipMemcpy(L.shared, tmp.data(), tmp.size(), hipMemcpyHostToDevice));
   }
+  c->hlayers[layer] = FusedLayer{L.router, L.store, L.map, L.shared};
+  HIPCHK(c, hipMemcpy(c->dlayers + layer, &c->hlayers[layer], sizeof(FusedLayer), hipMemcpyHostToDevice));
   L.registered = true;
   return MOE_OK;
 }
@@ -373,7 +454,7 @@ moe_status moe_route(moe_ctx* c, int32_t layer, const void* x, int32_t T, const 
   RouterArgs ra{(const uint16_t*)x, c->layers[layer].router, T, g.n_experts, g.hidden, g.top_k,
                 g.renorm, logits ? logits : c->logits, forced_ids, ids, w, c->err,
                 (int)(g.flags & MOE_FLAG_ROUTER_EXACT_ALWAYS)};
-  launch_router(ra, (hipStream_t)stream);
+  run_router(c, ra, (hipStream_t)stream);
   HIPCHK(c, hipGetLastError());
   return MOE_OK;
 }
@@ -403,15 +484,50 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t layer_begin, int32_t layer_end,
   if (pooled(c) && !forced_ids) return fail(c, MOE_E_ARG, "a slot pool needs forced_ids");
   hipStream_t s = (hipStream_t)stream;
   const int64_t tk = (int64_t)T * g.top_k, th = (int64_t)T * g.hidden;
+  if (fused_eligible(c, T)) {
+    FusedArgs fa{};
+    fa.layers = c->dlayers;
+    fa.l0 = layer_begin;
+    fa.l1 = layer_end;
+    fa.T = T;
+    fa.E = g.n_experts;
+    fa.I = g.inter;
+    fa.k = g.top_k;
+    fa.renorm = g.renorm;
+    fa.has_shared = g.shared_inter ? 1 : 0;
+    fa.exact_always = (int)(g.flags & MOE_FLAG_ROUTER_EXACT_ALWAYS);
+    fa.lay = c->lay;
+    fa.blob_stride = c->lay.total();
+    fa.h = h;
+    fa.logits = c->logits;
+    fa.hbuf = c->hbuf;
+    fa.forced = forced_ids;
+    fa.x_trace = (uint16_t*)x_trace;
+    fa.ids_trace = ids_trace;
+    fa.w_trace = w_trace;
+    fa.flags = c->flags;
+    fa.err = c->err;
+    {
+      ScopedTimer tm(c, kKindFused, s);
+      launch_fused_decode(fa, c->grid, s);
+    }
+    HIPCHK(c, hipGetLastError());
+    if (pooled(c))
+      for (int l = layer_begin; l < layer_end; ++l) HIPCHK(c, hipEventRecord(c->layers[l].retired, s));
+    return MOE_OK;
+  }
   for (int l = layer_begin; l < layer_end; ++l) {
     uint16_t* x = x_trace ? (uint16_t*)x_trace + l * th : c->xbuf;
     int32_t* ids = ids_trace ? ids_trace + l * tk : c->ids;
     float* w = w_trace ? w_trace + l * tk : c->w;
-    launch_rmsnorm(h, T, g.hidden, 1e-5f, x, s);
+    {
+      ScopedTimer tm(c, kKindNorm, s);
+      launch_rmsnorm(h, T, g.hidden, 1e-5f, x, s);
+    }
     RouterArgs ra{x, c->layers[l].router, T, g.n_experts, g.hidden, g.top_k, g.renorm, c->logits,
                   forced_ids ? forced_ids + l * tk : nullptr, ids, w, c->err,
                   (int)(g.flags & MOE_FLAG_ROUTER_EXACT_ALWAYS)};
-    launch_router(ra, s);
+    run_router(c, ra, s);
     if (moe_status st = run_experts(c, l, x, T, ids, w, nullptr, h, s)) return st;
   }
   return MOE_OK;
@@ -544,6 +660,29 @@ moe_status moe_cache_event_log(const moe_ctx* c, int32_t layer, moe_cache_event*
   if (m > 0 && !buf) return MOE_E_ARG;
   for (int32_t i = 0; i < m; ++i) buf[i] = lg[i];
   *n = m;
+  return MOE_OK;
+}
+
+moe_status moe_timer_enable(moe_ctx* c, int32_t kind) {
+  if (!c) return MOE_E_ARG;
+  if (kind < -1 || kind > kKindFused) return fail(c, MOE_E_ARG, "unknown kernel kind");
+  c->timer_kind = kind;
+  return MOE_OK;
+}
+
+moe_status moe_timer_read(moe_ctx* c, double* total_ms, int64_t* launches) {
+  if (!c || !total_ms || !launches) return MOE_E_ARG;
+  double tot = 0.0;
+  for (size_t i = 0; i < c->timer_used; ++i) {
+    auto& p = c->timer_events[i];
+    HIPCHK(c, hipEventSynchronize(p.second));
+    float ms = 0.0f;
+    HIPCHK(c, hipEventElapsedTime(&ms, p.first, p.second));
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = (int64_t)c->timer_used;
+  c->timer_used = 0;
   return MOE_OK;
 }
 

@@ -16,6 +16,7 @@ constexpr int kGroup = 128;  // INT4 quantisation group along K
 constexpr uint32_t kErrBadId = 1u;
 constexpr uint32_t kErrDupId = 2u;
 constexpr uint32_t kErrNotResident = 4u;
+constexpr uint32_t kErrBarrier = 8u;
 
 // One active expert of a call, produced by the grouping kernel.
 struct ActiveExpert {

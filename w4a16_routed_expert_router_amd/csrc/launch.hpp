@@ -19,7 +19,8 @@ struct RouterArgs {
   uint32_t* err;
   int exact_always;
 };
-void launch_router(const RouterArgs& a, hipStream_t stream);
+void launch_router_logits(const RouterArgs& a, hipStream_t stream);
+void launch_router_topk(const RouterArgs& a, hipStream_t stream);
 
 struct GroupArgs {
   const int32_t* ids_in;    // [T,k] caller ids
@@ -65,6 +66,35 @@ struct CombineArgs {
 void launch_combine(const CombineArgs& a, hipStream_t stream);
 
 void launch_rmsnorm(const float* h, int T, int H, float eps, uint16_t* x, hipStream_t stream);
+
+// Fused persistent decode path (decode_fused.hip)
+constexpr int kFMaxT = 8;      // tokens per call
+constexpr int kFMaxP = 64;     // (token, rank) pairs per call
+constexpr int kFMaxTE = 4096;  // T * E
+constexpr int kFMaxCand = 128; // ceil(E/64) * k
+struct FusedLayer {
+  const uint16_t* router;
+  const uint8_t* store;
+  const int32_t* map;
+  const uint8_t* shared;
+};
+struct FusedArgs {
+  const FusedLayer* layers;   // device array, indexed by absolute layer
+  int l0, l1, T, E, I, k, renorm, has_shared, exact_always;
+  BlobLayout lay;             // routed and shared blobs (shared inter == inter)
+  int64_t blob_stride;
+  float* h;                   // [T,H] residual, updated in place
+  float* logits;              // [T,E] scratch
+  uint16_t* hbuf;             // [(T*k + T), I] fp16 scratch
+  const int32_t* forced;      // [L,T,k] or null
+  uint16_t* x_trace;
+  int32_t* ids_trace;
+  float* w_trace;
+  uint32_t* flags;            // [grid] barrier flags
+  uint32_t* err;
+};
+bool fused_supported(int H, int I);
+void launch_fused_decode(const FusedArgs& a, int grid, hipStream_t stream);
 
 struct PublishUpdate {
   int32_t expert;

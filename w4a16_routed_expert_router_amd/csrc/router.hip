@@ -18,85 +18,13 @@
 //      as a 128-bit fixed-point integer (unit 2^-48) and rounds it once.
 #include "common.hpp"
 #include "launch.hpp"
+#include "exact_dot.hpp"
 
 namespace moe {
 
 constexpr int kRtTok = 4;  // tokens per logits work item
 constexpr int kRtExp = 4;  // experts per logits work item
 constexpr int kCombos = kRtTok * kRtExp;
-
-__device__ __forceinline__ void f16_fixed(uint16_t b, int32_t& m, int32_t& sh) {
-  // FP16 value = m * 2^sh * 2^-24 with |m| < 2^11, 0 <= sh <= 29.
-  const int32_t e = (b >> 10) & 0x1F;
-  const int32_t f = b & 0x3FF;
-  if (e == 0) {
-    m = f;
-    sh = 0;
-  } else {
-    m = 1024 + f;
-    sh = e - 1;
-  }
-  if (b & 0x8000) m = -m;
-}
-
-__device__ __forceinline__ int clz128(unsigned __int128 v) {
-  const uint64_t hi = (uint64_t)(v >> 64);
-  const uint64_t lo = (uint64_t)v;
-  return hi ? __clzll(hi) : 64 + (lo ? __clzll(lo) : 64);
-}
-
-// Nearest FP32 (ties to even) to S * 2^exp2; S*2^exp2 is always in FP32's
-// normal range here (|S| < 2^92, exp2 = -48).
-__device__ float round_i128_to_f32(__int128 S, int exp2) {
-  if (S == 0) return 0.0f;
-  const bool neg = S < 0;
-  const unsigned __int128 m = neg ? (unsigned __int128)(-S) : (unsigned __int128)S;
-  const int nb = 128 - clz128(m);
-  float f;
-  if (nb <= 24) {
-    f = ldexpf((float)(uint32_t)m, exp2);
-  } else {
-    const int sh = nb - 24;
-    unsigned __int128 q = m >> sh;
-    const unsigned __int128 r = m & ((((unsigned __int128)1) << sh) - 1);
-    const unsigned __int128 half = ((unsigned __int128)1) << (sh - 1);
-    if (r > half || (r == half && (q & 1))) q += 1;
-    f = ldexpf((float)(uint32_t)q, sh + exp2);  // q <= 2^24: exact
-  }
-  return neg ? -f : f;
-}
-
-// Exact dot product of FP16 rows a, b of length H, over the whole wave.
-// Every lane returns the correctly rounded FP32 result.
-__device__ float exact_dot_wave(const uint16_t* a, const uint16_t* b, int H, int lane) {
-  __int128 acc = 0;
-  for (int k = lane * 8; k < H; k += kWave * 8) {
-    const uint4 av = *reinterpret_cast<const uint4*>(a + k);
-    const uint4 bv = *reinterpret_cast<const uint4*>(b + k);
-    const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
-    const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint16_t ah = (uint16_t)(aw[i >> 1] >> (16 * (i & 1)));
-      const uint16_t bh = (uint16_t)(bw[i >> 1] >> (16 * (i & 1)));
-      int32_t ma, sa, mb, sb;
-      f16_fixed(ah, ma, sa);
-      f16_fixed(bh, mb, sb);
-      acc += ((__int128)(ma * mb)) << (sa + sb);
-    }
-  }
-  uint64_t lo = (uint64_t)acc;
-  int64_t hi = (int64_t)(acc >> 64);
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const uint64_t lo2 = __shfl_xor(lo, o, kWave);
-    const int64_t hi2 = __shfl_xor(hi, o, kWave);
-    const uint64_t nlo = lo + lo2;
-    hi = hi + hi2 + (nlo < lo ? 1 : 0);
-    lo = nlo;
-  }
-  const __int128 S = (((__int128)hi) << 64) | (__int128)lo;
-  return round_i128_to_f32(S, -48);
-}
 
 // Sum 2*kCombos doubles across the wave, each lane keeping one index:
 // afterwards lane l holds the full sum of value index (l >> 1) in v[0].
@@ -279,10 +207,13 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict
   }
 }
 
-void launch_router(const RouterArgs& a, hipStream_t stream) {
+void launch_router_logits(const RouterArgs& a, hipStream_t stream) {
   dim3 g1((a.E + kRtExp - 1) / kRtExp, (a.T + kRtTok - 1) / kRtTok);
   hipLaunchKernelGGL(router_logits_kernel, g1, dim3(64), 0, stream, a.x, a.wr, a.T, a.E, a.H,
                      a.logits, a.exact_always);
+}
+
+void launch_router_topk(const RouterArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(router_topk_kernel, dim3(a.T), dim3(64), 0, stream, a.logits, a.T, a.E,
                      a.k, a.renorm, a.forced, a.ids, a.w, a.err);
 }
