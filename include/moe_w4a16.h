@@ -232,6 +232,19 @@ moe_status moe_check_device_errors(moe_ctx* ctx, void* stream, uint32_t* bits);
 moe_status moe_timer_enable(moe_ctx* ctx, int32_t kind);
 moe_status moe_timer_read(moe_ctx* ctx, double* total_ms, int64_t* launches);
 
+/* Phase timestamps of the fused decode path: with dev_buf (device, uint64,
+ * caller-owned, at least 2*grid*stride entries) set, every block of later
+ * fused launches writes the GPU's 100 MHz real-time counter at each phase
+ * boundary to dev_buf[block*stride + (layer - layer_begin)*per_layer + event]
+ * and its shader-clock counter at the same index + grid*stride; events
+ * 0 layer start, 1 norm done, 2 logits done, 3 after barrier A, 4 logits in
+ * LDS, 5 ranking done, 6 selection and grouping done, 7 gate/up done, 8 after
+ * barrier B, 9 down done, 10 after barrier C.
+ * dev_buf NULL disables.  grid, stride and per_layer (optional outputs)
+ * receive the layout. */
+moe_status moe_fused_phase_stamps(moe_ctx* ctx, uint64_t* dev_buf, int64_t count, int32_t* grid,
+                                  int32_t* stride, int32_t* per_layer);
+
 /* ---- expert-slot pool (partial residency) ------------------------------------ */
 
 /* ensure() of the slot pool of `layer` for one routed group.

@@ -193,6 +193,21 @@ class MoEContext:
         self._check(_lib.moe_timer_read(self._h, C.byref(ms), C.byref(n)))
         return ms.value, n.value
 
+    def phase_stamps(self, enable=True):
+        """Turn the fused path's phase timestamps on (returns the device buffer,
+        [2, grid, stride]: real-time counter, shader-clock counter) or off."""
+        g, st, pl = C.c_int32(0), C.c_int32(0), C.c_int32(0)
+        self._check(_lib.moe_fused_phase_stamps(self._h, None, 0, C.byref(g), C.byref(st), C.byref(pl)))
+        if not enable:
+            self._stamps = None
+            return None
+        buf = torch.zeros((2, g.value, st.value), dtype=torch.int64, device=torch.device("cuda", self.device))
+        self._check(_lib.moe_fused_phase_stamps(self._h, C.c_void_p(buf.data_ptr()), buf.numel(),
+                                                None, None, None))
+        self._stamps = buf            # keeps the buffer alive while the library uses it
+        self.stamp_layout = (g.value, st.value, pl.value)
+        return buf
+
     def inject_transfer_failure(self, layer, mode):
         self._check(_lib.moe_debug_inject_transfer_failure(self._h, layer, mode))
 

@@ -65,6 +65,7 @@ SIGNATURES = {
     "moe_debug_inject_transfer_failure": (_I, [_P, _I, _I]),
     "moe_timer_enable": (_I, [_P, _I]),
     "moe_timer_read": (_I, [_P, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
+    "moe_fused_phase_stamps": (_I, [_P, _P, C.c_int64, C.POINTER(_I), C.POINTER(_I), C.POINTER(_I)]),
     "moe_policy_new": (_P, [_I, _I, _I, _I]),
     "moe_policy_free": (None, [_P]),
     "moe_policy_access": (_I, [_P, _P, _I, _I, _P]),

@@ -76,6 +76,7 @@ struct moe_ctx {
   FusedLayer* dlayers = nullptr;
   uint32_t* flags = nullptr;
   int grid = 0;
+  uint64_t* stamps = nullptr;  // caller-owned phase-timestamp buffer or null
   // kernel timer
   int timer_kind = -1;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> timer_events;
@@ -166,8 +167,9 @@ bool fused_eligible(const moe_ctx* c, int T) {
   const moe_config& g = c->cfg;
   if (g.flags & MOE_FLAG_NO_FUSED) return false;
   if (T > kFMaxT || T * g.top_k > kFMaxP || T * g.n_experts > kFMaxTE) return false;
-  if (((g.n_experts + 63) / 64) * g.top_k > kFMaxCand) return false;
+  if (g.n_experts % 64 != 0 || (g.n_experts / 64) * g.top_k > kFMaxCand) return false;
   if (g.shared_inter != 0 && g.shared_inter != g.inter) return false;
+  if ((int64_t)(T * g.top_k + (g.shared_inter ? T : 0)) * g.inter > kFStageHalves) return false;
   return c->grid > 0 && fused_supported(g.hidden, g.inter);
 }
 
@@ -438,7 +440,8 @@ moe_status moe_register_layer(moe_ctx* c, int32_t layer, const uint16_t* router,
     repack_expert(shared_q, shared_s, scb, ssc, tmp.data());
     HIPCHK(c, hipMemcpy(L.shared, tmp.data(), tmp.size(), hipMemcpyHostToDevice));
   }
-  c->hlayers[layer] = FusedLayer{L.router, L.store, L.map, L.shared};
+  // full residency: slot = expert, the fused path skips the map lookup
+  c->hlayers[layer] = FusedLayer{L.router, L.store, pooled(c) ? L.map : nullptr, L.shared};
   HIPCHK(c, hipMemcpy(c->dlayers + layer, &c->hlayers[layer], sizeof(FusedLayer), hipMemcpyHostToDevice));
   L.registered = true;
   return MOE_OK;
@@ -507,6 +510,7 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t layer_begin, int32_t layer_end,
     fa.w_trace = w_trace;
     fa.flags = c->flags;
     fa.err = c->err;
+    fa.stamps = c->stamps;
     {
       ScopedTimer tm(c, kKindFused, s);
       launch_fused_decode(fa, c->grid, s);
@@ -683,6 +687,18 @@ moe_status moe_timer_read(moe_ctx* c, double* total_ms, int64_t* launches) {
   *total_ms = tot;
   *launches = (int64_t)c->timer_used;
   c->timer_used = 0;
+  return MOE_OK;
+}
+
+moe_status moe_fused_phase_stamps(moe_ctx* c, uint64_t* dev_buf, int64_t count, int32_t* grid,
+                                  int32_t* stride, int32_t* per_layer) {
+  if (!c) return MOE_E_ARG;
+  if (dev_buf && count < 2 * (int64_t)c->grid * kStampStride)
+    return fail(c, MOE_E_ARG, "stamp buffer smaller than 2 * grid * stride");
+  c->stamps = dev_buf;
+  if (grid) *grid = c->grid;
+  if (stride) *stride = kStampStride;
+  if (per_layer) *per_layer = kStampsPerLayer;
   return MOE_OK;
 }
 

@@ -72,6 +72,9 @@ constexpr int kFMaxT = 8;      // tokens per call
 constexpr int kFMaxP = 64;     // (token, rank) pairs per call
 constexpr int kFMaxTE = 4096;  // T * E
 constexpr int kFMaxCand = 128; // ceil(E/64) * k
+constexpr int kFStageHalves = 32768;  // (T*k + shared T) * I FP16 staged in LDS
+constexpr int kStampsPerLayer = 11;   // phase timestamps per layer (instrumentation)
+constexpr int kStampStride = 64 * kStampsPerLayer;  // per block, up to 64 layers
 struct FusedLayer {
   const uint16_t* router;
   const uint8_t* store;
@@ -92,6 +95,7 @@ struct FusedArgs {
   float* w_trace;
   uint32_t* flags;            // [grid] barrier flags
   uint32_t* err;
+  uint64_t* stamps;           // [grid][kStampStride] phase timestamps or null
 };
 bool fused_supported(int H, int I);
 void launch_fused_decode(const FusedArgs& a, int grid, hipStream_t stream);
