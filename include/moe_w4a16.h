@@ -225,7 +225,9 @@ moe_status moe_check_device_errors(moe_ctx* ctx, void* stream, uint32_t* bits);
  * Kernel timer: while enabled for a kernel kind, every launch of that kind is
  * bracketed by a HIP event pair recorded on the stream it is launched on.
  * Kinds: 0 router logits, 1 top-k, 2 grouping, 3 gate/up + SwiGLU,
- * 4 down projection, 5 combine, 6 RMSNorm, 7 fused decode (whole stack call).
+ * 4 down projection, 5 combine, 6 RMSNorm, 7 fused decode (whole stack call),
+ * 8 MFMA gate/up + SwiGLU, 9 MFMA down projection (the GEMV kernels are
+ * kinds 3 and 4).
  * kind = -1 disables.
  * moe_timer_read synchronises the recorded events, returns the summed
  * elapsed milliseconds and the number of launches, and resets both. */

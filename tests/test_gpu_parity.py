@@ -195,3 +195,19 @@ def test_expert_forward_bad_ids_are_contained(moe):
     bits = ctx.check_device_errors()
     assert bits & 1 and bits & 2
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("T", [1, 5, 64])
+@pytest.mark.parametrize("path", ["mfma", "gemv"])
+def test_layer_small_forced_expert_path(moe, T, path):
+    """Each expert path alone (MFMA grouped GEMM / INT4 GEMV) matches the oracle."""
+    say(f"test_layer_small_forced_expert_path T={T} path={path}")
+    flags = moe.MOE_FLAG_FORCE_MFMA if path == "mfma" else moe.MOE_FLAG_FORCE_GEMV
+    _layer_case(moe, SMALL, "gpu-layer-small", T, flags=flags)
+    _layer_case(moe, SMALL_SHARED, "gpu-layer-shared", T, flags=flags)
+
+
+@pytest.mark.parametrize("T", [64, 512])
+def test_layer_olmoe_forced_mfma(moe, olmoe_layer, T):
+    say(f"test_layer_olmoe_forced_mfma T={T}")
+    _layer_case(moe, fx.OLMOE, "olmoe-layer", T, flags=moe.MOE_FLAG_FORCE_MFMA, wts=olmoe_layer)

@@ -182,7 +182,7 @@ class MoEContext:
         return [buf[i].as_tuple() for i in range(n.value)]
 
     KERNEL_KINDS = {"logits": 0, "topk": 1, "group": 2, "gateup": 3, "down": 4, "combine": 5,
-                    "rmsnorm": 6, "fused": 7}
+                    "rmsnorm": 6, "fused": 7, "mfma_gateup": 8, "mfma_down": 9}
 
     def timer_enable(self, kind):
         self._check(_lib.moe_timer_enable(self._h, -1 if kind is None else self.KERNEL_KINDS[kind]))

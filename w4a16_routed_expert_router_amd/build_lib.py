@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_w4a16.so")
 
-SOURCES = ["api.hip", "router.hip", "group.hip", "expert_gemv.hip", "decode_fused.hip", "policy.cpp"]
+SOURCES = ["api.hip", "router.hip", "group.hip", "expert_gemv.hip", "expert_mfma.hip",
+           "decode_fused.hip", "policy.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",
@@ -35,7 +36,10 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    missing = [s for s in srcs if not os.path.exists(s)]
+    if missing:
+        raise RuntimeError(f"missing sources: {missing}")
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, "-shared", "-o", tmp,
            "-I", os.path.join(ROOT, "include"), *srcs, "-lpthread"]

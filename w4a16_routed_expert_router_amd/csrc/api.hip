@@ -62,6 +62,7 @@ struct moe_ctx {
   int32_t* n_active = nullptr;
   int32_t* perm_tok = nullptr;
   int32_t* pos_of = nullptr;
+  int32_t* mtile_off = nullptr;
   uint16_t* hbuf = nullptr;
   uint16_t* hshared = nullptr;
   float* ybuf = nullptr;
@@ -160,8 +161,11 @@ moe_status check_layer(moe_ctx* c, int layer) {
 bool pooled(const moe_ctx* c) { return c->cfg.policy != MOE_RESIDENT_ALL; }
 
 enum KernelKind {
-  kKindLogits = 0, kKindTopk, kKindGroup, kKindGateUp, kKindDown, kKindCombine, kKindNorm, kKindFused
+  kKindLogits = 0, kKindTopk, kKindGroup, kKindGateUp, kKindDown, kKindCombine, kKindNorm, kKindFused,
+  kKindMfmaGateUp, kKindMfmaDown
 };
+
+constexpr int kMfmaMinTokens = 8;  // per-expert token count from which MFMA is used
 
 bool fused_eligible(const moe_ctx* c, int T) {
   const moe_config& g = c->cfg;
@@ -213,13 +217,21 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
                        const float* w, uint16_t* out, float* resid, hipStream_t s) {
   LayerState& L = c->layers[layer];
   const moe_config& g = c->cfg;
+  // experts with at least mfma_min tokens run on the MFMA grouped GEMM; the
+  // choice depends only on the token counts
+  const int mfma_min = (g.flags & MOE_FLAG_FORCE_GEMV) ? INT32_MAX
+                       : (g.flags & MOE_FLAG_FORCE_MFMA) ? 1 : kMfmaMinTokens;
   GroupArgs ga{ids, T, g.top_k, g.n_experts, L.map, c->ids_s, c->active, c->n_active,
-               c->perm_tok, c->pos_of, c->err};
+               c->perm_tok, c->pos_of, c->err, mfma_min, c->mtile_off};
   {
     ScopedTimer tm(c, kKindGroup, s);
     launch_group(ga, s);
   }
+  const bool any_mfma = T >= mfma_min;
+  MfmaArgs ma{L.store, c->lay.total(), c->lay, c->active, c->n_active, c->mtile_off,
+              g.hidden, g.inter, x, c->perm_tok, c->hbuf, c->ybuf};
   ExpertArgs ea{};
+  ea.mfma_min = mfma_min;
   ea.blobs = L.store;
   ea.blob_stride = c->lay.total();
   ea.lay = c->lay;
@@ -236,9 +248,17 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
     ScopedTimer tm(c, kKindGateUp, s);
     launch_gateup_gemv(ea, s);
   }
+  if (any_mfma) {
+    ScopedTimer tm(c, kKindMfmaGateUp, s);
+    launch_mfma_gateup(ma, mfma_max_tiles(T, g.top_k, g.n_experts, g.inter, 0), s);
+  }
   {
     ScopedTimer tm(c, kKindDown, s);
     launch_down_gemv(ea, s);
+  }
+  if (any_mfma) {
+    ScopedTimer tm(c, kKindMfmaDown, s);
+    launch_mfma_down(ma, mfma_max_tiles(T, g.top_k, g.n_experts, g.hidden, 1), s);
   }
   if (g.shared_inter) {
     ExpertArgs sa = ea;
@@ -339,6 +359,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ok = ok && dalloc((void**)&c->n_active, 4);
   ok = ok && dalloc((void**)&c->perm_tok, (size_t)P * 4);
   ok = ok && dalloc((void**)&c->pos_of, (size_t)P * 4);
+  ok = ok && dalloc((void**)&c->mtile_off, (size_t)(g.n_experts + 1) * 4);
   // rows: routed (token, rank) pairs, then the shared expert's tokens
   ok = ok && dalloc((void**)&c->hbuf, (size_t)(P + g.max_tokens) * std::max(Imax, g.shared_inter) * 2);
   ok = ok && dalloc((void**)&c->dlayers, (size_t)g.n_layers * sizeof(FusedLayer));
@@ -389,7 +410,7 @@ void moe_destroy(moe_ctx* c) {
   }
   void* bufs[] = {c->logits, c->ids,  c->w,    c->ids_s,   c->active,  c->n_active, c->perm_tok,
                   c->pos_of, c->hbuf, c->ybuf, c->xbuf,    c->err,     c->hshared,  c->yshared,
-                  c->dlayers, c->flags};
+                  c->dlayers, c->flags, c->mtile_off};
   for (void* p : bufs) (void)hipFree(p);
   if (c->side) (void)hipStreamDestroy(c->side);
   for (auto& p : c->timer_events) {
@@ -669,7 +690,7 @@ moe_status moe_cache_event_log(const moe_ctx* c, int32_t layer, moe_cache_event*
 
 moe_status moe_timer_enable(moe_ctx* c, int32_t kind) {
   if (!c) return MOE_E_ARG;
-  if (kind < -1 || kind > kKindFused) return fail(c, MOE_E_ARG, "unknown kernel kind");
+  if (kind < -1 || kind > kKindMfmaDown) return fail(c, MOE_E_ARG, "unknown kernel kind");
   c->timer_kind = kind;
   return MOE_OK;
 }

@@ -57,6 +57,7 @@ __device__ __forceinline__ bool resolve(const ExpertArgs& a, int ai, const uint8
   }
   if (ai >= *a.n_active) return false;
   const ActiveExpert ae = a.active[ai];
+  if (ae.count >= a.mfma_min) return false;  // handled by the MFMA kernels
   blob = a.blobs + (int64_t)ae.slot * a.blob_stride;
   cnt = ae.count;
   off = ae.offset;

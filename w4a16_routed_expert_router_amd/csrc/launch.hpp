@@ -32,8 +32,28 @@ struct GroupArgs {
   int32_t* perm_tok;        // [T*k] token at sorted position
   int32_t* pos_of;          // [T*k] sorted position of pair t*k+j
   uint32_t* err;
+  int mfma_min;             // experts with at least this many tokens take the MFMA path
+  int32_t* mtile_off;       // [E+1] MFMA token-tile offsets over the active list
 };
 void launch_group(const GroupArgs& a, hipStream_t stream);
+
+// Grouped GEMM on MFMA (expert_mfma.hip)
+struct MfmaArgs {
+  const uint8_t* blobs;
+  int64_t blob_stride;
+  BlobLayout lay;
+  const ActiveExpert* active;
+  const int32_t* n_active;
+  const int32_t* mtile_off;   // [n_active+1]
+  int H, I;
+  const uint16_t* x;          // [T,H] (gate/up input)
+  const int32_t* perm_tok;    // token at each sorted position
+  uint16_t* hbuf;             // [positions, I] fp16
+  float* ybuf;                // [positions, H] fp32
+};
+int mfma_max_tiles(int T, int k, int E, int rows, int mode);
+void launch_mfma_gateup(const MfmaArgs& a, int max_tiles, hipStream_t stream);
+void launch_mfma_down(const MfmaArgs& a, int max_tiles, hipStream_t stream);
 
 struct ExpertArgs {
   const uint8_t* blobs;       // expert storage of the layer (slot-indexed)
@@ -50,6 +70,7 @@ struct ExpertArgs {
   const int32_t* perm_tok;    // token at each sorted position (routed mode)
   uint16_t* hbuf;             // [positions, I] fp16
   float* ybuf;                // [positions, H] fp32
+  int mfma_min;               // routed experts with count >= this are skipped (MFMA path)
 };
 void launch_gateup_gemv(const ExpertArgs& a, hipStream_t stream);
 void launch_down_gemv(const ExpertArgs& a, hipStream_t stream);
