@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
   // offsets and the active list (ascending expert id); E <= 1024 = one per thread
   const int c = (tid < E) ? cnt[tid] : 0;
   const int off = block_exclusive_scan(c, sh_warp, &sh_total);
-  const int mtiles = c >= a.mfma_min ? (c + 63) / 64 : 0;
+  const int mtiles = c >= a.mfma_min ? (c + kMfmaTileTokens - 1) / kMfmaTileTokens : 0;
   const int moff = block_exclusive_scan(mtiles, sh_warp, &sh_total);
   const int mtotal = sh_total;
   const int act = block_exclusive_scan(c > 0 ? 1 : 0, sh_warp, &sh_total);

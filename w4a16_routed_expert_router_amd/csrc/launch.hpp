@@ -38,6 +38,7 @@ struct GroupArgs {
 void launch_group(const GroupArgs& a, hipStream_t stream);
 
 // Grouped GEMM on MFMA (expert_mfma.hip)
+constexpr int kMfmaTileTokens = 128;  // tokens of one expert per MFMA tile
 struct MfmaArgs {
   const uint8_t* blobs;
   int64_t blob_stride;
