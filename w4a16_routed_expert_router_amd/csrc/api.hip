@@ -75,7 +75,11 @@ struct moe_ctx {
   // fused decode path
   std::vector<FusedLayer> hlayers;
   FusedLayer* dlayers = nullptr;
-  uint32_t* flags = nullptr;
+  uint64_t* xh = nullptr;      // tagged exchange buffers of the fused path
+  uint64_t* xlg = nullptr;
+  uint64_t* xhb = nullptr;
+  uint64_t* xgate = nullptr;
+  uint32_t* epoch = nullptr;   // per-block epoch counters
   int grid = 0;
   uint64_t* stamps = nullptr;  // caller-owned phase-timestamp buffer or null
   // kernel timer
@@ -174,7 +178,7 @@ bool fused_eligible(const moe_ctx* c, int T) {
   if (g.n_experts % 64 != 0 || (g.n_experts / 64) * g.top_k > kFMaxCand) return false;
   if (g.shared_inter != 0 && g.shared_inter != g.inter) return false;
   if ((int64_t)(T * g.top_k + (g.shared_inter ? T : 0)) * g.inter > kFStageHalves) return false;
-  return c->grid > 0 && fused_supported(g.hidden, g.inter);
+  return c->grid == kFGrid && fused_supported(g.hidden, g.inter);
 }
 
 // Brackets one launch with a recorded event pair when the timer is on for `kind`.
@@ -365,11 +369,21 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ok = ok && dalloc((void**)&c->dlayers, (size_t)g.n_layers * sizeof(FusedLayer));
   c->hlayers.assign(g.n_layers, FusedLayer{nullptr, nullptr, nullptr, nullptr});
   {
+    // the fused path runs one block per compute unit on exactly kFGrid of them
     int ncu = 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, g.device) != hipSuccess) ncu = 0;
-    c->grid = ncu;
-    ok = ok && dalloc((void**)&c->flags, (size_t)std::max(ncu, 1) * 4);
-    if (ok) ok = hipMemset(c->flags, 0, (size_t)std::max(ncu, 1) * 4) == hipSuccess;
+    c->grid = ncu >= kFGrid ? kFGrid : 0;
+    ok = ok && dalloc((void**)&c->xh, (size_t)kFXhWords * 8);
+    ok = ok && dalloc((void**)&c->xlg, (size_t)kFXlgWords * 8);
+    ok = ok && dalloc((void**)&c->xhb, (size_t)kFXhbWords * 8);
+    ok = ok && dalloc((void**)&c->xgate, (size_t)kFGrid * 8);
+    ok = ok && dalloc((void**)&c->epoch, (size_t)kFGrid * 4);
+    // tag 0 never names a layer: every later launch starts at epoch 1
+    if (ok) ok = hipMemset(c->xh, 0, (size_t)kFXhWords * 8) == hipSuccess;
+    if (ok) ok = hipMemset(c->xlg, 0, (size_t)kFXlgWords * 8) == hipSuccess;
+    if (ok) ok = hipMemset(c->xhb, 0, (size_t)kFXhbWords * 8) == hipSuccess;
+    if (ok) ok = hipMemset(c->xgate, 0, (size_t)kFGrid * 8) == hipSuccess;
+    if (ok) ok = hipMemset(c->epoch, 0, (size_t)kFGrid * 4) == hipSuccess;
   }
   ok = ok && dalloc((void**)&c->ybuf, (size_t)P * g.hidden * 4);
   ok = ok && dalloc((void**)&c->xbuf, (size_t)g.max_tokens * g.hidden * 2);
@@ -410,7 +424,7 @@ void moe_destroy(moe_ctx* c) {
   }
   void* bufs[] = {c->logits, c->ids,  c->w,    c->ids_s,   c->active,  c->n_active, c->perm_tok,
                   c->pos_of, c->hbuf, c->ybuf, c->xbuf,    c->err,     c->hshared,  c->yshared,
-                  c->dlayers, c->flags, c->mtile_off};
+                  c->dlayers, c->mtile_off, c->xh, c->xlg, c->xhb, c->xgate, c->epoch};
   for (void* p : bufs) (void)hipFree(p);
   if (c->side) (void)hipStreamDestroy(c->side);
   for (auto& p : c->timer_events) {
@@ -522,19 +536,22 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t layer_begin, int32_t layer_end,
     fa.exact_always = (int)(g.flags & MOE_FLAG_ROUTER_EXACT_ALWAYS);
     fa.lay = c->lay;
     fa.blob_stride = c->lay.total();
+    fa.lg_reps = T * g.n_experts <= 512 ? kFLogitReps : 1;
     fa.h = h;
-    fa.logits = c->logits;
-    fa.hbuf = c->hbuf;
+    fa.xh = c->xh;
+    fa.xlg = c->xlg;
+    fa.xhb = c->xhb;
+    fa.xgate = c->xgate;
+    fa.epoch = c->epoch;
     fa.forced = forced_ids;
     fa.x_trace = (uint16_t*)x_trace;
     fa.ids_trace = ids_trace;
     fa.w_trace = w_trace;
-    fa.flags = c->flags;
     fa.err = c->err;
     fa.stamps = c->stamps;
     {
       ScopedTimer tm(c, kKindFused, s);
-      launch_fused_decode(fa, c->grid, s);
+      launch_fused_decode(fa, s);
     }
     HIPCHK(c, hipGetLastError());
     if (pooled(c))
@@ -714,10 +731,10 @@ moe_status moe_timer_read(moe_ctx* c, double* total_ms, int64_t* launches) {
 moe_status moe_fused_phase_stamps(moe_ctx* c, uint64_t* dev_buf, int64_t count, int32_t* grid,
                                   int32_t* stride, int32_t* per_layer) {
   if (!c) return MOE_E_ARG;
-  if (dev_buf && count < 2 * (int64_t)c->grid * kStampStride)
+  if (dev_buf && count < 2 * (int64_t)kFGrid * kStampStride)
     return fail(c, MOE_E_ARG, "stamp buffer smaller than 2 * grid * stride");
   c->stamps = dev_buf;
-  if (grid) *grid = c->grid;
+  if (grid) *grid = kFGrid;
   if (stride) *stride = kStampStride;
   if (per_layer) *per_layer = kStampsPerLayer;
   return MOE_OK;

@@ -95,6 +95,9 @@ constexpr int kFMaxP = 64;     // (token, rank) pairs per call
 constexpr int kFMaxTE = 4096;  // T * E
 constexpr int kFMaxCand = 128; // ceil(E/64) * k
 constexpr int kFStageHalves = 32768;  // (T*k + shared T) * I FP16 staged in LDS
+constexpr int kFGrid = 256;    // blocks: one per compute unit
+constexpr int kFRows = 8;      // residual rows per block (H / kFGrid)
+constexpr int kFLogitReps = 8; // logit replicas (one per XCD) for small steps
 constexpr int kStampsPerLayer = 11;   // phase timestamps per layer (instrumentation)
 constexpr int kStampStride = 64 * kStampsPerLayer;  // per block, up to 64 layers
 struct FusedLayer {
@@ -106,21 +109,28 @@ struct FusedLayer {
 struct FusedArgs {
   const FusedLayer* layers;   // device array, indexed by absolute layer
   int l0, l1, T, E, I, k, renorm, has_shared, exact_always;
+  int lg_reps;                // logit replicas: kFLogitReps or 1
   BlobLayout lay;             // routed and shared blobs (shared inter == inter)
   int64_t blob_stride;
   float* h;                   // [T,H] residual, updated in place
-  float* logits;              // [T,E] scratch
-  uint16_t* hbuf;             // [(T*k + T), I] fp16 scratch
+  uint64_t* xh;               // [2][kFMaxT][H] tagged residual exchange
+  uint64_t* xlg;              // [kFLogitReps][kFMaxTE] tagged logits
+  uint64_t* xhb;              // [kFStageHalves/2] tagged FP16 pairs of intermediates
+  uint64_t* xgate;            // [kFGrid] tagged "residual read" marks
+  uint32_t* epoch;            // [kFGrid] per-block epoch counters
   const int32_t* forced;      // [L,T,k] or null
   uint16_t* x_trace;
   int32_t* ids_trace;
   float* w_trace;
-  uint32_t* flags;            // [grid] barrier flags
   uint32_t* err;
   uint64_t* stamps;           // [grid][kStampStride] phase timestamps or null
 };
 bool fused_supported(int H, int I);
-void launch_fused_decode(const FusedArgs& a, int grid, hipStream_t stream);
+void launch_fused_decode(const FusedArgs& a, hipStream_t stream);
+// words of each exchange buffer
+constexpr int64_t kFXhWords = 2ll * kFMaxT * 2048;
+constexpr int64_t kFXlgWords = (int64_t)kFLogitReps * kFMaxTE;
+constexpr int64_t kFXhbWords = kFStageHalves / 2;
 
 struct PublishUpdate {
   int32_t expert;
