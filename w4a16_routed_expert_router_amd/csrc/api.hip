@@ -537,6 +537,13 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t layer_begin, int32_t layer_end,
     fa.lay = c->lay;
     fa.blob_stride = c->lay.total();
     fa.lg_reps = T * g.n_experts <= 512 ? kFLogitReps : 1;
+    {
+      // split each logit over up to 4 waves while every wave of a replica
+      // still has at most one item
+      const int waves = (kFGrid / fa.lg_reps) * 8;
+      fa.lg_sub = 1;
+      while (fa.lg_sub < 4 && T * g.n_experts * fa.lg_sub * 2 <= waves) fa.lg_sub *= 2;
+    }
     fa.h = h;
     fa.xh = c->xh;
     fa.xlg = c->xlg;

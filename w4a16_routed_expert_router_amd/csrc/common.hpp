@@ -59,6 +59,20 @@ __device__ __forceinline__ void dequant8(uint32_t d, h2 out[4]) {
   out[3] = hi1 * k16th + km72;
 }
 
+// Load through a pointer that addresses global memory.  A pointer read from
+// memory (rather than passed as a kernel argument) is generic to the compiler,
+// which then emits flat loads; those also count against the LDS wait counter,
+// so every later LDS access would wait for them.  This keeps them global loads.
+template <class T>
+__device__ __forceinline__ T ldg(const void* p) {
+  return *(const __attribute__((address_space(1))) T*)(uintptr_t)p;
+}
+__device__ __forceinline__ uint4 ldg_u4(const void* p) {
+  typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+  const v4 v = ldg<v4>(p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ float dot2(h2 a, h2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }

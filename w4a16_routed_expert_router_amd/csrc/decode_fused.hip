@@ -60,6 +60,7 @@ constexpr int kFT = 512;
 constexpr int kFW = kFT / kWave;  // 8 waves
 constexpr uint32_t kSpinLimit = 1u << 18;  // polls of one word before giving up
 
+template <int I>
 struct FusedSmem {
   _Float16 x[kFMaxT * 2048];                 // normalised tokens (gate/up A operand)
   union {
@@ -75,11 +76,16 @@ struct FusedSmem {
   float ypart[2][kFMaxP + kFMaxT][kFRows];   // down K-part outputs per pair
   float hown[kFMaxT][kFRows];                // residual rows owned by the block
   float part[kFMaxT][kFW];
+  double lgacc[kFW], lgsum[kFW];             // logit partial sums of the waves
   int ids[kFMaxP];
   float w[kFMaxP];
   int unit_slot[kFMaxP + 1];                 // blob slot of each routed expert
   int pair_of[(kFMaxP + 1) * kFMaxT];        // [unit][token] -> pair, -1
   int nunits;
+  // down-projection weights of each wave's current task, written by direct
+  // global->LDS loads: codes [group][lane] 16 B, scales [lane] 2 groups
+  uint4 dpre[kFW][I / 128][kWave];
+  uint32_t dsc[kFW][kWave];
 };
 
 __device__ __forceinline__ void stamp(const FusedArgs& a, int l, int ev) {
@@ -112,8 +118,9 @@ __device__ __forceinline__ uint32_t wait_word(const uint64_t* p, uint64_t w, uin
   return (uint32_t)w;
 }
 
-// Block-cooperative read of n tagged words: sink(i, payload) for each.  Eight
-// loads per thread are in flight before the first wait.
+// Block-cooperative read of n tagged words: sink(i, payload) for each.  A
+// thread holds up to eight words in flight; every poll round re-issues all of
+// its words that are not current yet, so one round trip refreshes them all.
 template <class F>
 __device__ __forceinline__ void read_tagged(const uint64_t* src, int n, uint32_t tag, bool& bail, F&& sink) {
   constexpr int NF = 8;
@@ -122,14 +129,45 @@ __device__ __forceinline__ void read_tagged(const uint64_t* src, int n, uint32_t
 #pragma unroll
     for (int u = 0; u < NF; ++u) {
       const int i = i0 + u * kFT;
-      w[u] = i < n ? ld_tag(src + i) : 0;
+      w[u] = i < n ? ld_tag(src + i) : ((uint64_t)tag << 32);
+    }
+    uint32_t spins = 0;
+    while (!bail) {
+      bool all = true;
+#pragma unroll
+      for (int u = 0; u < NF; ++u) all &= tag_is(w[u], tag);
+      if (all) break;
+      if (++spins > kSpinLimit) {
+        bail = true;
+        break;
+      }
+#pragma unroll
+      for (int u = 0; u < NF; ++u)
+        if (!tag_is(w[u], tag)) w[u] = ld_tag(src + i0 + u * kFT);
     }
 #pragma unroll
     for (int u = 0; u < NF; ++u) {
       const int i = i0 + u * kFT;
-      if (i < n) sink(i, wait_word(src + i, w[u], tag, bail));
+      if (i < n) sink(i, (uint32_t)w[u]);
     }
   }
+}
+
+// Direct global -> LDS loads (gfx950 LDS DMA): lane l's `bytes` land at the
+// wave-uniform LDS address `lds` + l * bytes.  Written as inline assembly so
+// that the compiler neither stalls on them when it reuses their address
+// registers nor waits for them before unrelated loads; they still count in
+// vmcnt, and the LDS data is read only after an explicit vmcnt(0).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma_lds16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_lds4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 
 // INT4 dword of 8 K values -> the 8 FP16 operands of one MFMA step.
@@ -146,23 +184,26 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& q, int i) {
   return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
 }
 
-// Router row of one logit item, 8 FP16 per lane per 512-wide chunk.
+// One wave's part of a router row: chunks c < nc of 512 FP16, 8 per lane.
 template <int H>
-__device__ __forceinline__ void load_router_row(const uint16_t* row, int lane, uint4 (&q)[H / 512]) {
+__device__ __forceinline__ void load_router_part(const uint16_t* part_row, int nc, int lane,
+                                                 uint4 (&q)[H / 512]) {
 #pragma unroll
-  for (int c = 0; c < H / 512; ++c) q[c] = *reinterpret_cast<const uint4*>(row + c * 512 + lane * 8);
+  for (int c = 0; c < H / 512; ++c)
+    if (c < nc) q[c] = ldg_u4(part_row + c * 512 + lane * 8);
 }
 
-// Certified FP64 dot of LDS x with a router row already in registers: returns
-// the FP32 rounding of the exact sum when the FP64 error bound proves it,
-// otherwise the exact 128-bit fixed-point result (reads the row again).
+// FP64 partial dot of LDS x with a router part already in registers; every
+// lane ends with the wave's sums (xor butterfly: bit-identical in all lanes).
+// Products of FP16 values are exact in FP32; |p| is summed alongside.
 template <int H>
-__device__ float certified_dot_regs(const _Float16* x, const uint4 (&q)[H / 512], const uint16_t* row,
-                                    int lane, int exact_always) {
-  if (!exact_always) {
-    double acc = 0.0, asum = 0.0;
+__device__ __forceinline__ void partial_dot(const _Float16* x, const uint4 (&q)[H / 512], int nc, int lane,
+                                            double& acc, double& asum) {
+  acc = 0.0;
+  asum = 0.0;
 #pragma unroll
-    for (int c = 0; c < H / 512; ++c) {
+  for (int c = 0; c < H / 512; ++c) {
+    if (c < nc) {
       const uint4 av = *reinterpret_cast<const uint4*>(x + c * 512 + lane * 8);
       const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
       const uint32_t bw[4] = {q[c].x, q[c].y, q[c].z, q[c].w};
@@ -175,21 +216,30 @@ __device__ float certified_dot_regs(const _Float16* x, const uint4 (&q)[H / 512]
         asum += fabs(p);
       }
     }
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-      acc += __shfl_xor(acc, o, kWave);
-      asum += __shfl_xor(asum, o, kWave);
-    }
-    const int depth = 8 * (H / 512) + 6;
-    const double eps = (double)(depth + 2) * 0x1p-52 * asum;
-    const float r = (float)acc;
-    if (r != 0.0f && isfinite(r) && isfinite(acc)) {
-      const double rd = (double)r;
-      const double m_lo = 0.5 * (rd + (double)nextafterf(r, -INFINITY));
-      const double m_hi = 0.5 * (rd + (double)nextafterf(r, INFINITY));
-      if (acc - eps > m_lo && acc + eps < m_hi) return r;
+  }
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    acc += __shfl_xor(acc, o, kWave);
+    asum += __shfl_xor(asum, o, kWave);
+  }
+}
+
+// Certified rounding: the FP32 rounding of an FP64 sum whose error is at most
+// (depth + 2) * 2^-52 * asum equals the rounding of the exact sum when the
+// whole error interval lies strictly between the two rounding midpoints of
+// that value.  Returns false when that is not proven.
+__device__ __forceinline__ bool certify(double acc, double asum, int depth, float& out) {
+  const double eps = (double)(depth + 2) * 0x1p-52 * asum;
+  const float r = (float)acc;
+  if (r != 0.0f && isfinite(r) && isfinite(acc)) {
+    const double rd = (double)r;
+    const double m_lo = 0.5 * (rd + (double)nextafterf(r, -INFINITY));
+    const double m_hi = 0.5 * (rd + (double)nextafterf(r, INFINITY));
+    if (acc - eps > m_lo && acc + eps < m_hi) {
+      out = r;
+      return true;
     }
   }
-  return exact_dot_wave(reinterpret_cast<const uint16_t*>(x), row, H, lane);
+  return false;
 }
 
 // OR of a per-thread flag over the block (all threads call it).
@@ -197,7 +247,7 @@ __device__ __forceinline__ bool block_any(bool v) { return __syncthreads_or(v ? 
 
 template <int H, int I>
 __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
-  __shared__ FusedSmem s;
+  __shared__ FusedSmem<I> s;
   static_assert(H / kFRows == kFGrid, "one block per 8 residual rows");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int b = blockIdx.x;
@@ -208,7 +258,13 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
   const int R = a.lg_reps;                 // logit replicas: 8 (one per XCD) or 1
   const int rep = b % R, rb = b / R, nrb = kFGrid / R;
   const int r0 = b * kFRows;               // residual rows owned by this block
-  const int item0 = rb + nrb * wv;         // first logit item of this wave
+  // logit items: `sub` waves of one block share an item, each over H / sub of
+  // it; item of round r for this wave = (r * nrb + rb) * ipb + islot
+  const int sub = a.lg_sub;
+  const int ipb = kFW / sub, islot = wv / sub, lpart = wv - islot * sub;
+  const int nchunk = (H / 512) / sub;
+  const int item0 = rb * ipb + islot;
+  const int lpoff = lpart * (H / sub);     // first K of the wave's part
   constexpr int GPU = I / 8;               // gate/up row groups per expert
   constexpr int GH = H / 256;              // scale groups per K half of gate/up
   constexpr int GDM = I / 128;             // scale groups of a whole down row
@@ -216,8 +272,8 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
   bool bail = false;
   uint32_t errs = 0;
 
-  uint4 rq[H / 512];  // router row of the wave's first logit item
-  if (item0 < TE) load_router_row<H>(a.layers[a.l0].router + (int64_t)(item0 % E) * H, lane, rq);
+  uint4 rq[H / 512];  // router part of the wave's first logit item
+  if (item0 < TE) load_router_part<H>(a.layers[a.l0].router + (int64_t)(item0 % E) * H + lpoff, nchunk, lane, rq);
 
   for (int l = a.l0; l < a.l1; ++l) {
     const FusedLayer L = a.layers[l];
@@ -265,16 +321,42 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
     stamp(a, l, 1);
 
     // ---------------- router logits of this replica ----------------
-    for (int item = item0, r = 0; item < TE; item += nrb * kFW, ++r) {
-      const int t = item / E, e = item - t * E;
-      const uint16_t* row = L.router + (int64_t)e * H;
-      if (r > 0) load_router_row<H>(row, lane, rq);
-      const float v = certified_dot_regs<H>(s.x + t * H, rq, row, lane, a.exact_always);
-      if (lane == 0) st_tag(a.xlg + (int64_t)rep * kFMaxTE + item, tag, __builtin_bit_cast(uint32_t, v));
+    {
+      const int nlr = (TE + nrb * ipb - 1) / (nrb * ipb);
+      for (int r = 0; r < nlr; ++r) {
+        const int item = (r * nrb + rb) * ipb + islot;
+        const bool on = item < TE;
+        const int t = on ? item / E : 0, e = on ? item - t * E : 0;
+        const uint16_t* row = L.router + (int64_t)e * H;
+        double acc = 0.0, asum = 0.0;
+        if (on) {
+          if (r > 0) load_router_part<H>(row + lpoff, nchunk, lane, rq);
+          partial_dot<H>(s.x + t * H + lpoff, rq, nchunk, lane, acc, asum);
+        }
+        if (sub > 1) {
+          if (lane == 0) {
+            s.lgacc[wv] = acc;
+            s.lgsum[wv] = asum;
+          }
+          __syncthreads();
+          if (lpart == 0) {
+            acc = s.lgacc[wv];
+            asum = s.lgsum[wv];
+            for (int j = 1; j < sub; ++j) {
+              acc += s.lgacc[wv + j];
+              asum += s.lgsum[wv + j];
+            }
+          }
+          __syncthreads();
+        }
+        if (on && lpart == 0) {
+          float v;
+          if (a.exact_always || !certify(acc, asum, 8 * (H / 512) + 9, v))
+            v = exact_dot_wave(reinterpret_cast<const uint16_t*>(s.x + t * H), row, H, lane);
+          if (lane == 0) st_tag(a.xlg + (int64_t)rep * kFMaxTE + item, tag, __builtin_bit_cast(uint32_t, v));
+        }
+      }
     }
-    // the next layer's router row of this wave's first item streams in meanwhile
-    if (l + 1 < a.l1 && item0 < TE)
-      load_router_row<H>(a.layers[l + 1].router + (int64_t)(item0 % E) * H, lane, rq);
     stamp(a, l, 2);
 
     // ---------------- E2: logits -> LDS ----------------
@@ -313,12 +395,12 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         const int task = t0 + wv;
         if (task < ntask) {
           const int t = task / nch, c = task - t * nch;
-          const float* row = s.u.sel.logit + t * E + c * kWave;
-          const float v = row[lane];
+          const float v = s.u.sel.logit[t * E + c * kWave + lane];
+          // every lane compares its value with all 64, broadcast by v_readlane
           int rank = 0;
-#pragma unroll 16
+#pragma unroll
           for (int j = 0; j < kWave; ++j) {
-            const float vj = row[j];
+            const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
             rank += (int)(vj > v) | ((int)(vj == v) & (int)(j < lane));
           }
           if (rank < k) {
@@ -341,12 +423,26 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
           const float vb = hb ? s.u.sel.cval[t][lane + kWave] : 0.0f;
           const int ea = ha ? s.u.sel.cid[t][lane] : 0;
           const int eb = hb ? s.u.sel.cid[t][lane + kWave] : 0;
+          // candidates broadcast from registers: a lane without one holds
+          // (-inf, INT_MAX), which ranks after every real candidate
+          const float pa_v = ha ? va : -INFINITY, pb_v = hb ? vb : -INFINITY;
+          const int pa_e = ha ? ea : 0x7fffffff, pb_e = hb ? eb : 0x7fffffff;
           int ra = 0, rbk = 0;
-          for (int j = 0; j < n; ++j) {
-            const float vj = s.u.sel.cval[t][j];
-            const int ej = s.u.sel.cid[t][j];
+#pragma unroll
+          for (int j = 0; j < kWave; ++j) {
+            const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pa_v), j));
+            const int ej = __builtin_amdgcn_readlane(pa_e, j);
             ra += (int)(vj > va) | ((int)(vj == va) & (int)(ej < ea));
             rbk += (int)(vj > vb) | ((int)(vj == vb) & (int)(ej < eb));
+          }
+          if (n > kWave) {
+#pragma unroll
+            for (int j = 0; j < kWave; ++j) {
+              const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pb_v), j));
+              const int ej = __builtin_amdgcn_readlane(pb_e, j);
+              ra += (int)(vj > va) | ((int)(vj == va) & (int)(ej < ea));
+              rbk += (int)(vj > vb) | ((int)(vj == vb) & (int)(ej < eb));
+            }
           }
           if (ha && ra < k) s.ids[t * k + ra] = ea;
           if (hb && rbk < k) s.ids[t * k + rbk] = eb;
@@ -399,7 +495,7 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
       const uint64_t fm = __ballot(first);
       const int ap = __popcll(fm & ((1ull << q0) - 1ull));
       if (first) {
-        int slot = L.map ? L.map[e] : e;
+        int slot = L.map ? ldg<int32_t>(L.map + e) : e;
         if (slot < 0) {
           errs |= kErrNotResident;
           slot = 0;
@@ -440,37 +536,45 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
       const uint16_t* sp = reinterpret_cast<const uint16_t*>(blob + a.lay.scales(mat)) + (int64_t)row * (H / 128) + half * GH;
 #pragma unroll
       for (int g2 = 0; g2 < GH; ++g2) {
-        gq[g2] = *reinterpret_cast<const uint4*>(cp + g2 * 64);
-        gs[g2] = sp[g2];
+        gq[g2] = ldg_u4(cp + g2 * 64);
+        gs[g2] = ldg<uint16_t>(sp + g2);
       }
     };
-    uint4 dq[GDM];
-    uint16_t ds[GDM];
-    auto load_d = [&](int task) {
+    // down weights go straight to LDS: no registers are held for them while
+    // gate/up runs and E3 completes.  Addresses are formed before any load of
+    // the burst is issued, so forming them waits on nothing.
+    struct DPtr {
+      const uint8_t* cp;
+      const uint16_t* sp;
+    };
+    auto d_ptrs = [&](int task) -> DPtr {
       const int cg = task / ks, kp = task - cg * ks;
       const int u = min(cg * 2 + (n16 >> 3), UU - 1);  // a dead column re-reads a live row
       const uint8_t* blob = unit_blob(u);
       const int row = r0 + (n16 & 7);
-      const uint8_t* cp = blob + a.lay.codes(2) + (int64_t)row * (I / 2) + kp * (I / 2 / ks) + q * 16;
-      const uint16_t* sp = reinterpret_cast<const uint16_t*>(blob + a.lay.scales(2)) + (int64_t)row * GDM + kp * ngd;
+      return DPtr{blob + a.lay.codes(2) + (int64_t)row * (I / 2) + kp * (I / 2 / ks) + q * 16,
+                  reinterpret_cast<const uint16_t*>(blob + a.lay.scales(2)) + (int64_t)row * GDM + kp * ngd + 2 * q};
+    };
+    auto load_d = [&](const DPtr& d) {
 #pragma unroll
-      for (int g2 = 0; g2 < GDM; ++g2) {
-        if (g2 < ngd) {
-          dq[g2] = *reinterpret_cast<const uint4*>(cp + g2 * 64);
-          ds[g2] = sp[g2];
-        }
-      }
+      for (int g2 = 0; g2 < GDM; ++g2)
+        if (g2 < ngd) dma_lds16(d.cp + g2 * 64, lds_addr(&s.dpre[wv][g2][0]));
+      // lane (n, q) fetches the scales of groups 2q, 2q+1 of column n
+      if (2 * q < ngd) dma_lds4(d.sp, lds_addr(&s.dsc[wv][0]));
     };
     const int gu_task0 = b * kFW + wv;
+    const DPtr d0 = d_ptrs(wv < ntask_d ? wv : 0);
+    // gate/up loads first (consumed first), then the down weights' direct loads
     if (gu_task0 < ntask_gu) load_gu(gu_task0);
-    if (wv < ntask_d) load_d(wv);
+    if (wv < ntask_d) load_d(d0);
     stamp(a, l, 5);
 
     // ---------------- gate/up + SwiGLU -> E3 publication ----------------
-    for (int r = 0; r < nround_gu; ++r) {
-      const int task = gu_task0 + r * kFGrid * kFW;
+    // one round: MFMA over the wave's K half, LDS sum of the halves, SwiGLU,
+    // publication.  Round 0 runs outside the loop so that its loads are
+    // waited for one group at a time.
+    auto gu_round = [&](int task) __attribute__((always_inline)) {
       const bool on = task < ntask_gu;
-      if (r > 0 && on) load_gu(task);
       if (on) {
         const int half = task & 1;
         f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -485,6 +589,9 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
             ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, decode_h8(dword_of(gq[g2], st)), ag, 0, 0, 0);
           }
           acc += ag * half_bits_to_float(gs[g2]);
+          // decode one group at a time: keeps the decoded operands of later
+          // groups from being hoisted (and held in registers) early
+          __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
@@ -510,7 +617,13 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
           }
         }
       }
-      if (r + 1 < nround_gu) __syncthreads();
+    };
+    gu_round(gu_task0);
+    for (int r = 1; r < nround_gu; ++r) {
+      const int task = gu_task0 + r * kFGrid * kFW;
+      __syncthreads();  // red is reused
+      if (task < ntask_gu) load_gu(task);
+      gu_round(task);
     }
     stamp(a, l, 6);
 
@@ -525,7 +638,9 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
     for (int r = 0; r < nround_d; ++r) {
       const int task = wv + r * kFW;
       const bool on = task < ntask_d;
-      if (r > 0 && on) load_d(task);
+      if (r > 0 && on) load_d(d_ptrs(task));
+      // this wave's direct loads into its LDS region have landed
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (on) {
         const int cg = task / ks, kp = task - cg * ks;
         // A row m: unit cg*2 + m/T, token m%T
@@ -539,13 +654,15 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
           if (g2 < ngd) {
             f4 ag = {0.f, 0.f, 0.f, 0.f};
             const int kb = kp * (I / ks) + g2 * 128 + 32 * q;
+            const uint4 dq = s.dpre[wv][g2][lane];
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
               h8 av = {};
               if (pa >= 0) av = *reinterpret_cast<const h8*>(hrow + kb + 8 * st);
-              ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, decode_h8(dword_of(dq[g2], st)), ag, 0, 0, 0);
+              ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, decode_h8(dword_of(dq, st)), ag, 0, 0, 0);
             }
-            acc += ag * half_bits_to_float(ds[g2]);
+            const uint32_t sw = s.dsc[wv][n16 + 16 * (g2 >> 1)];
+            acc += ag * half_bits_to_float((uint16_t)(sw >> (16 * (g2 & 1))));
           }
         }
         // D[m][n]: row m = (unit m/T, token m%T), column n = (unit n/8, row n%8)
@@ -563,6 +680,10 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         }
       }
     }
+    // the next layer's router part of this wave's first item streams in
+    // during the combine and the residual exchange
+    if (l + 1 < a.l1 && item0 < TE)
+      load_router_part<H>(a.layers[l + 1].router + (int64_t)(item0 % E) * H + lpoff, nchunk, lane, rq);
     __syncthreads();
     stamp(a, l, 8);
 

@@ -48,12 +48,12 @@ __device__ inline float round_i128_to_f32(__int128 S, int exp2) {
 }
 
 // Exact dot product of FP16 rows a, b of length H, over the whole wave.
-// Every lane returns the correctly rounded FP32 result.
+// Every lane returns the correctly rounded FP32 result.  b is in global memory.
 __device__ inline float exact_dot_wave(const uint16_t* a, const uint16_t* b, int H, int lane) {
   __int128 acc = 0;
   for (int k = lane * 8; k < H; k += kWave * 8) {
     const uint4 av = *reinterpret_cast<const uint4*>(a + k);
-    const uint4 bv = *reinterpret_cast<const uint4*>(b + k);
+    const uint4 bv = ldg_u4(b + k);
     const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
     const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll

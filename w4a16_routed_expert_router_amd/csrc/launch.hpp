@@ -90,7 +90,7 @@ void launch_combine(const CombineArgs& a, hipStream_t stream);
 void launch_rmsnorm(const float* h, int T, int H, float eps, uint16_t* x, hipStream_t stream);
 
 // Fused persistent decode path (decode_fused.hip)
-constexpr int kFMaxT = 8;      // tokens per call
+constexpr int kFMaxT = 4;      // tokens per call
 constexpr int kFMaxP = 64;     // (token, rank) pairs per call
 constexpr int kFMaxTE = 4096;  // T * E
 constexpr int kFMaxCand = 128; // ceil(E/64) * k
@@ -110,6 +110,7 @@ struct FusedArgs {
   const FusedLayer* layers;   // device array, indexed by absolute layer
   int l0, l1, T, E, I, k, renorm, has_shared, exact_always;
   int lg_reps;                // logit replicas: kFLogitReps or 1
+  int lg_sub;                 // waves sharing one logit item: 1, 2 or 4
   BlobLayout lay;             // routed and shared blobs (shared inter == inter)
   int64_t blob_stride;
   float* h;                   // [T,H] residual, updated in place
