@@ -89,6 +89,59 @@ __device__ __forceinline__ float wave_sum_xor(float v, int width) {
   return v;
 }
 
+// Wave reductions on the DPP network (no LDS round trips): inclusive sums
+// within each row of 16 lanes, then row broadcasts, leave the total in lane 63,
+// which is broadcast to every lane.  The order of the additions is fixed, so
+// every lane -- and every wave given the same inputs -- gets the same bits.
+template <int CTRL, int RM>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v, uint32_t ident) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, CTRL, RM, 0xf, false);
+}
+template <int CTRL, int RM>
+__device__ __forceinline__ float dppf(float v, float ident) {
+  return __builtin_bit_cast(float, dpp32<CTRL, RM>(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, ident)));
+}
+template <int CTRL, int RM>
+__device__ __forceinline__ double dppd(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = dpp32<CTRL, RM>((uint32_t)u, 0u);
+  const uint32_t hi = dpp32<CTRL, RM>((uint32_t)(u >> 32), 0u);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float bcast63(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dppf<0x111, 0xf>(x, 0.0f);  // row_shr:1
+  x += dppf<0x112, 0xf>(x, 0.0f);  // row_shr:2
+  x += dppf<0x114, 0xf>(x, 0.0f);  // row_shr:4
+  x += dppf<0x118, 0xf>(x, 0.0f);  // row_shr:8
+  x += dppf<0x142, 0xa>(x, 0.0f);  // row_bcast:15
+  x += dppf<0x143, 0xc>(x, 0.0f);  // row_bcast:31
+  return bcast63(x);
+}
+__device__ __forceinline__ double wave_sum(double x) {
+  x += dppd<0x111, 0xf>(x);
+  x += dppd<0x112, 0xf>(x);
+  x += dppd<0x114, 0xf>(x);
+  x += dppd<0x118, 0xf>(x);
+  x += dppd<0x142, 0xa>(x);
+  x += dppd<0x143, 0xc>(x);
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dppf<0x111, 0xf>(x, -INFINITY));
+  x = fmaxf(x, dppf<0x112, 0xf>(x, -INFINITY));
+  x = fmaxf(x, dppf<0x114, 0xf>(x, -INFINITY));
+  x = fmaxf(x, dppf<0x118, 0xf>(x, -INFINITY));
+  x = fmaxf(x, dppf<0x142, 0xa>(x, -INFINITY));
+  x = fmaxf(x, dppf<0x143, 0xc>(x, -INFINITY));
+  return bcast63(x);
+}
+
 __device__ __forceinline__ void atomic_or_err(uint32_t* err, uint32_t bits) {
   if (err) atomicOr(err, bits);
 }

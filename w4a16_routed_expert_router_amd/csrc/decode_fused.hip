@@ -68,6 +68,8 @@ struct FusedSmem {
       float logit[kFMaxTE];                  // logits of the step
       float cval[kFMaxT][kFMaxCand];         // per-chunk candidates (E > 64)
       int cid[kFMaxT][kFMaxCand];
+      int prank[kFW][kWave];                 // partial ranks of the waves
+      int prank2[kFW][kWave];
     } sel;
     _Float16 hst[kFStageHalves];             // intermediates of every pair (down A operand)
     float hfull[kFStageHalves / 2];          // residual of every token (E1 staging)
@@ -194,7 +196,7 @@ __device__ __forceinline__ void load_router_part(const uint16_t* part_row, int n
 }
 
 // FP64 partial dot of LDS x with a router part already in registers; every
-// lane ends with the wave's sums (xor butterfly: bit-identical in all lanes).
+// lane ends with the wave's sums (bit-identical in all lanes).
 // Products of FP16 values are exact in FP32; |p| is summed alongside.
 template <int H>
 __device__ __forceinline__ void partial_dot(const _Float16* x, const uint4 (&q)[H / 512], int nc, int lane,
@@ -217,10 +219,8 @@ __device__ __forceinline__ void partial_dot(const _Float16* x, const uint4 (&q)[
       }
     }
   }
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    acc += __shfl_xor(acc, o, kWave);
-    asum += __shfl_xor(asum, o, kWave);
-  }
+  acc = wave_sum(acc);
+  asum = wave_sum(asum);
 }
 
 // Certified rounding: the FP32 rounding of an FP64 sum whose error is at most
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         const float v = s.u.hfull[t * H + tid + j * kFT];
         ss += v * v;
       }
-      ss = wave_sum_xor(ss, kWave);
+      ss = wave_sum(ss);
       if (lane == 0) s.part[t][wv] = ss;
     }
     __syncthreads();
@@ -389,20 +389,34 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         if (valid) s.ids[p] = tok_bad ? (p - t * k) : e;
       }
     } else {
-      // rank of every expert within its chunk of 64: one wave per (token, chunk)
+      // rank of every expert within its chunk of 64: `wpt` waves share one
+      // (token, chunk) task, each comparing all 64 lanes against a slice of
+      // the chunk read with batched LDS broadcasts; partial ranks are summed
       const int ntask = T * nch;
-      for (int t0 = 0; t0 < ntask; t0 += kFW) {
-        const int task = t0 + wv;
-        if (task < ntask) {
-          const int t = task / nch, c = task - t * nch;
-          const float v = s.u.sel.logit[t * E + c * kWave + lane];
-          // every lane compares its value with all 64, broadcast by v_readlane
-          int rank = 0;
+      int wpt = 1;
+      while (wpt * 2 * ntask <= kFW) wpt *= 2;
+      const int span = kWave / wpt, sl = wv % wpt;
+      for (int t0 = 0; t0 < ntask; t0 += kFW / wpt) {
+        const int task = t0 + wv / wpt;
+        const bool on = task < ntask;
+        const int t = on ? task / nch : 0, c = on ? task - t * nch : 0;
+        const float* row = s.u.sel.logit + t * E + c * kWave;
+        const float v = row[lane];
+        int pr = 0;
+        if (on) {
+          for (int j0 = sl * span; j0 < (sl + 1) * span; j0 += 8) {
+            float vj[8];
 #pragma unroll
-          for (int j = 0; j < kWave; ++j) {
-            const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
-            rank += (int)(vj > v) | ((int)(vj == v) & (int)(j < lane));
+            for (int u = 0; u < 8; ++u) vj[u] = row[j0 + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) pr += (int)(vj[u] > v) | ((int)(vj[u] == v) & (int)(j0 + u < lane));
           }
+        }
+        s.u.sel.prank[wv][lane] = pr;
+        __syncthreads();
+        if (on && sl == 0) {
+          int rank = 0;
+          for (int qq = 0; qq < wpt; ++qq) rank += s.u.sel.prank[wv + qq][lane];
           if (rank < k) {
             if (nch == 1) {
               s.ids[t * k + rank] = lane;
@@ -412,44 +426,62 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
             }
           }
         }
+        __syncthreads();
       }
       if (nch > 1) {
-        __syncthreads();
-        // rank among the chunks' candidates (<= 128): lanes hold lane, lane + 64
-        if (wv < T) {
-          const int t = wv, n = nch * k;
-          const bool ha = lane < n, hb = lane + kWave < n;
-          const float va = ha ? s.u.sel.cval[t][lane] : 0.0f;
-          const float vb = hb ? s.u.sel.cval[t][lane + kWave] : 0.0f;
-          const int ea = ha ? s.u.sel.cid[t][lane] : 0;
-          const int eb = hb ? s.u.sel.cid[t][lane + kWave] : 0;
-          // candidates broadcast from registers: a lane without one holds
-          // (-inf, INT_MAX), which ranks after every real candidate
-          const float pa_v = ha ? va : -INFINITY, pb_v = hb ? vb : -INFINITY;
-          const int pa_e = ha ? ea : 0x7fffffff, pb_e = hb ? eb : 0x7fffffff;
+        // rank among the chunks' candidates (<= 128 per token): lanes hold
+        // candidates lane and lane + 64; `wpt2` waves share a token, each
+        // comparing against a slice of the candidates
+        const int n = nch * k;
+        int wpt2 = 1;
+        while (wpt2 * 2 * T <= kFW) wpt2 *= 2;
+        const int span2 = (n + wpt2 - 1) / wpt2, sl2 = wv % wpt2;
+        for (int t0 = 0; t0 < T; t0 += kFW / wpt2) {
+          const int t = t0 + wv / wpt2;
+          const bool on = t < T;
+          const int tt = on ? t : 0;
+          const bool ha = on && lane < n, hb = on && lane + kWave < n;
+          const float va = ha ? s.u.sel.cval[tt][lane] : 0.0f;
+          const float vb = hb ? s.u.sel.cval[tt][lane + kWave] : 0.0f;
+          const int ea = ha ? s.u.sel.cid[tt][lane] : 0;
+          const int eb = hb ? s.u.sel.cid[tt][lane + kWave] : 0;
           int ra = 0, rbk = 0;
+          if (on) {
+            const int j1 = min(n, (sl2 + 1) * span2);
+            for (int j0 = sl2 * span2; j0 < j1; j0 += 8) {
+              float vj[8];
+              int ej[8];
 #pragma unroll
-          for (int j = 0; j < kWave; ++j) {
-            const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pa_v), j));
-            const int ej = __builtin_amdgcn_readlane(pa_e, j);
-            ra += (int)(vj > va) | ((int)(vj == va) & (int)(ej < ea));
-            rbk += (int)(vj > vb) | ((int)(vj == vb) & (int)(ej < eb));
-          }
-          if (n > kWave) {
+              for (int u = 0; u < 8; ++u) {
+                const bool in = j0 + u < j1;
+                vj[u] = in ? s.u.sel.cval[tt][j0 + u] : -INFINITY;
+                ej[u] = in ? s.u.sel.cid[tt][j0 + u] : 0x7fffffff;
+              }
 #pragma unroll
-            for (int j = 0; j < kWave; ++j) {
-              const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pb_v), j));
-              const int ej = __builtin_amdgcn_readlane(pb_e, j);
-              ra += (int)(vj > va) | ((int)(vj == va) & (int)(ej < ea));
-              rbk += (int)(vj > vb) | ((int)(vj == vb) & (int)(ej < eb));
+              for (int u = 0; u < 8; ++u) {
+                ra += (int)(vj[u] > va) | ((int)(vj[u] == va) & (int)(ej[u] < ea));
+                rbk += (int)(vj[u] > vb) | ((int)(vj[u] == vb) & (int)(ej[u] < eb));
+              }
             }
           }
-          if (ha && ra < k) s.ids[t * k + ra] = ea;
-          if (hb && rbk < k) s.ids[t * k + rbk] = eb;
+          s.u.sel.prank[wv][lane] = ra;
+          s.u.sel.prank2[wv][lane] = rbk;
+          __syncthreads();
+          if (on && sl2 == 0) {
+            int rsa = 0, rsb = 0;
+            for (int qq = 0; qq < wpt2; ++qq) {
+              rsa += s.u.sel.prank[wv + qq][lane];
+              rsb += s.u.sel.prank2[wv + qq][lane];
+            }
+            if (ha && rsa < k) s.ids[t * k + rsa] = ea;
+            if (hb && rsb < k) s.ids[t * k + rsb] = eb;
+          }
+          __syncthreads();
         }
       }
     }
     __syncthreads();
+    stamp(a, l, 10);
     // softmax weights of the chosen experts: one wave per token; sums over the
     // experts and the renormalisation run as fixed-order wave reductions
     if (wv < T) {
@@ -459,17 +491,17 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
       if (a.forced) {
         mx = -INFINITY;
         for (int c = 0; c < nch; ++c) mx = fmaxf(mx, lg[c * kWave + lane]);
-        for (int o = kWave / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+        mx = wave_max(mx);
       } else {
         mx = lg[s.ids[t * k]];
       }
       float sm = 0.0f;
       for (int c = 0; c < nch; ++c) sm += expf(lg[c * kWave + lane] - mx);
-      sm = wave_sum_xor(sm, kWave);
+      sm = wave_sum(sm);
       float wj = 0.0f;
       if (lane < k) wj = expf(lg[s.ids[t * k + lane]] - mx) / sm;
       if (a.renorm) {
-        const float tot = wave_sum_xor(lane < k ? wj : 0.0f, kWave);
+        const float tot = wave_sum(lane < k ? wj : 0.0f);
         wj = wj / tot;
       }
       if (lane < k) {
@@ -479,6 +511,7 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
       }
     }
     __syncthreads();
+    stamp(a, l, 11);
     // grouping: distinct experts ("units") in order of first appearance
     if (wv == 0) {
       const int p = lane;
@@ -597,7 +630,9 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         for (int rr = 0; rr < 4; ++rr)
           if (4 * q + rr < T) s.red[wv][4 * q + rr][n16] = acc[rr];
       }
+      stamp(a, l, 13);
       __syncthreads();
+      stamp(a, l, 14);
       if (on && (wv & 1) == 0) {
         // sum the two K halves (sibling waves), SwiGLU, publish FP16 pairs
         const int m = lane >> 3, n = lane & 7;
@@ -641,6 +676,7 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
       if (r > 0 && on) load_d(d_ptrs(task));
       // this wave's direct loads into its LDS region have landed
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (r == 0) stamp(a, l, 12);
       if (on) {
         const int cg = task / ks, kp = task - cg * ks;
         // A row m: unit cg*2 + m/T, token m%T

@@ -98,7 +98,7 @@ constexpr int kFStageHalves = 32768;  // (T*k + shared T) * I FP16 staged in LDS
 constexpr int kFGrid = 256;    // blocks: one per compute unit
 constexpr int kFRows = 8;      // residual rows per block (H / kFGrid)
 constexpr int kFLogitReps = 8; // logit replicas (one per XCD) for small steps
-constexpr int kStampsPerLayer = 11;   // phase timestamps per layer (instrumentation)
+constexpr int kStampsPerLayer = 16;   // phase timestamps per layer (instrumentation)
 constexpr int kStampStride = 64 * kStampsPerLayer;  // per block, up to 64 layers
 struct FusedLayer {
   const uint16_t* router;
