@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--graph", type=int, default=1, help="replay each step as a captured HIP graph")
     p.add_argument("--fused", type=int, default=1,
                    help="1: one persistent kernel per step; 0: per-layer kernels")
+    p.add_argument("--extras", type=int, default=1,
+                   help="1: also measure the batched (prefill / batch-64), Qwen-like and "
+                        "partial-residency workloads, reported under \"extra\"")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="run one device-to-device copy of this many MiB first (a reference "
                         "kernel of known traffic for hardware byte counters)")
@@ -95,6 +98,172 @@ def cpu_baseline(shape, layers_np, h0_np, budget_s):
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} of the {len(h0_np)} batch-1 inputs through all {len(layers_np)} layers "
                       f"(float64 numpy oracle, exact router), {dt:.1f} s"}, outs
+
+
+MFMA_FP16_PEAK_TFLOPS = 2500.0
+N_REPLICAS = 4   # weight replicas rotated through so that 207.6 MB layers do not sit in the 256 MB MALL
+
+
+def _event_time_ms(fn, n, stream):
+    import torch
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def extra_batched(moe, fx, dev, stream):
+    """One OLMoE-shaped layer (route + experts + combine) at 512-token prefill and
+    batch-64 decode; router logits from the seeded FP16 router give the natural
+    per-expert imbalance.  Weights rotate over 4 replicas (830 MB > MALL)."""
+    import numpy as np
+    import torch
+    shape = fx.OLMOE
+    ctx = moe.MoEContext(shape, n_layers=N_REPLICAS, max_tokens=512)
+    for r in range(N_REPLICAS):
+        w = fx.layer_weights(shape, "bench-batched", r, device="cuda", batched=True)
+        ctx.register_layer(r, {k: v.cpu().numpy() for k, v in w.items()})
+        del w
+    res = {}
+    for T, name in ((512, "prefill_512"), (64, "decode_batch64")):
+        x = fx.activations(("bench-batched-x", T), T, shape.hidden, device="cuda")
+        out = torch.empty_like(x)
+        ids_w = [ctx.route(r, x, stream=stream) for r in range(N_REPLICAS)]
+        stream.synchronize()
+
+        def layer(i):
+            r = i % N_REPLICAS
+            ids, w = ctx.route(r, x, stream=stream)
+            ctx.expert_forward(r, x, ids, w, out=out, stream=stream)
+
+        for i in range(8):
+            layer(i)
+        ms = _event_time_ms(layer, 40, stream)
+        # experts' part alone: the MFMA / GEMV expert kernels with ids fixed
+        def experts(i):
+            r = i % N_REPLICAS
+            ids, w = ids_w[r]
+            ctx.expert_forward(r, x, ids, w, out=out, stream=stream)
+        ms_e = _event_time_ms(experts, 40, stream)
+        counts = np.stack([np.bincount(ids.cpu().numpy().ravel(), minlength=shape.n_experts)
+                           for ids, _ in ids_w])
+        pairs = T * shape.top_k
+        flops = 2.0 * pairs * 3 * shape.hidden * shape.inter + 2.0 * T * shape.n_experts * shape.hidden
+        used = float(np.mean((counts > 0).sum(1)))
+        nbytes = used * shape.blob_bytes + shape.n_experts * shape.hidden * 2 + T * shape.hidden * 4
+        res[name] = {
+            "tokens": T, "layer_us": round(ms * 1e3, 2), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "experts_us": round(ms_e * 1e3, 2),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
+            "hbm_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "tokens_per_expert_min_max": [int(counts.min()), int(counts.max())],
+            "experts_used": used,
+        }
+    assert ctx.check_device_errors(stream) == 0
+    ctx.close()
+    return res
+
+
+def extra_qwen(moe, fx, dev, stream, n_layers=8, full_layers=48):
+    """Qwen3-Next-like layers (512 experts, top-10 renormalised, shared expert, I=512),
+    decode at batch 1 and 16: `n_layers` distinct layers are timed; the 48-layer
+    rate is the measured per-layer time times 48 (every layer has the same shape)."""
+    import torch
+    shape = fx.QWEN_NEXT
+    res = {}
+    ctx = moe.MoEContext(shape, n_layers=n_layers, max_tokens=16)
+    for l in range(n_layers):
+        w = fx.layer_weights(shape, "bench-qwen", l, device="cuda", batched=True)
+        ctx.register_layer(l, {k: v.cpu().numpy() for k, v in w.items()})
+        del w
+    for T in (1, 16):
+        h0 = fx.activations(("bench-qwen-h0", T), T, shape.hidden, device="cuda").float()
+        h = torch.empty_like(h0)
+
+        def step(i):
+            h.copy_(h0)
+            ctx.stack_forward(h, stream=stream)
+
+        for i in range(5):
+            step(i)
+        ms = _event_time_ms(step, 30, stream)
+        per_layer_us = ms * 1e3 / n_layers
+        tok_s = T / (per_layer_us * full_layers * 1e-6)
+        entry = {"tokens": T, "layers_timed": n_layers, "per_layer_us": round(per_layer_us, 2),
+                 "tokens_per_s_48_layers": round(tok_s, 1),
+                 "path": "fused" if T <= 4 else "per-layer kernels"}
+        if T == 1:
+            bpt = full_layers * ((shape.top_k + 1) * shape.blob_bytes + shape.n_experts * shape.hidden * 2)
+            entry["bytes_per_token_48_layers"] = bpt
+            entry["hbm_frac"] = round(bpt * tok_s / 1e9 / HBM_PEAK_GBPS, 4)
+        res[f"batch_{T}"] = entry
+    assert ctx.check_device_errors(stream) == 0
+    ctx.close()
+    return res
+
+
+def extra_pool(moe, fx, dev, stream, steps=256, layers=16):
+    """Partial residency on OLMoE shapes: per-layer HBM slot pools of C experts
+    backed by pinned host copies of all 1,024 experts, routing forced by a seeded
+    Zipf(1.1) popularity trace; hit rate, H2D traffic and tokens/s per policy and C,
+    and bit-identity with full residency."""
+    import numpy as np
+    import torch
+    shape = fx.OLMOE
+    lw = [{k: v.cpu().numpy() for k, v in
+           fx.layer_weights(shape, "bench-pool", l, device="cuda", batched=True).items()}
+          for l in range(layers)]
+    trace = fx.zipf_trace("bench-pool-zipf", steps, layers, shape.n_experts, shape.top_k, s=1.1)
+    ftr = torch.from_numpy(trace[:, :, None, :].copy()).cuda()
+    h0s = torch.stack([fx.activations(("bench-pool-h0", i), 1, shape.hidden, device="cuda").float()
+                       for i in range(32)])
+
+    def run(policy, C):
+        ctx = moe.MoEContext(shape, n_layers=layers, max_tokens=1,
+                             policy=policy, slots=C)
+        for l, w in enumerate(lw):
+            ctx.register_layer(l, w)
+        outs = torch.empty((steps, 1, shape.hidden), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for s_ in range(steps):
+                if policy != "resident":
+                    for l in range(layers):
+                        ctx.cache_ensure(l, trace[s_, l], step=s_, stream=stream)
+                outs[s_].copy_(h0s[s_ % 32])
+                ctx.stack_forward(outs[s_], forced_ids=ftr[s_], stream=stream)
+        stream.synchronize()
+        dt = time.perf_counter() - t0
+        stats = [ctx.cache_stats(l) for l in range(layers)] if policy != "resident" else []
+        assert ctx.check_device_errors(stream) == 0
+        ctx.close()
+        return outs, dt, stats
+
+    ref, dt_ref, _ = run("resident", 0)
+    res = {"steps": steps, "layers": layers, "resident_tokens_per_s": round(steps / dt_ref, 1)}
+    for policy, C in (("lru", 16), ("lfu", 16), ("lru", 32), ("lfu", 32), ("lru", 48), ("lfu", 48)):
+        out, dt, st = run(policy, C)
+        acc = sum(x["accesses"] for x in st)
+        hits = sum(x["hits"] for x in st)
+        h2d = sum(x["h2d_bytes"] for x in st)
+        h2d_s = sum(x["h2d_seconds"] for x in st)
+        res[f"{policy}_C{C}"] = {
+            "hit_rate": round(hits / max(acc, 1), 4),
+            "h2d_gb": round(h2d / 1e9, 3),
+            "h2d_gbps_copy": round(h2d / max(h2d_s, 1e-12) / 1e9, 2),
+            "h2d_gbps_wall": round(h2d / dt / 1e9, 2),
+            "tokens_per_s": round(steps / dt, 1),
+            "bit_identical_to_resident": bool(torch.equal(out, ref)),
+        }
+    return res
 
 
 def main():
@@ -235,6 +404,17 @@ def main():
                      "bytes_per_launch": per_launch, "avg_launch_us": round(avg_ms * 1e3, 3),
                      "launches": launches},
     }
+    if args.extras:
+        stream.synchronize()
+        extra = {}
+        t_x = time.perf_counter()
+        extra["olmoe_layer_batched"] = extra_batched(moe, fx, dev, stream)
+        print(f"[bench] batched extras done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
+        extra["qwen_next_like_stack"] = extra_qwen(moe, fx, dev, stream)
+        print(f"[bench] qwen extras done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
+        extra["partial_residency_olmoe16"] = extra_pool(moe, fx, dev, stream)
+        print(f"[bench] pool extras done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
+        out["extra"] = extra
     if not args.no_cpu_baseline:
         h0_np = [h0[i].cpu().numpy().astype(np.float16) for i in range(N_INPUTS)]
         cb, refs = cpu_baseline(shape, layers_np, h0_np, args.cpu_seconds)
