@@ -81,6 +81,7 @@ struct moe_ctx {
   uint64_t* xgate = nullptr;
   uint32_t* epoch = nullptr;   // per-block epoch counters
   int grid = 0;
+  int ncu = 1;                 // compute units (grid of the streaming kernel)
   uint64_t* stamps = nullptr;  // caller-owned phase-timestamp buffer or null
   // kernel timer
   int timer_kind = -1;
@@ -223,8 +224,15 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   const moe_config& g = c->cfg;
   // experts with at least mfma_min tokens run on the MFMA grouped GEMM; the
   // choice depends only on the token counts
-  const int mfma_min = (g.flags & MOE_FLAG_FORCE_GEMV) ? INT32_MAX
-                       : (g.flags & MOE_FLAG_FORCE_MFMA) ? 1 : kMfmaMinTokens;
+  // experts with few tokens take the persistent streaming kernel where the
+  // shapes allow it (then every expert with up to kStreamTokens tokens), else
+  // the GEMV kernels
+  const bool force_gemv = (g.flags & MOE_FLAG_FORCE_GEMV) != 0;
+  const bool stream_gu = !force_gemv && stream_supported(0, g.hidden, g.inter);
+  const bool stream_dn = !force_gemv && stream_supported(1, g.inter, g.hidden);
+  const int mfma_min = force_gemv ? INT32_MAX
+                       : (g.flags & MOE_FLAG_FORCE_MFMA) ? 1
+                       : (stream_gu ? kStreamTokens + 1 : kMfmaMinTokens);
   GroupArgs ga{ids, T, g.top_k, g.n_experts, L.map, c->ids_s, c->active, c->n_active,
                c->perm_tok, c->pos_of, c->err, mfma_min, c->mtile_off};
   {
@@ -250,7 +258,8 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   ea.ybuf = c->ybuf;
   {
     ScopedTimer tm(c, kKindGateUp, s);
-    launch_gateup_gemv(ea, s);
+    if (stream_gu) launch_stream_expert(ea, 0, c->ncu, s);
+    else launch_gateup_gemv(ea, s);
   }
   if (any_mfma) {
     ScopedTimer tm(c, kKindMfmaGateUp, s);
@@ -258,7 +267,8 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   }
   {
     ScopedTimer tm(c, kKindDown, s);
-    launch_down_gemv(ea, s);
+    if (stream_dn && stream_gu) launch_stream_expert(ea, 1, c->ncu, s);
+    else launch_down_gemv(ea, s);
   }
   if (any_mfma) {
     ScopedTimer tm(c, kKindMfmaDown, s);
@@ -273,8 +283,12 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
     sa.I = g.shared_inter;
     sa.hbuf = c->hshared;
     sa.ybuf = c->yshared;
-    launch_gateup_gemv(sa, s);
-    launch_down_gemv(sa, s);
+    const bool st_gu = !force_gemv && T <= kStreamTokens && stream_supported(0, g.hidden, g.shared_inter);
+    const bool st_dn = st_gu && stream_supported(1, g.shared_inter, g.hidden);
+    if (st_gu) launch_stream_expert(sa, 0, c->ncu, s);
+    else launch_gateup_gemv(sa, s);
+    if (st_dn) launch_stream_expert(sa, 1, c->ncu, s);
+    else launch_down_gemv(sa, s);
   }
   CombineArgs ca{c->ybuf, g.shared_inter ? c->yshared : nullptr, c->pos_of, w, T, g.top_k,
                  g.hidden, out, resid};
@@ -373,6 +387,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     int ncu = 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, g.device) != hipSuccess) ncu = 0;
     c->grid = ncu >= kFGrid ? kFGrid : 0;
+    c->ncu = ncu > 0 ? ncu : 1;
     ok = ok && dalloc((void**)&c->xh, (size_t)kFXhWords * 8);
     ok = ok && dalloc((void**)&c->xlg, (size_t)kFXlgWords * 8);
     ok = ok && dalloc((void**)&c->xhb, (size_t)kFXhbWords * 8);

@@ -155,23 +155,6 @@ __device__ __forceinline__ void read_tagged(const uint64_t* src, int n, uint32_t
   }
 }
 
-// Direct global -> LDS loads (gfx950 LDS DMA): lane l's `bytes` land at the
-// wave-uniform LDS address `lds` + l * bytes.  Written as inline assembly so
-// that the compiler neither stalls on them when it reuses their address
-// registers nor waits for them before unrelated loads; they still count in
-// vmcnt, and the LDS data is read only after an explicit vmcnt(0).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void dma_lds16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
-}
-__device__ __forceinline__ void dma_lds4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
-}
-
 // INT4 dword of 8 K values -> the 8 FP16 operands of one MFMA step.
 __device__ __forceinline__ h8 decode_h8(uint32_t d) {
   h2 p[4];

@@ -63,6 +63,22 @@ struct MfmaSmem {
   int tok[kMT];
 };
 
+// Tiles of few tokens keep their whole activation block (all K) in LDS, so the
+// main loop has no barrier and no activation traffic and only streams weights,
+// with a deeper ring of weight groups in flight.  Fits when MS * K <= 4096.
+constexpr int kFullRing = 8;
+constexpr int kAFullHalves = 64 * (1024 + kAPad);  // >= MS*16 x (K + pad) for MS*K <= 4096
+struct MfmaSmemFull {
+  _Float16 a[kAFullHalves];
+  int tok[kMT];
+};
+union MfmaShared {
+  MfmaSmem d;
+  MfmaSmemFull f;
+};
+template <int MODE, int MS>
+constexpr bool afull_fits(int K) { return MS * K <= 4096; }
+
 // One tile with MS 16-token sub-tiles (MS*16 >= tokens in the tile).
 // MODE 0: gate/up + SwiGLU -> hbuf FP16 [position, I]; MODE 1: down -> ybuf FP32 [position, H].
 template <int MODE, int MS>
@@ -221,9 +237,124 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, MfmaSmem& s, const 
   }
 }
 
+// Same arithmetic and summation order as mfma_tile, activation block resident.
+template <int MODE, int MS>
+__device__ __forceinline__ void mfma_tile_full(const MfmaArgs& a, MfmaSmemFull& s, const ActiveExpert& ae,
+                                               int m0, int mcount, int nt) {
+  constexpr int K = MODE == 0 ? 2048 : 1024;  // H (gate/up) or I (down) of the shapes that take this path
+  constexpr int LD = K + kAPad;               // LDS row stride (halves)
+  constexpr int NG = K / kKC;
+  static_assert(MS * 16 * LD <= kAFullHalves, "activation block fits");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 15, q = lane >> 4;
+  const uint8_t* blob = a.blobs + (int64_t)ae.slot * a.blob_stride;
+  const uint8_t* codes[2];
+  const uint16_t* scales[2];
+  int row[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int mat, r;
+    if (MODE == 0) {
+      mat = j;
+      r = nt * (kMW * 16) + wv * 16 + n;
+    } else {
+      mat = 2;
+      r = nt * (kMW * 32) + wv * 32 + j * 16 + n;
+    }
+    row[j] = r;
+    codes[j] = blob + a.lay.codes(mat) + (int64_t)r * (K / 2) + q * 16;
+    scales[j] = reinterpret_cast<const uint16_t*>(blob + a.lay.scales(mat)) + (int64_t)r * NG;
+  }
+  // the activation block goes straight to LDS (direct loads: no registers),
+  // 512 halves of one row per wave instruction; rows past the tile's tokens
+  // are zero; then the first kFullRing - 1 weight groups go out
+  if (tid < kMT) {
+    int v = -1;
+    if (tid < mcount) v = MODE == 0 ? a.perm_tok[ae.offset + m0 + tid] : ae.offset + m0 + tid;
+    s.tok[tid] = v;
+  }
+  __syncthreads();
+  {
+    const uint16_t* src = MODE == 0 ? a.x : a.hbuf;
+    constexpr int SEG = K / 512;                      // 1-KB segments per row
+    for (int c = wv; c < MS * 16 * SEG; c += kMW) {   // wave-uniform
+      const int r = c / SEG, b = c - r * SEG;
+      _Float16* dst = &s.a[r * LD + b * 512];
+      if (r < mcount)
+        dma_lds16(src + (int64_t)s.tok[r] * K + b * 512 + lane * 8, lds_addr(dst));
+      else
+        *reinterpret_cast<u4*>(dst + lane * 8) = u4{0u, 0u, 0u, 0u};
+    }
+  }
+  u4 bq[kFullRing][2];
+  uint32_t bs[kFullRing][2];
+  auto load_b = [&](int g, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bq[slot][j] = *reinterpret_cast<const u4*>(codes[j] + g * 64);
+      bs[slot][j] = scales[j][g];
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kFullRing - 1; ++u) load_b(min(u, NG - 1), u);
+  // the direct loads were issued first, so they have landed once all but the
+  // weight loads issued after them are done; the barrier publishes them
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  f4 acc[MS][2];
+#pragma unroll
+  for (int mi = 0; mi < MS; ++mi) acc[mi][0] = acc[mi][1] = f4{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](int g, auto uc) __attribute__((always_inline)) {
+    constexpr int U = decltype(uc)::value;
+    load_b(min(g + kFullRing - 1, NG - 1), (U + kFullRing - 1) % kFullRing);
+    __builtin_amdgcn_sched_barrier(0);
+    h2 s2[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)bs[U][j]);
+      s2[j] = h2{sv, sv};
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const h8 b0 = decode_scaled(bq[U][0][st], s2[0]);
+      const h8 b1 = decode_scaled(bq[U][1][st], s2[1]);
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi) {
+        const h8 af = *reinterpret_cast<const h8*>(&s.a[(mi * 16 + n) * LD + g * kKC + 32 * q + 8 * st]);
+        acc[mi][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b0, acc[mi][0], 0, 0, 0);
+        acc[mi][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b1, acc[mi][1], 0, 0, 0);
+      }
+    }
+  };
+  static_assert(NG % kFullRing == 0, "whole rings of groups");
+  for (int g = 0; g < NG; g += kFullRing) {
+    [&]<int... Us>(std::integer_sequence<int, Us...>) {
+      (step(g + Us, std::integral_constant<int, Us>{}), ...);
+    }(std::make_integer_sequence<int, kFullRing>{});
+  }
+#pragma unroll
+  for (int mi = 0; mi < MS; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tr = mi * 16 + 4 * q + r;
+      if (tr >= mcount) continue;
+      const int pos = ae.offset + m0 + tr;
+      if (MODE == 0) {
+        const float gv = acc[mi][0][r], uv = acc[mi][1][r];
+        reinterpret_cast<_Float16*>(a.hbuf)[(int64_t)pos * a.I + row[0]] =
+            (_Float16)(gv / (1.0f + expf(-gv)) * uv);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) a.ybuf[(int64_t)pos * a.H + row[j]] = acc[mi][j][r];
+      }
+    }
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kMW * kWave) void mfma_expert_kernel(MfmaArgs a) {
-  __shared__ MfmaSmem s;
+  __shared__ MfmaShared sh;
+  MfmaSmem& s = sh.d;
   const int rows_per_block = kMW * (MODE == 0 ? 16 : 32);
   const int ntn = (MODE == 0 ? a.I : a.H) / rows_per_block;
   // block -> (token tile mg, row tile nt): the ntn row tiles of a token tile
@@ -243,11 +374,25 @@ __global__ __launch_bounds__(kMW * kWave) void mfma_expert_kernel(MfmaArgs a) {
   const int mcount = min(kMT, ae.count - m0);
   // exactly as many 16-token sub-tiles as the tile needs: MFMA work is not
   // padded beyond the next multiple of 16 tokens
+  // the resident-activation tiles serve the two shapes it is built for
+  const bool full_ok = (MODE == 0 ? a.H : a.I) == (MODE == 0 ? 2048 : 1024);
   switch ((mcount + 15) >> 4) {
-    case 1: mfma_tile<MODE, 1>(a, s, ae, m0, mcount, nt); break;
-    case 2: mfma_tile<MODE, 2>(a, s, ae, m0, mcount, nt); break;
-    case 3: mfma_tile<MODE, 3>(a, s, ae, m0, mcount, nt); break;
-    case 4: mfma_tile<MODE, 4>(a, s, ae, m0, mcount, nt); break;
+    case 1:
+      if (full_ok) mfma_tile_full<MODE, 1>(a, sh.f, ae, m0, mcount, nt);
+      else mfma_tile<MODE, 1>(a, s, ae, m0, mcount, nt);
+      break;
+    case 2:
+      if (full_ok) mfma_tile_full<MODE, 2>(a, sh.f, ae, m0, mcount, nt);
+      else mfma_tile<MODE, 2>(a, s, ae, m0, mcount, nt);
+      break;
+    case 3:
+      if (MODE == 1 && full_ok) mfma_tile_full<1, 3>(a, sh.f, ae, m0, mcount, nt);
+      else mfma_tile<MODE, 3>(a, s, ae, m0, mcount, nt);
+      break;
+    case 4:
+      if (MODE == 1 && full_ok) mfma_tile_full<1, 4>(a, sh.f, ae, m0, mcount, nt);
+      else mfma_tile<MODE, 4>(a, s, ae, m0, mcount, nt);
+      break;
     case 5: mfma_tile<MODE, 5>(a, s, ae, m0, mcount, nt); break;
     case 6: mfma_tile<MODE, 6>(a, s, ae, m0, mcount, nt); break;
     case 7: mfma_tile<MODE, 7>(a, s, ae, m0, mcount, nt); break;

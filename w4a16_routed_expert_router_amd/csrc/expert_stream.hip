@@ -1,0 +1,252 @@
+// Expert FFN for experts that receive few tokens (batched decode, the small
+// experts of a prefill, the shared expert of a small batch): a persistent
+// weight-streaming kernel on FP16 MFMA.
+//
+// The experts run straight from packed INT4 codes with FP16 group scales and
+// FP16 activations; weights are never expanded in memory ("Horizon RunMap",
+// "Architecture invariants").  With at most 16 tokens per expert the work is
+// bound by streaming the weights, so the kernel is shaped for that:
+//   * one block per compute unit takes a contiguous run of work items
+//     (expert, tile of output rows), so consecutive items are mostly row tiles
+//     of the same expert and its activation tile stays in LDS;
+//   * every wave streams "units" (one 128-wide scale group of its two 16-row
+//     weight sub-tiles, 2 KiB) through a ring of kRing units in registers; the
+//     ring runs across item boundaries, so the weight stream never drains
+//     between items and no barrier stops it (a barrier is taken only when the
+//     next item belongs to another expert and its activations are loaded);
+//   * the tokens of the expert (<= 16, zero-padded) are the A operand of
+//     v_mfma_f32_16x16x32_f16; INT4 codes are decoded in registers and scaled
+//     by their FP16 group scale (the same arithmetic, decode and summation
+//     order as the grouped-GEMM kernel).
+// MFMA operand layout (gfx950): lane l holds A[l%16][8*(l/16)+e],
+// B[8*(l/16)+e][l%16], D[4*(l/16)+r][l%16]; the K index of step st, lane group
+// q, element e is 128g + 32q + 8st + e for both operands.
+#include <utility>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSW = 8;          // waves per block
+constexpr int kRing = 8;        // weight units in flight per wave
+constexpr int kTok = 16;        // tokens per expert handled here
+constexpr int kPad = 8;         // LDS row padding (halves)
+constexpr int kMaxList = 1024;  // experts per call
+
+__device__ __forceinline__ h8 decode_scaled(uint32_t d, h2 s2) {
+  h2 p[4];
+  dequant8(d, p);
+  p[0] *= s2; p[1] *= s2; p[2] *= s2; p[3] *= s2;
+  h8 r;
+  r[0] = p[0][0]; r[1] = p[0][1]; r[2] = p[1][0]; r[3] = p[1][1];
+  r[4] = p[2][0]; r[5] = p[2][1]; r[6] = p[3][0]; r[7] = p[3][1];
+  return r;
+}
+
+template <int K>
+struct StreamSmem {
+  _Float16 a[kTok * (K + kPad)];  // activation tile of the current expert
+  int slot[kMaxList];             // small experts of the call: blob slot, count, offset
+  int count[kMaxList];
+  int offset[kMaxList];
+  int tok[kTok];
+  int ns;
+  int scan[kSW];
+};
+
+}  // namespace
+
+// MODE 0: gate/up + SwiGLU (K = H, rows = I, 128 rows per item);
+// MODE 1: down (K = I, rows = H, 256 rows per item).
+template <int MODE, int K>
+__global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a) {
+  __shared__ StreamSmem<K> s;
+  constexpr int LD = K + kPad;
+  constexpr int NG = K / kGroup;
+  constexpr int ROWS = MODE == 0 ? kSW * 16 : kSW * 32;
+  static_assert(NG % 2 == 0 || NG == 1, "scale groups per row");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 15, q = lane >> 4;
+  const int N = MODE == 0 ? a.I : a.H;
+  const int ntn = N / ROWS;
+
+  // ---- the call's experts with at most 16 tokens (and below the MFMA threshold)
+  if (a.fixed_blob) {
+    if (tid == 0) {
+      s.slot[0] = 0;
+      s.count[0] = a.fixed_count;
+      s.offset[0] = a.fixed_offset;
+      s.ns = 1;
+    }
+  } else {
+    const int na = *a.n_active;
+    int base = 0;
+    for (int c0 = 0; c0 < na; c0 += kSW * kWave) {  // uniform
+      const int ai = c0 + tid;
+      ActiveExpert ae{0, 0, 0, 0};
+      bool take = false;
+      if (ai < na) {
+        ae = a.active[ai];
+        take = ae.count > 0 && ae.count <= kTok && ae.count < a.mfma_min;
+      }
+      const uint64_t m = __ballot(take);
+      const int before = __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == 0) s.scan[wv] = __popcll(m);
+      __syncthreads();
+      int wbase = base;
+      for (int w = 0; w < wv; ++w) wbase += s.scan[w];
+      int tot = 0;
+      for (int w = 0; w < kSW; ++w) tot += s.scan[w];
+      if (take) {
+        const int p = wbase + before;
+        s.slot[p] = ae.slot;
+        s.count[p] = ae.count;
+        s.offset[p] = ae.offset;
+      }
+      base += tot;
+      __syncthreads();
+    }
+    if (tid == 0) s.ns = base;
+  }
+  __syncthreads();
+  const int items = s.ns * ntn;
+  const int per = (items + gridDim.x - 1) / gridDim.x;
+  const int lo = blockIdx.x * per;
+  const int hi = min(items, lo + per);
+  if (lo >= hi) return;  // uniform over the block
+  const int nv = (hi - lo) * NG;  // units of every wave
+
+  // ---- weight stream: unit v = (item lo + v / NG, scale group v % NG)
+  // The unit loads are issued as inline assembly and waited for explicitly:
+  // every step issues exactly kUnitLoads loads (the tail re-reads the last
+  // unit), so the loads younger than unit v are always (kRing - 1) *
+  // kUnitLoads and "vmcnt <= that" means unit v has landed (loads return in
+  // order; stores and the activation-tile loads only make the wait longer).
+  // The compiler tracks none of these loads, so it never drains the ring.
+  constexpr int kUnitLoads = 4;
+  u4 bq[kRing][2];
+  uint32_t bs[kRing][2];
+  auto load_unit = [&](int v, int slot_) __attribute__((always_inline)) {
+    const int it = lo + v / NG, g = v - (v / NG) * NG;
+    const int se = it / ntn, nt = it - se * ntn;
+    const uint8_t* blob = a.fixed_blob ? a.fixed_blob : a.blobs + (int64_t)s.slot[se] * a.blob_stride;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int mat = MODE == 0 ? j : 2;
+      const int r = MODE == 0 ? nt * ROWS + wv * 16 + n : nt * ROWS + wv * 32 + j * 16 + n;
+      const uint8_t* cp = blob + a.lay.codes(mat) + (int64_t)r * (K / 2) + q * 16 + g * 64;
+      const uint8_t* sp = blob + a.lay.scales(mat) + ((int64_t)r * NG + g) * 2;
+      asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(bq[slot_][j]) : "v"(cp) : "memory");
+      asm volatile("global_load_ushort %0, %1, off" : "=v"(bs[slot_][j]) : "v"(sp) : "memory");
+    }
+  };
+  auto wait_unit = [&](int slot_) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(%4)"
+                 : "+v"(bq[slot_][0]), "+v"(bq[slot_][1]), "+v"(bs[slot_][0]), "+v"(bs[slot_][1])
+                 : "n"((kRing - 1) * kUnitLoads)
+                 : "memory");
+  };
+#pragma unroll
+  for (int u = 0; u < kRing - 1; ++u) load_unit(min(u, nv - 1), u);
+
+  // ---- activation tile of one expert: rows = its tokens, zero past the count
+  int cur = -1;  // small-expert index whose tile is in LDS
+  auto load_tile = [&](int se) __attribute__((always_inline)) {
+    __syncthreads();  // every wave is done with the previous tile
+    const int cnt = s.count[se];
+    if (tid < kTok) {
+      int v = -1;
+      if (tid < cnt) v = a.fixed_blob ? tid : (MODE == 0 ? a.perm_tok[s.offset[se] + tid] : s.offset[se] + tid);
+      s.tok[tid] = v;
+    }
+    __syncthreads();
+    const uint16_t* src = MODE == 0 ? a.x : a.hbuf;
+    for (int c = tid; c < kTok * (K / 8); c += kSW * kWave) {
+      const int r = c / (K / 8), col = (c - r * (K / 8)) * 8;
+      u4 v = u4{0u, 0u, 0u, 0u};
+      if (r < cnt) {
+        const int t = s.tok[r];
+        // gate/up reads token rows of x; down reads the rows of hbuf at the
+        // expert's positions (the shared expert: positions offset + t)
+        const int64_t src_row = MODE == 0 ? (int64_t)t : (a.fixed_blob ? (int64_t)s.offset[se] + t : (int64_t)t);
+        v = *reinterpret_cast<const u4*>(src + src_row * K + col);
+      }
+      *reinterpret_cast<u4*>(&s.a[r * LD + col]) = v;
+    }
+    __syncthreads();
+    cur = se;
+  };
+
+  f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+  auto step = [&](int v, auto uc) __attribute__((always_inline)) {
+    constexpr int U = decltype(uc)::value;
+    const int it = lo + v / NG, g = v - (v / NG) * NG;
+    const int se = it / ntn;
+    if (g == 0 && se != cur) load_tile(se);  // uniform: same v sequence in every wave
+    load_unit(min(v + kRing - 1, nv - 1), (U + kRing - 1) % kRing);
+    wait_unit(U);
+    h2 s2[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)bs[U][j]);
+      s2[j] = h2{sv, sv};
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const h8 af = *reinterpret_cast<const h8*>(&s.a[n * LD + g * kGroup + 32 * q + 8 * st]);
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, decode_scaled(bq[U][0][st], s2[0]), acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, decode_scaled(bq[U][1][st], s2[1]), acc[1], 0, 0, 0);
+    }
+    if (g == NG - 1) {
+      // item done: lane holds D[token 4q + r][row n] of both sub-tiles
+      const int nt = it - se * ntn;
+      const int cnt = s.count[se], off = s.offset[se];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tr = 4 * q + r;
+        if (tr < cnt) {
+          const int64_t pos = off + tr;
+          if (MODE == 0) {
+            const int row = nt * ROWS + wv * 16 + n;
+            const float gv = acc[0][r], uv = acc[1][r];
+            reinterpret_cast<_Float16*>(a.hbuf)[pos * a.I + row] = (_Float16)(gv / (1.0f + expf(-gv)) * uv);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) a.ybuf[pos * a.H + nt * ROWS + wv * 32 + j * 16 + n] = acc[j][r];
+          }
+        }
+      }
+      acc[0] = acc[1] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  for (int v0 = 0; v0 < nv; v0 += kRing) {
+    [&]<int... Us>(std::integer_sequence<int, Us...>) {
+      ((v0 + Us < nv ? step(v0 + Us, std::integral_constant<int, Us>{}) : void()), ...);
+    }(std::make_integer_sequence<int, kRing>{});
+  }
+}
+
+bool stream_supported(int mode, int K, int rows) {
+  const int per_item = mode == 0 ? kSW * 16 : kSW * 32;
+  if (rows % per_item) return false;
+  return mode == 0 ? K == 2048 : (K == 1024 || K == 512);
+}
+
+void launch_stream_expert(const ExpertArgs& a, int mode, int grid, hipStream_t stream) {
+  if (mode == 0) {
+    hipLaunchKernelGGL((stream_expert_kernel<0, 2048>), dim3(grid), dim3(kSW * kWave), 0, stream, a);
+  } else if (a.I == 1024) {
+    hipLaunchKernelGGL((stream_expert_kernel<1, 1024>), dim3(grid), dim3(kSW * kWave), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((stream_expert_kernel<1, 512>), dim3(grid), dim3(kSW * kWave), 0, stream, a);
+  }
+}
+
+}  // namespace moe

@@ -74,6 +74,11 @@ struct ExpertArgs {
   int mfma_min;               // routed experts with count >= this are skipped (MFMA path)
 };
 void launch_gateup_gemv(const ExpertArgs& a, hipStream_t stream);
+// Persistent weight-streaming expert kernel (expert_stream.hip) for experts with
+// at most kStreamTokens tokens (and below mfma_min); mode 0 gate/up, 1 down.
+constexpr int kStreamTokens = 16;
+bool stream_supported(int mode, int K, int rows);
+void launch_stream_expert(const ExpertArgs& a, int mode, int grid, hipStream_t stream);
 void launch_down_gemv(const ExpertArgs& a, hipStream_t stream);
 
 struct CombineArgs {
