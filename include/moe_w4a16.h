@@ -239,9 +239,12 @@ moe_status moe_timer_read(moe_ctx* ctx, double* total_ms, int64_t* launches);
  * fused launches writes the GPU's 100 MHz real-time counter at each phase
  * boundary to dev_buf[block*stride + (layer - layer_begin)*per_layer + event]
  * and its shader-clock counter at the same index + grid*stride; events
- * 0 layer start, 1 norm done, 2 logits done, 3 after barrier A, 4 logits in
- * LDS, 5 ranking done, 6 selection and grouping done, 7 gate/up done, 8 after
- * barrier B, 9 down done, 10 after barrier C.
+ * 0 layer start, 1 residual exchanged and normalised, 2 router logits
+ * published, 3 logits exchanged, 4 selection and grouping done, 5 weight loads
+ * issued, 6 gate/up published, 7 intermediates exchanged, 8 down projection
+ * done, 9 residual rows published, 10 ranking done, 11 softmax done,
+ * 12 down weights in LDS, 13 gate/up MFMA done, 14 gate/up partials summed.
+ * Only the first 64 layers of a call are stamped.
  * dev_buf NULL disables.  grid, stride and per_layer (optional outputs)
  * receive the layout. */
 moe_status moe_fused_phase_stamps(moe_ctx* ctx, uint64_t* dev_buf, int64_t count, int32_t* grid,

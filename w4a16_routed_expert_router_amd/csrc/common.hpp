@@ -73,6 +73,31 @@ __device__ __forceinline__ uint4 ldg_u4(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// (a & m) | o in one VALU instruction.  gfx9 VOP3 takes one scalar operand,
+// so the mask comes in a VGPR (callers keep it in one across their loop).
+__device__ __forceinline__ uint32_t and_or_b32(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "s"(o));
+  return r;
+}
+
+// dequant8 with the masks held in VGPRs (mlo = 0x000F000F, mhi = 0x00F000F0):
+// five instructions form the four FP16 pairs, four more turn them into q - 8.
+__device__ __forceinline__ void dequant8_v(uint32_t d, h2 out[4], uint32_t mlo, uint32_t mhi) {
+  const uint32_t d8 = d >> 8;
+  const h2 lo0 = __builtin_bit_cast(h2, and_or_b32(d, mlo, 0x64006400u));
+  const h2 hi0 = __builtin_bit_cast(h2, and_or_b32(d, mhi, 0x64006400u));
+  const h2 lo1 = __builtin_bit_cast(h2, and_or_b32(d8, mlo, 0x64006400u));
+  const h2 hi1 = __builtin_bit_cast(h2, and_or_b32(d8, mhi, 0x64006400u));
+  const h2 k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const h2 k16th = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const h2 km72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  out[0] = lo0 - k1032;
+  out[1] = hi0 * k16th + km72;
+  out[2] = lo1 - k1032;
+  out[3] = hi1 * k16th + km72;
+}
+
 __device__ __forceinline__ float dot2(h2 a, h2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }

@@ -91,7 +91,7 @@ struct FusedSmem {
 };
 
 __device__ __forceinline__ void stamp(const FusedArgs& a, int l, int ev) {
-  if (a.stamps && threadIdx.x == 0) {
+  if (a.stamps && threadIdx.x == 0 && l - a.l0 < kStampStride / kStampsPerLayer) {
     const int64_t i = (int64_t)blockIdx.x * kStampStride + (l - a.l0) * kStampsPerLayer + ev;
     a.stamps[i] = __builtin_amdgcn_s_memrealtime();
     a.stamps[(int64_t)gridDim.x * kStampStride + i] = __builtin_amdgcn_s_memtime();

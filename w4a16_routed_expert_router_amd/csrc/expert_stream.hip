@@ -15,9 +15,9 @@
 //     between items and no barrier stops it (a barrier is taken only when the
 //     next item belongs to another expert and its activations are loaded);
 //   * the tokens of the expert (<= 16, zero-padded) are the A operand of
-//     v_mfma_f32_16x16x32_f16; INT4 codes are decoded in registers and scaled
-//     by their FP16 group scale (the same arithmetic, decode and summation
-//     order as the grouped-GEMM kernel).
+//     v_mfma_f32_16x16x32_f16; INT4 codes are decoded in registers to the
+//     exact FP16 values q - 8, and each 128-wide group's FP32 MFMA result is
+//     multiplied by its FP16 scale before it is added to the accumulator.
 // MFMA operand layout (gfx950): lane l holds A[l%16][8*(l/16)+e],
 // B[8*(l/16)+e][l%16], D[4*(l/16)+r][l%16]; the K index of step st, lane group
 // q, element e is 128g + 32q + 8st + e for both operands.
@@ -40,10 +40,12 @@ constexpr int kTok = 16;        // tokens per expert handled here
 constexpr int kPad = 8;         // LDS row padding (halves)
 constexpr int kMaxList = 1024;  // experts per call
 
-__device__ __forceinline__ h8 decode_scaled(uint32_t d, h2 s2) {
+// 8 INT4 codes -> (q - 8) as FP16 (exact); the group scale is applied to the
+// FP32 MFMA result of the group instead (one FMA per output, fewer VALU
+// instructions per weight than scaling every weight when few tokens share it).
+__device__ __forceinline__ h8 decode_unscaled(uint32_t d, uint32_t mlo, uint32_t mhi) {
   h2 p[4];
-  dequant8(d, p);
-  p[0] *= s2; p[1] *= s2; p[2] *= s2; p[3] *= s2;
+  dequant8_v(d, p, mlo, mhi);
   h8 r;
   r[0] = p[0][0]; r[1] = p[0][1]; r[2] = p[1][0]; r[3] = p[1][1];
   r[4] = p[2][0]; r[5] = p[2][1]; r[6] = p[3][0]; r[7] = p[3][1];
@@ -185,6 +187,8 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   };
 
   f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+  uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u;
+  asm("" : "+v"(mlo), "+v"(mhi));  // the decode masks live in VGPRs
   auto step = [&](int v, auto uc) __attribute__((always_inline)) {
     constexpr int U = decltype(uc)::value;
     const int it = lo + v / NG, g = v - (v / NG) * NG;
@@ -192,18 +196,15 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
     if (g == 0 && se != cur) load_tile(se);  // uniform: same v sequence in every wave
     load_unit(min(v + kRing - 1, nv - 1), (U + kRing - 1) % kRing);
     wait_unit(U);
-    h2 s2[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)bs[U][j]);
-      s2[j] = h2{sv, sv};
-    }
+    f4 ag[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const h8 af = *reinterpret_cast<const h8*>(&s.a[n * LD + g * kGroup + 32 * q + 8 * st]);
-      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, decode_scaled(bq[U][0][st], s2[0]), acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, decode_scaled(bq[U][1][st], s2[1]), acc[1], 0, 0, 0);
+      ag[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, decode_unscaled(bq[U][0][st], mlo, mhi), ag[0], 0, 0, 0);
+      ag[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, decode_unscaled(bq[U][1][st], mlo, mhi), ag[1], 0, 0, 0);
     }
+    acc[0] += ag[0] * half_bits_to_float((uint16_t)bs[U][0]);
+    acc[1] += ag[1] * half_bits_to_float((uint16_t)bs[U][1]);
     if (g == NG - 1) {
       // item done: lane holds D[token 4q + r][row n] of both sub-tiles
       const int nt = it - se * ntn;
