@@ -244,7 +244,8 @@ moe_status moe_timer_read(moe_ctx* ctx, double* total_ms, int64_t* launches);
  * issued, 6 gate/up published, 7 intermediates exchanged, 8 down projection
  * done, 9 residual rows published, 10 ranking done, 11 softmax done,
  * 12 down weights in LDS, 13 gate/up MFMA done, 14 gate/up partials summed.
- * Only the first 64 layers of a call are stamped.
+ * Only the first 16 layers of a call are stamped; the stamps are kept on chip
+ * and written when the launch ends.
  * dev_buf NULL disables.  grid, stride and per_layer (optional outputs)
  * receive the layout. */
 moe_status moe_fused_phase_stamps(moe_ctx* ctx, uint64_t* dev_buf, int64_t count, int32_t* grid,

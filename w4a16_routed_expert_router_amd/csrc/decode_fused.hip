@@ -62,14 +62,16 @@ constexpr uint32_t kSpinLimit = 1u << 18;  // polls of one word before giving up
 
 template <int I>
 struct FusedSmem {
-  _Float16 x[kFMaxT * 2048];                 // normalised tokens (gate/up A operand)
-  union {
+  alignas(16) _Float16 x[kFMaxT * 2048];     // normalised tokens (gate/up A operand)
+  alignas(16) _Float16 xz[32];               // zeros: the A operand of padding rows
+  union alignas(16) {
     struct {
       float logit[kFMaxTE];                  // logits of the step
       float cval[kFMaxT][kFMaxCand];         // per-chunk candidates (E > 64)
       int cid[kFMaxT][kFMaxCand];
       int prank[kFW][kWave];                 // partial ranks of the waves
       int prank2[kFW][kWave];
+      uint64_t key[kFW][kWave];              // per-wave (logit, id) sort keys
     } sel;
     _Float16 hst[kFStageHalves];             // intermediates of every pair (down A operand)
     float hfull[kFStageHalves / 2];          // residual of every token (E1 staging)
@@ -88,13 +90,18 @@ struct FusedSmem {
   // global->LDS loads: codes [group][lane] 16 B, scales [lane] 2 groups
   uint4 dpre[kFW][I / 128][kWave];
   uint32_t dsc[kFW][kWave];
+  // phase timestamps (instrumentation): kept in LDS during the call and
+  // written out at its end, so that no timestamp store is in flight while a
+  // phase waits for its own memory operations
+  uint64_t stampbuf[2][kStampStride];
 };
 
-__device__ __forceinline__ void stamp(const FusedArgs& a, int l, int ev) {
-  if (a.stamps && threadIdx.x == 0 && l - a.l0 < kStampStride / kStampsPerLayer) {
-    const int64_t i = (int64_t)blockIdx.x * kStampStride + (l - a.l0) * kStampsPerLayer + ev;
-    a.stamps[i] = __builtin_amdgcn_s_memrealtime();
-    a.stamps[(int64_t)gridDim.x * kStampStride + i] = __builtin_amdgcn_s_memtime();
+template <class S>
+__device__ __forceinline__ void stamp(S& s, const FusedArgs& a, int l, int ev) {
+  if (a.stamps && threadIdx.x == 0 && l - a.l0 < kStampLayers) {
+    const int i = (l - a.l0) * kStampsPerLayer + ev;
+    s.stampbuf[0][i] = __builtin_amdgcn_s_memrealtime();
+    s.stampbuf[1][i] = __builtin_amdgcn_s_memtime();
   }
 }
 
@@ -232,7 +239,8 @@ template <int H, int I>
 __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
   __shared__ FusedSmem<I> s;
   static_assert(H / kFRows == kFGrid, "one block per 8 residual rows");
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int b = blockIdx.x;
   const int T = a.T, E = a.E, k = a.k;
   const int P = T * k;
@@ -255,14 +263,25 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
   bool bail = false;
   uint32_t errs = 0;
 
+  if (tid < 32) s.xz[tid] = (_Float16)0.0f;
   uint4 rq[H / 512];  // router part of the wave's first logit item
   if (item0 < TE) load_router_part<H>(a.layers[a.l0].router + (int64_t)(item0 % E) * H + lpoff, nchunk, lane, rq);
 
   for (int l = a.l0; l < a.l1; ++l) {
+    // Lane-derived indices are formed anew in every layer (from an opaque
+    // copy of the thread index): hoisted out of the loop, they and the
+    // addresses built from them would hold registers for the whole kernel.
+    int tid_l = tid;
+    asm volatile("" : "+v"(tid_l));
+    const int tid = tid_l, lane = tid_l & 63, n16 = lane & 15, q = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid_l >> 6);
     const FusedLayer L = a.layers[l];
+    // the next layer's router, read early so that its prefetch at the end of
+    // this layer does not wait for the descriptor
+    const uint16_t* next_router = l + 1 < a.l1 ? a.layers[l + 1].router : nullptr;
     const int li = l - a.l0;
     const uint32_t tag = ep + (uint32_t)li + 1u;  // epoch of the data this layer writes
-    stamp(a, l, 0);
+    stamp(s, a, l, 0);
 
     // ---------------- E1: residual -> RMSNorm -> x in LDS ----------------
     if (li == 0) {
@@ -301,7 +320,7 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
       }
     }
     __syncthreads();
-    stamp(a, l, 1);
+    stamp(s, a, l, 1);
 
     // ---------------- router logits of this replica ----------------
     {
@@ -340,191 +359,245 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         }
       }
     }
-    stamp(a, l, 2);
+    stamp(s, a, l, 2);
 
     // ---------------- E2: logits -> LDS ----------------
     read_tagged(a.xlg + (int64_t)rep * kFMaxTE, TE, tag, bail,
                 [&](int i, uint32_t v) { s.u.sel.logit[i] = __builtin_bit_cast(float, v); });
     for (int i = tid; i < (kFMaxP + 1) * kFMaxT; i += kFT) s.pair_of[i] = -1;
     bail = block_any(bail);
-    stamp(a, l, 3);
+    stamp(s, a, l, 3);
 
     // ---------------- selection: top-k by (logit desc, id asc) ----------------
     const int nch = E >> 6;
-    if (a.forced) {
-      if (wv == 0) {
-        const int p = lane;
-        const bool valid = p < P;
-        const int t = valid ? p / k : 0;
-        const int e = valid ? a.forced[((int64_t)l * T) * k + p] : 0;
-        const bool bad = valid && (e < 0 || e >= E);
-        bool dup = false;
-        for (int qq = 0; qq < P; ++qq) {
-          const int other = __shfl(e, qq, kWave);
-          dup |= valid && qq != p && qq / k == t && other == e;
-        }
-        // a token with any bad or repeated id gets ids 0..k-1
-        const uint64_t badm = __ballot(bad || dup);
-        const uint64_t bm = __ballot(bad), dm = __ballot(dup);
-        bool tok_bad = false;
-        for (int j = 0; j < k; ++j) tok_bad |= valid && ((badm >> (t * k + j)) & 1ull);
-        if (lane == 0 && badm) errs |= (bm ? kErrBadId : 0u) | (dm ? kErrDupId : 0u);
-        if (valid) s.ids[p] = tok_bad ? (p - t * k) : e;
-      }
-    } else {
-      // rank of every expert within its chunk of 64: `wpt` waves share one
-      // (token, chunk) task, each comparing all 64 lanes against a slice of
-      // the chunk read with batched LDS broadcasts; partial ranks are summed
-      const int ntask = T * nch;
-      int wpt = 1;
-      while (wpt * 2 * ntask <= kFW) wpt *= 2;
-      const int span = kWave / wpt, sl = wv % wpt;
-      for (int t0 = 0; t0 < ntask; t0 += kFW / wpt) {
-        const int task = t0 + wv / wpt;
-        const bool on = task < ntask;
-        const int t = on ? task / nch : 0, c = on ? task - t * nch : 0;
-        const float* row = s.u.sel.logit + t * E + c * kWave;
-        const float v = row[lane];
-        int pr = 0;
-        if (on) {
-          for (int j0 = sl * span; j0 < (sl + 1) * span; j0 += 8) {
-            float vj[8];
+    if (T == 1 && nch == 1 && !a.forced) {
+      // one token, 64 experts: every wave ranks, weighs and groups by itself
+      // (bit-identical results in every wave), so the phase needs no barrier;
+      // a wave's LDS accesses complete in order, so it reads back its own writes
+      const float* lg = s.u.sel.logit;
+      const float v = lg[lane];
+      // 64-bit key ordered like (logit desc, id asc): the logit's bits mapped
+      // to an order-preserving unsigned integer, then the complemented id;
+      // rank = number of keys above this lane's (logits are never -0 or NaN)
+      const uint32_t vb = __builtin_bit_cast(uint32_t, v);
+      const uint32_t ob = (vb & 0x80000000u) ? ~vb : (vb | 0x80000000u);
+      const uint64_t key = ((uint64_t)ob << 32) | (uint32_t)(kWave - 1 - lane);
+      uint64_t* kw = s.u.sel.key[wv];
+      kw[lane] = key;
+      int r = 0;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) vj[u] = row[j0 + u];
+      for (int j0 = 0; j0 < kWave; j0 += 8) {
+        uint64_t kj[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) pr += (int)(vj[u] > v) | ((int)(vj[u] == v) & (int)(j0 + u < lane));
-          }
+        for (int u = 0; u < 8; u += 2) {
+          const uint4 two = *reinterpret_cast<const uint4*>(kw + j0 + u);
+          kj[u] = ((uint64_t)two.y << 32) | two.x;
+          kj[u + 1] = ((uint64_t)two.w << 32) | two.z;
         }
-        s.u.sel.prank[wv][lane] = pr;
-        __syncthreads();
-        if (on && sl == 0) {
-          int rank = 0;
-          for (int qq = 0; qq < wpt; ++qq) rank += s.u.sel.prank[wv + qq][lane];
-          if (rank < k) {
-            if (nch == 1) {
-              s.ids[t * k + rank] = lane;
-            } else {
-              s.u.sel.cval[t][c * k + rank] = v;
-              s.u.sel.cid[t][c * k + rank] = c * kWave + lane;
-            }
-          }
-        }
-        __syncthreads();
-      }
-      if (nch > 1) {
-        // rank among the chunks' candidates (<= 128 per token): lanes hold
-        // candidates lane and lane + 64; `wpt2` waves share a token, each
-        // comparing against a slice of the candidates
-        const int n = nch * k;
-        int wpt2 = 1;
-        while (wpt2 * 2 * T <= kFW) wpt2 *= 2;
-        const int span2 = (n + wpt2 - 1) / wpt2, sl2 = wv % wpt2;
-        for (int t0 = 0; t0 < T; t0 += kFW / wpt2) {
-          const int t = t0 + wv / wpt2;
-          const bool on = t < T;
-          const int tt = on ? t : 0;
-          const bool ha = on && lane < n, hb = on && lane + kWave < n;
-          const float va = ha ? s.u.sel.cval[tt][lane] : 0.0f;
-          const float vb = hb ? s.u.sel.cval[tt][lane + kWave] : 0.0f;
-          const int ea = ha ? s.u.sel.cid[tt][lane] : 0;
-          const int eb = hb ? s.u.sel.cid[tt][lane + kWave] : 0;
-          int ra = 0, rbk = 0;
-          if (on) {
-            const int j1 = min(n, (sl2 + 1) * span2);
-            for (int j0 = sl2 * span2; j0 < j1; j0 += 8) {
-              float vj[8];
-              int ej[8];
 #pragma unroll
-              for (int u = 0; u < 8; ++u) {
-                const bool in = j0 + u < j1;
-                vj[u] = in ? s.u.sel.cval[tt][j0 + u] : -INFINITY;
-                ej[u] = in ? s.u.sel.cid[tt][j0 + u] : 0x7fffffff;
-              }
-#pragma unroll
-              for (int u = 0; u < 8; ++u) {
-                ra += (int)(vj[u] > va) | ((int)(vj[u] == va) & (int)(ej[u] < ea));
-                rbk += (int)(vj[u] > vb) | ((int)(vj[u] == vb) & (int)(ej[u] < eb));
-              }
-            }
-          }
-          s.u.sel.prank[wv][lane] = ra;
-          s.u.sel.prank2[wv][lane] = rbk;
-          __syncthreads();
-          if (on && sl2 == 0) {
-            int rsa = 0, rsb = 0;
-            for (int qq = 0; qq < wpt2; ++qq) {
-              rsa += s.u.sel.prank[wv + qq][lane];
-              rsb += s.u.sel.prank2[wv + qq][lane];
-            }
-            if (ha && rsa < k) s.ids[t * k + rsa] = ea;
-            if (hb && rsb < k) s.ids[t * k + rsb] = eb;
-          }
-          __syncthreads();
-        }
+        for (int u = 0; u < 8; ++u) r += (int)(kj[u] > key);
       }
-    }
-    __syncthreads();
-    stamp(a, l, 10);
-    // softmax weights of the chosen experts: one wave per token; sums over the
-    // experts and the renormalisation run as fixed-order wave reductions
-    if (wv < T) {
-      const int t = wv;
-      const float* lg = s.u.sel.logit + t * E;
-      float mx;
-      if (a.forced) {
-        mx = -INFINITY;
-        for (int c = 0; c < nch; ++c) mx = fmaxf(mx, lg[c * kWave + lane]);
-        mx = wave_max(mx);
-      } else {
-        mx = lg[s.ids[t * k]];
-      }
-      float sm = 0.0f;
-      for (int c = 0; c < nch; ++c) sm += expf(lg[c * kWave + lane] - mx);
-      sm = wave_sum(sm);
-      float wj = 0.0f;
-      if (lane < k) wj = expf(lg[s.ids[t * k + lane]] - mx) / sm;
-      if (a.renorm) {
-        const float tot = wave_sum(lane < k ? wj : 0.0f);
-        wj = wj / tot;
-      }
+      if (r < k) s.ids[r] = lane;
+      const float mx = lg[s.ids[0]];
+      const float sm = wave_sum(expf(v - mx));
+      const int ej = lane < k ? s.ids[lane] : 0;
+      float wj = lane < k ? expf(lg[ej] - mx) / sm : 0.0f;
+      if (a.renorm) wj = wj / wave_sum(wj);
       if (lane < k) {
-        s.w[t * k + lane] = wj;
-        if (b == 0 && a.ids_trace) a.ids_trace[(int64_t)l * P + t * k + lane] = s.ids[t * k + lane];
-        if (b == 0 && a.w_trace) a.w_trace[(int64_t)l * P + t * k + lane] = wj;
-      }
-    }
-    __syncthreads();
-    stamp(a, l, 11);
-    // grouping: distinct experts ("units") in order of first appearance
-    if (wv == 0) {
-      const int p = lane;
-      const bool valid = p < P;
-      const int e = valid ? s.ids[p] : -1;
-      int q0 = p;  // first pair naming the same expert (ids of one token are distinct)
-      if (T > 1) {
-        for (int qq = kWave - 1; qq >= 0; --qq) {
-          const int eq = qq < P ? s.ids[qq] : -2;
-          q0 = ((qq < p) & (eq == e)) ? qq : q0;
-        }
-      }
-      const bool first = valid && q0 == p;
-      const uint64_t fm = __ballot(first);
-      const int ap = __popcll(fm & ((1ull << q0) - 1ull));
-      if (first) {
-        int slot = L.map ? ldg<int32_t>(L.map + e) : e;
+        s.w[lane] = wj;
+        if (b == 0 && wv == 0 && a.ids_trace) a.ids_trace[(int64_t)l * P + lane] = ej;
+        if (b == 0 && wv == 0 && a.w_trace) a.w_trace[(int64_t)l * P + lane] = wj;
+        // unit u = rank u; pair u
+        int slot = L.map ? ldg<int32_t>(L.map + ej) : ej;
         if (slot < 0) {
           errs |= kErrNotResident;
           slot = 0;
         }
-        s.unit_slot[ap] = slot;
+        s.unit_slot[lane] = slot;
+        s.pair_of[lane] = lane;
       }
-      if (valid) s.pair_of[ap * T + p / k] = p;
-      const int U = __popcll(fm);
-      if (a.has_shared && p < T) s.pair_of[U * T + p] = P + p;
-      if (lane == 0) s.nunits = U;
+      if (lane == 0) {
+        if (a.has_shared) s.pair_of[k] = P;
+        s.nunits = k;
+      }
+    } else {
+      if (a.forced) {
+        if (wv == 0) {
+          const int p = lane;
+          const bool valid = p < P;
+          const int t = valid ? p / k : 0;
+          const int e = valid ? a.forced[((int64_t)l * T) * k + p] : 0;
+          const bool bad = valid && (e < 0 || e >= E);
+          bool dup = false;
+#pragma unroll 1
+          for (int qq = 0; qq < P; ++qq) {
+            const int other = __shfl(e, qq, kWave);
+            dup |= valid && qq != p && qq / k == t && other == e;
+          }
+          // a token with any bad or repeated id gets ids 0..k-1
+          const uint64_t badm = __ballot(bad || dup);
+          const uint64_t bm = __ballot(bad), dm = __ballot(dup);
+          bool tok_bad = false;
+          for (int j = 0; j < k; ++j) tok_bad |= valid && ((badm >> (t * k + j)) & 1ull);
+          if (lane == 0 && badm) errs |= (bm ? kErrBadId : 0u) | (dm ? kErrDupId : 0u);
+          if (valid) s.ids[p] = tok_bad ? (p - t * k) : e;
+        }
+      } else {
+        // rank of every expert within its chunk of 64: `wpt` waves share one
+        // (token, chunk) task, each comparing all 64 lanes against a slice of
+        // the chunk read with batched LDS broadcasts; partial ranks are summed
+        const int ntask = T * nch;
+        int wpt = 1;
+        while (wpt * 2 * ntask <= kFW) wpt *= 2;
+        const int span = kWave / wpt, sl = wv % wpt;
+        for (int t0 = 0; t0 < ntask; t0 += kFW / wpt) {
+          const int task = t0 + wv / wpt;
+          const bool on = task < ntask;
+          const int t = on ? task / nch : 0, c = on ? task - t * nch : 0;
+          const float* row = s.u.sel.logit + t * E + c * kWave;
+          const float v = row[lane];
+          int pr = 0;
+          if (on) {
+            for (int j0 = sl * span; j0 < (sl + 1) * span; j0 += 8) {
+              float vj[8];
+  #pragma unroll
+              for (int u = 0; u < 8; ++u) vj[u] = row[j0 + u];
+  #pragma unroll
+              for (int u = 0; u < 8; ++u) pr += (int)(vj[u] > v) | ((int)(vj[u] == v) & (int)(j0 + u < lane));
+            }
+          }
+          s.u.sel.prank[wv][lane] = pr;
+          __syncthreads();
+          if (on && sl == 0) {
+            int rank = 0;
+            for (int qq = 0; qq < wpt; ++qq) rank += s.u.sel.prank[wv + qq][lane];
+            if (rank < k) {
+              if (nch == 1) {
+                s.ids[t * k + rank] = lane;
+              } else {
+                s.u.sel.cval[t][c * k + rank] = v;
+                s.u.sel.cid[t][c * k + rank] = c * kWave + lane;
+              }
+            }
+          }
+          __syncthreads();
+        }
+        if (nch > 1) {
+          // rank among the chunks' candidates (<= 128 per token): lanes hold
+          // candidates lane and lane + 64; `wpt2` waves share a token, each
+          // comparing against a slice of the candidates
+          const int n = nch * k;
+          int wpt2 = 1;
+          while (wpt2 * 2 * T <= kFW) wpt2 *= 2;
+          const int span2 = (n + wpt2 - 1) / wpt2, sl2 = wv % wpt2;
+          for (int t0 = 0; t0 < T; t0 += kFW / wpt2) {
+            const int t = t0 + wv / wpt2;
+            const bool on = t < T;
+            const int tt = on ? t : 0;
+            const bool ha = on && lane < n, hb = on && lane + kWave < n;
+            const float va = ha ? s.u.sel.cval[tt][lane] : 0.0f;
+            const float vb = hb ? s.u.sel.cval[tt][lane + kWave] : 0.0f;
+            const int ea = ha ? s.u.sel.cid[tt][lane] : 0;
+            const int eb = hb ? s.u.sel.cid[tt][lane + kWave] : 0;
+            int ra = 0, rbk = 0;
+            if (on) {
+              const int j1 = min(n, (sl2 + 1) * span2);
+              for (int j0 = sl2 * span2; j0 < j1; j0 += 8) {
+                float vj[8];
+                int ej[8];
+  #pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                  const bool in = j0 + u < j1;
+                  vj[u] = in ? s.u.sel.cval[tt][j0 + u] : -INFINITY;
+                  ej[u] = in ? s.u.sel.cid[tt][j0 + u] : 0x7fffffff;
+                }
+  #pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                  ra += (int)(vj[u] > va) | ((int)(vj[u] == va) & (int)(ej[u] < ea));
+                  rbk += (int)(vj[u] > vb) | ((int)(vj[u] == vb) & (int)(ej[u] < eb));
+                }
+              }
+            }
+            s.u.sel.prank[wv][lane] = ra;
+            s.u.sel.prank2[wv][lane] = rbk;
+            __syncthreads();
+            if (on && sl2 == 0) {
+              int rsa = 0, rsb = 0;
+              for (int qq = 0; qq < wpt2; ++qq) {
+                rsa += s.u.sel.prank[wv + qq][lane];
+                rsb += s.u.sel.prank2[wv + qq][lane];
+              }
+              if (ha && rsa < k) s.ids[t * k + rsa] = ea;
+              if (hb && rsb < k) s.ids[t * k + rsb] = eb;
+            }
+            __syncthreads();
+          }
+        }
+      }
+      __syncthreads();
+      stamp(s, a, l, 10);
+      // softmax weights of the chosen experts: one wave per token; sums over the
+      // experts and the renormalisation run as fixed-order wave reductions
+      if (wv < T) {
+        const int t = wv;
+        const float* lg = s.u.sel.logit + t * E;
+        float mx;
+        if (a.forced) {
+          mx = -INFINITY;
+          for (int c = 0; c < nch; ++c) mx = fmaxf(mx, lg[c * kWave + lane]);
+          mx = wave_max(mx);
+        } else {
+          mx = lg[s.ids[t * k]];
+        }
+        float sm = 0.0f;
+        for (int c = 0; c < nch; ++c) sm += expf(lg[c * kWave + lane] - mx);
+        sm = wave_sum(sm);
+        float wj = 0.0f;
+        if (lane < k) wj = expf(lg[s.ids[t * k + lane]] - mx) / sm;
+        if (a.renorm) {
+          const float tot = wave_sum(lane < k ? wj : 0.0f);
+          wj = wj / tot;
+        }
+        if (lane < k) {
+          s.w[t * k + lane] = wj;
+          if (b == 0 && a.ids_trace) a.ids_trace[(int64_t)l * P + t * k + lane] = s.ids[t * k + lane];
+          if (b == 0 && a.w_trace) a.w_trace[(int64_t)l * P + t * k + lane] = wj;
+        }
+      }
+      __syncthreads();
+      stamp(s, a, l, 11);
+      // grouping: distinct experts ("units") in order of first appearance
+      if (wv == 0) {
+        const int p = lane;
+        const bool valid = p < P;
+        const int e = valid ? s.ids[p] : -1;
+        int q0 = p;  // first pair naming the same expert (ids of one token are distinct)
+        if (T > 1) {
+#pragma unroll 1
+          for (int qq = kWave - 1; qq >= 0; --qq) {
+            const int eq = qq < P ? s.ids[qq] : -2;
+            q0 = ((qq < p) & (eq == e)) ? qq : q0;
+          }
+        }
+        const bool first = valid && q0 == p;
+        const uint64_t fm = __ballot(first);
+        const int ap = __popcll(fm & ((1ull << q0) - 1ull));
+        if (first) {
+          int slot = L.map ? ldg<int32_t>(L.map + e) : e;
+          if (slot < 0) {
+            errs |= kErrNotResident;
+            slot = 0;
+          }
+          s.unit_slot[ap] = slot;
+        }
+        if (valid) s.pair_of[ap * T + p / k] = p;
+        const int U = __popcll(fm);
+        if (a.has_shared && p < T) s.pair_of[U * T + p] = P + p;
+        if (lane == 0) s.nunits = U;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    stamp(a, l, 4);
+    stamp(s, a, l, 4);
 
     // ---------------- weights: first gate/up task and first down task ----------------
     const int U = s.nunits;
@@ -580,16 +653,18 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
     };
     const int gu_task0 = b * kFW + wv;
     const DPtr d0 = d_ptrs(wv < ntask_d ? wv : 0);
-    // gate/up loads first (consumed first), then the down weights' direct loads
+    // the gate/up loads are issued now; the down weights' direct loads only
+    // once the wave's gate/up weights have arrived, so that the whole chip's
+    // gate/up weights lead the burst (the down weights are needed only after
+    // the intermediates have been exchanged)
     if (gu_task0 < ntask_gu) load_gu(gu_task0);
-    if (wv < ntask_d) load_d(d0);
-    stamp(a, l, 5);
+    stamp(s, a, l, 5);
 
     // ---------------- gate/up + SwiGLU -> E3 publication ----------------
     // one round: MFMA over the wave's K half, LDS sum of the halves, SwiGLU,
     // publication.  Round 0 runs outside the loop so that its loads are
     // waited for one group at a time.
-    auto gu_round = [&](int task) __attribute__((always_inline)) {
+    auto gu_round = [&](int task, bool first) __attribute__((always_inline)) {
       const bool on = task < ntask_gu;
       if (on) {
         const int half = task & 1;
@@ -598,12 +673,14 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         for (int g2 = 0; g2 < GH; ++g2) {
           f4 ag = {0.f, 0.f, 0.f, 0.f};
           const int kb = half * (H / 2) + g2 * 128 + 32 * q;
+          // padding rows (n16 >= T) read 32 zeros; all four reads issue together
+          const _Float16* ap = n16 < T ? s.x + n16 * H + kb : s.xz;
+          h8 av[4];
 #pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            h8 av = {};
-            if (n16 < T) av = *reinterpret_cast<const h8*>(s.x + n16 * H + kb + 8 * st);
-            ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, decode_h8(dword_of(gq[g2], st)), ag, 0, 0, 0);
-          }
+          for (int st = 0; st < 4; ++st) av[st] = *reinterpret_cast<const h8*>(ap + 8 * st);
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+            ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[st], decode_h8(dword_of(gq[g2], st)), ag, 0, 0, 0);
           acc += ag * half_bits_to_float(gs[g2]);
           // decode one group at a time: keeps the decoded operands of later
           // groups from being hoisted (and held in registers) early
@@ -613,9 +690,10 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         for (int rr = 0; rr < 4; ++rr)
           if (4 * q + rr < T) s.red[wv][4 * q + rr][n16] = acc[rr];
       }
-      stamp(a, l, 13);
+      if (first && wv < ntask_d) load_d(d0);
+      stamp(s, a, l, 13);
       __syncthreads();
-      stamp(a, l, 14);
+      stamp(s, a, l, 14);
       if (on && (wv & 1) == 0) {
         // sum the two K halves (sibling waves), SwiGLU, publish FP16 pairs
         const int m = lane >> 3, n = lane & 7;
@@ -636,21 +714,51 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         }
       }
     };
-    gu_round(gu_task0);
+    gu_round(gu_task0, true);
     for (int r = 1; r < nround_gu; ++r) {
       const int task = gu_task0 + r * kFGrid * kFW;
       __syncthreads();  // red is reused
       if (task < ntask_gu) load_gu(task);
-      gu_round(task);
+      gu_round(task, false);
     }
-    stamp(a, l, 6);
+    stamp(s, a, l, 6);
+
+    // ---------------- down weights of the first down task -> registers ----------------
+    // When the wave has a single down task, its direct loads are waited for
+    // and the INT4 codes of its first kPre scale groups decoded (with their
+    // scales) before the intermediates are exchanged: the exchange is a wait,
+    // and after it less work remains for the down projection.
+    constexpr int kPre = 4;
+    const bool pre = nround_d == 1 && wv < ntask_d;
+    h8 bd[kPre][4];
+    float bsc[kPre];
+    if (pre) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int g2 = 0; g2 < kPre; ++g2) {
+        if (g2 < ngd) {
+          const uint4 dq = s.dpre[wv][g2][lane];
+#pragma unroll
+          for (int st = 0; st < 4; ++st) bd[g2][st] = decode_h8(dword_of(dq, st));
+          const uint32_t sw = s.dsc[wv][n16 + 16 * (g2 >> 1)];
+          bsc[g2] = half_bits_to_float((uint16_t)(sw >> (16 * (g2 & 1))));
+        } else {
+#pragma unroll
+          for (int st = 0; st < 4; ++st) bd[g2][st] = h8{};
+          bsc[g2] = 0.0f;
+        }
+        // keep the decoded operands here, ahead of the exchange
+#pragma unroll
+        for (int st = 0; st < 4; ++st) asm volatile("" : "+v"(bd[g2][st]));
+      }
+    }
 
     // ---------------- E3: intermediates of every pair -> LDS ----------------
     const int npairs = P + (a.has_shared ? T : 0);
     read_tagged(a.xhb, npairs * (I / 2), tag, bail,
                 [&](int i, uint32_t v) { reinterpret_cast<uint32_t*>(s.u.hst)[i] = v; });
     bail = block_any(bail);
-    stamp(a, l, 7);
+    stamp(s, a, l, 7);
 
     // ---------------- down projection of the block's 8 rows ----------------
     for (int r = 0; r < nround_d; ++r) {
@@ -658,8 +766,8 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
       const bool on = task < ntask_d;
       if (r > 0 && on) load_d(d_ptrs(task));
       // this wave's direct loads into its LDS region have landed
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (r == 0) stamp(a, l, 12);
+      if (!pre) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (r == 0) stamp(s, a, l, 12);
       if (on) {
         const int cg = task / ks, kp = task - cg * ks;
         // A row m: unit cg*2 + m/T, token m%T
@@ -674,14 +782,22 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
             f4 ag = {0.f, 0.f, 0.f, 0.f};
             const int kb = kp * (I / ks) + g2 * 128 + 32 * q;
             const uint4 dq = s.dpre[wv][g2][lane];
+            const _Float16* ap = pa >= 0 ? hrow + kb : s.xz;
+            h8 av[4];
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-              h8 av = {};
-              if (pa >= 0) av = *reinterpret_cast<const h8*>(hrow + kb + 8 * st);
-              ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, decode_h8(dword_of(dq, st)), ag, 0, 0, 0);
+            for (int st = 0; st < 4; ++st) av[st] = *reinterpret_cast<const h8*>(ap + 8 * st);
+            if (g2 < kPre && pre) {
+#pragma unroll
+              for (int st = 0; st < 4; ++st)
+                ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[st], bd[g2 < kPre ? g2 : 0][st], ag, 0, 0, 0);
+              acc += ag * bsc[g2 < kPre ? g2 : 0];
+            } else {
+#pragma unroll
+              for (int st = 0; st < 4; ++st)
+                ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[st], decode_h8(dword_of(dq, st)), ag, 0, 0, 0);
+              const uint32_t sw = s.dsc[wv][n16 + 16 * (g2 >> 1)];
+              acc += ag * half_bits_to_float((uint16_t)(sw >> (16 * (g2 & 1))));
             }
-            const uint32_t sw = s.dsc[wv][n16 + 16 * (g2 >> 1)];
-            acc += ag * half_bits_to_float((uint16_t)(sw >> (16 * (g2 & 1))));
           }
         }
         // D[m][n]: row m = (unit m/T, token m%T), column n = (unit n/8, row n%8)
@@ -701,10 +817,10 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
     }
     // the next layer's router part of this wave's first item streams in
     // during the combine and the residual exchange
-    if (l + 1 < a.l1 && item0 < TE)
-      load_router_part<H>(a.layers[l + 1].router + (int64_t)(item0 % E) * H + lpoff, nchunk, lane, rq);
+    if (next_router && item0 < TE)
+      load_router_part<H>(next_router + (int64_t)(item0 % E) * H + lpoff, nchunk, lane, rq);
     __syncthreads();
-    stamp(a, l, 8);
+    stamp(s, a, l, 8);
 
     // ---------------- rank-ordered combine, residual update, E1 publication ----------------
     const bool last = l + 1 == a.l1;
@@ -717,10 +833,18 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
     if (tid < T * kFRows) {
       const int t = tid / kFRows, row = tid - t * kFRows;
       float o = 0.0f;
-      for (int j = 0; j < k; ++j) {
-        const int p = t * k + j;
-        const float y = ks == 2 ? s.ypart[0][p][row] + s.ypart[1][p][row] : s.ypart[0][p][row];
-        o += s.w[p] * y;
+      // rank order; the LDS reads of four ranks are issued together
+      for (int j0 = 0; j0 < k; j0 += 4) {
+        float y[4], wq[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int p = t * k + min(j0 + u, k - 1);
+          y[u] = ks == 2 ? s.ypart[0][p][row] + s.ypart[1][p][row] : s.ypart[0][p][row];
+          wq[u] = s.w[p];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (j0 + u < k) o += wq[u] * y[u];
       }
       if (a.has_shared) {
         const int p = P + t;
@@ -732,7 +856,14 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
       else
         st_tag(a.xh + (int64_t)((li + 1) & 1) * kFMaxT * H + t * H + r0 + row, tag, __builtin_bit_cast(uint32_t, hn));
     }
-    stamp(a, l, 9);
+    stamp(s, a, l, 9);
+  }
+  if (a.stamps && tid == 0) {
+    const int n = min(a.l1 - a.l0, kStampLayers) * kStampsPerLayer;
+    for (int i = 0; i < n; ++i) {
+      a.stamps[(int64_t)b * kStampStride + i] = s.stampbuf[0][i];
+      a.stamps[(int64_t)(kFGrid + b) * kStampStride + i] = s.stampbuf[1][i];
+    }
   }
   if (bail) errs |= kErrBarrier;
   if (tid == 0) __hip_atomic_store(&a.epoch[b], ep + (uint32_t)(a.l1 - a.l0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

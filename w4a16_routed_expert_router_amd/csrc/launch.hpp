@@ -104,7 +104,8 @@ constexpr int kFGrid = 256;    // blocks: one per compute unit
 constexpr int kFRows = 8;      // residual rows per block (H / kFGrid)
 constexpr int kFLogitReps = 8; // logit replicas (one per XCD) for small steps
 constexpr int kStampsPerLayer = 16;   // phase timestamps per layer (instrumentation)
-constexpr int kStampStride = 64 * kStampsPerLayer;  // per block, up to 64 layers
+constexpr int kStampLayers = 16;      // layers of a call that are stamped
+constexpr int kStampStride = kStampLayers * kStampsPerLayer;  // per block
 struct FusedLayer {
   const uint16_t* router;
   const uint8_t* store;
