@@ -228,10 +228,14 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   // shapes allow it (then every expert with up to kStreamTokens tokens), else
   // the GEMV kernels
   const bool force_gemv = (g.flags & MOE_FLAG_FORCE_GEMV) != 0;
+  // with at least kStreamTokens pairs per expert on average (prefill) every
+  // expert runs on the grouped GEMM and the few-token kernels are not launched
+  const bool all_mfma = !force_gemv && ((g.flags & MOE_FLAG_FORCE_MFMA) ||
+                                        (int64_t)T * g.top_k >= (int64_t)kStreamTokens * g.n_experts);
   const bool stream_gu = !force_gemv && stream_supported(0, g.hidden, g.inter);
   const bool stream_dn = !force_gemv && stream_supported(1, g.inter, g.hidden);
   const int mfma_min = force_gemv ? INT32_MAX
-                       : (g.flags & MOE_FLAG_FORCE_MFMA) ? 1
+                       : all_mfma ? 1
                        : (stream_gu ? kStreamTokens + 1 : kMfmaMinTokens);
   GroupArgs ga{ids, T, g.top_k, g.n_experts, L.map, c->ids_s, c->active, c->n_active,
                c->perm_tok, c->pos_of, c->err, mfma_min, c->mtile_off};
@@ -256,7 +260,7 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   ea.perm_tok = c->perm_tok;
   ea.hbuf = c->hbuf;
   ea.ybuf = c->ybuf;
-  {
+  if (!all_mfma) {
     ScopedTimer tm(c, kKindGateUp, s);
     if (stream_gu) launch_stream_expert(ea, 0, c->ncu, s);
     else launch_gateup_gemv(ea, s);
@@ -265,7 +269,7 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
     ScopedTimer tm(c, kKindMfmaGateUp, s);
     launch_mfma_gateup(ma, mfma_max_tiles(T, g.top_k, g.n_experts, g.inter, 0), s);
   }
-  {
+  if (!all_mfma) {
     ScopedTimer tm(c, kKindDown, s);
     if (stream_dn && stream_gu) launch_stream_expert(ea, 1, c->ncu, s);
     else launch_down_gemv(ea, s);

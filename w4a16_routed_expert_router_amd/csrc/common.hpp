@@ -184,6 +184,17 @@ __device__ __forceinline__ float wave_max(float x) {
   return bcast63(x);
 }
 
+// Inclusive prefix sum over the lanes of a wave, on the same DPP network.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += (int)dpp32<0x111, 0xf>((uint32_t)x, 0u);
+  x += (int)dpp32<0x112, 0xf>((uint32_t)x, 0u);
+  x += (int)dpp32<0x114, 0xf>((uint32_t)x, 0u);
+  x += (int)dpp32<0x118, 0xf>((uint32_t)x, 0u);
+  x += (int)dpp32<0x142, 0xa>((uint32_t)x, 0u);
+  x += (int)dpp32<0x143, 0xc>((uint32_t)x, 0u);
+  return x;
+}
+
 __device__ __forceinline__ void atomic_or_err(uint32_t* err, uint32_t bits) {
   if (err) atomicOr(err, bits);
 }

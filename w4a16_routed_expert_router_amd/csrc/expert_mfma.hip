@@ -49,7 +49,7 @@ constexpr int kXcd = 8;                 // XCDs; blocks go round-robin over them
 // 8 INT4 codes (one dword) -> 8 FP16 weights (q - 8) * scale.
 __device__ __forceinline__ h8 decode_scaled(uint32_t d, h2 s2) {
   h2 p[4];
-  dequant8(d, p);
+  dequant8_v(d, p, 0x000F000Fu, 0x00F000F0u);
   p[0] *= s2; p[1] *= s2; p[2] *= s2; p[3] *= s2;
   h8 r;
   r[0] = p[0][0]; r[1] = p[0][1]; r[2] = p[1][0]; r[3] = p[1][1];
@@ -58,8 +58,9 @@ __device__ __forceinline__ h8 decode_scaled(uint32_t d, h2 s2) {
 }
 
 
+// (16-byte alignment lets the 16-byte operand reads be single instructions)
 struct MfmaSmem {
-  _Float16 a[2][kMT + 1][kKC + kAPad];   // row kMT takes the stores of padding rows
+  alignas(16) _Float16 a[2][kMT + 1][kKC + kAPad];   // row kMT takes the stores of padding rows
   int tok[kMT];
 };
 
@@ -69,7 +70,7 @@ struct MfmaSmem {
 constexpr int kFullRing = 8;
 constexpr int kAFullHalves = 64 * (1024 + kAPad);  // >= MS*16 x (K + pad) for MS*K <= 4096
 struct MfmaSmemFull {
-  _Float16 a[kAFullHalves];
+  alignas(16) _Float16 a[kAFullHalves];
   int tok[kMT];
 };
 union MfmaShared {
@@ -148,35 +149,40 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, MfmaSmem& s, const 
       ds[j] = scales[j][g];
     }
   };
-  u4 av[NA];
-  auto load_a = [&](int g) __attribute__((always_inline)) {
+  // activation chunks of two groups in flight: group g + 1 is staged into
+  // LDS during step g, group g + 2 is being loaded
+  u4 av[2][NA];
+  auto load_a = [&](int g, u4 (&dst)[NA]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i) av[i] = *reinterpret_cast<const u4*>(abase[i] + g * kKC);
+    for (int i = 0; i < NA; ++i) dst[i] = *reinterpret_cast<const u4*>(abase[i] + g * kKC);
   };
-  auto store_a = [&](int buf) __attribute__((always_inline)) {
+  auto store_a = [&](int buf, const u4 (&src)[NA]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i) *reinterpret_cast<u4*>(&s.a[buf][arow[i]][acol[i]]) = av[i];
+    for (int i = 0; i < NA; ++i) *reinterpret_cast<u4*>(&s.a[buf][arow[i]][acol[i]]) = src[i];
   };
 
   f4 acc[MS][2];
 #pragma unroll
   for (int mi = 0; mi < MS; ++mi) acc[mi][0] = acc[mi][1] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: groups 0..kRing-2 of weights in flight, group 0 of activations in LDS
+  // prologue: groups 0..kRing-2 of weights in flight, group 0 of activations
+  // in LDS, group 1 in flight
+  load_a(0, av[0]);
+  load_a(min(1, ng - 1), av[1]);
 #pragma unroll
   for (int u = 0; u < kRing - 1; ++u) load_b(min(u, ng - 1), bq[u], bs[u]);
-  load_a(0);
-  store_a(0);
+  store_a(0, av[0]);
   __syncthreads();
 
   // one K group: prefetch, decode + MFMA, stage the next activations
   auto step = [&](int g, auto uc) __attribute__((always_inline)) {
     constexpr int U = decltype(uc)::value;
-    // activations first, then weights: the wait for the activations before
-    // they are staged then leaves the weight loads in flight (loads complete
-    // in issue order).  The scheduling barriers keep this order and keep the
-    // loads at the top instead of next to their first use.
-    load_a(min(g + 1, ng - 1));
+    // activations first, then weights: the wait for the activations staged
+    // at the end of the step (loaded one step earlier) then leaves this
+    // step's loads in flight (loads complete in issue order).  The
+    // scheduling barriers keep this order and keep the loads at the top
+    // instead of next to their first use.
+    load_a(min(g + 2, ng - 1), av[U & 1]);
     __builtin_amdgcn_sched_barrier(0);
     load_b(min(g + kRing - 1, ng - 1), bq[(U + kRing - 1) % kRing], bs[(U + kRing - 1) % kRing]);
     __builtin_amdgcn_sched_barrier(0);
@@ -198,7 +204,7 @@ __device__ __forceinline__ void mfma_tile(const MfmaArgs& a, MfmaSmem& s, const 
         acc[mi][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b1, acc[mi][1], 0, 0, 0);
       }
     }
-    store_a((g + 1) & 1);
+    store_a((g + 1) & 1, av[(U + 1) & 1]);
     __syncthreads();
   };
   using C0 = std::integral_constant<int, 0>;

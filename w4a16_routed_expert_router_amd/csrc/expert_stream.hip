@@ -54,7 +54,7 @@ __device__ __forceinline__ h8 decode_unscaled(uint32_t d, uint32_t mlo, uint32_t
 
 template <int K>
 struct StreamSmem {
-  _Float16 a[kTok * (K + kPad)];  // activation tile of the current expert
+  alignas(16) _Float16 a[kTok * (K + kPad)];  // activation tile of the current expert
   int slot[kMaxList];             // small experts of the call: blob slot, count, offset
   int count[kMaxList];
   int offset[kMaxList];

@@ -14,111 +14,182 @@ namespace moe {
 constexpr int kGroupThreads = 1024;
 constexpr int kMaxExperts = 1024;
 constexpr int kChunk = 64;  // tokens per stable-placement round
+constexpr int kLdsPairs = 16384;  // validated ids are kept in LDS up to this many pairs
+constexpr int kMaxK = 16;         // largest top-k a context accepts
+constexpr int kRounds = 4;        // placement chunks per round at most
 
-__device__ int block_exclusive_scan(int v, int* sh_warp, int* total) {
-  // 1024 threads = 16 waves
+// Exclusive prefix sums of N values per thread over the block (1024 threads =
+// 16 waves) and their block totals; three barriers for all N.
+template <int N>
+__device__ void block_exclusive_scan(const int (&v)[N], int (&excl)[N], int (&total)[N], int (*sh_warp)[16],
+                                     int* sh_tot) {
+  constexpr int NW = kGroupThreads / 64;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  int incl = v;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += n;
+  int incl[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    incl[i] = wave_incl_scan(v[i]);
+    if (lane == 63) sh_warp[i][wid] = incl[i];
   }
-  if (lane == 63) sh_warp[wid] = incl;
   __syncthreads();
   if (wid == 0) {
-    int s = (lane < kGroupThreads / 64) ? sh_warp[lane] : 0;
-    int si = s;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int n = __shfl_up(si, o, 64);
-      if (lane >= o) si += n;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int s = lane < NW ? sh_warp[i][lane] : 0;
+      const int si = wave_incl_scan(s);
+      if (lane < NW) sh_warp[i][lane] = si - s;
+      if (lane == NW - 1) sh_tot[i] = si;
     }
-    if (lane < kGroupThreads / 64) sh_warp[lane] = si - s;
-    if (lane == kGroupThreads / 64 - 1) *total = si;
   }
   __syncthreads();
-  const int r = sh_warp[wid] + incl - v;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    excl[i] = sh_warp[i][wid] + incl[i] - v[i];
+    total[i] = sh_tot[i];
+  }
   __syncthreads();
-  return r;
 }
 
 // One block of 1024 threads.
 __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int base[kMaxExperts];
-  __shared__ unsigned long long mask[kMaxExperts];
-  __shared__ int sh_warp[16];
-  __shared__ int sh_total;
+  __shared__ unsigned long long mask[kRounds][kMaxExperts];
+  __shared__ int sh_warp[3][16];
+  __shared__ int sh_tot[3];
+  __shared__ int16_t sid[kLdsPairs];    // ids by pair (validated in place)
+  __shared__ int16_t sperm[kLdsPairs];  // token at each sorted position
+  __shared__ int16_t spos[kLdsPairs];   // sorted position of each pair
   const int tid = threadIdx.x;
   const int T = a.T, k = a.k, E = a.E;
   const int P = T * k;
+  // Ids, positions and the permutation live in LDS when they fit (else in
+  // their global buffers), and every global store is issued at the end: a
+  // barrier waits for the block's outstanding stores, so stores issued
+  // between the placement rounds would stall each round.
+  const bool lds_ids = P <= kLdsPairs;
+  auto get_id = [&](int p) -> int { return lds_ids ? (int)sid[p] : a.ids_s[p]; };
 
   for (int e = tid; e < E; e += kGroupThreads) cnt[e] = 0;
+  // the caller's ids, read coalesced (out-of-range values are clamped into
+  // int16 so that they stay out of range)
+  if (lds_ids) {
+    for (int p = tid; p < P; p += kGroupThreads) {
+      const int v = a.ids_in[p];
+      sid[p] = (int16_t)(v < 0 || v >= E ? -1 : v);
+    }
+    __syncthreads();
+  }
   // validate each token's ids; a bad token gets ids 0..k-1 (valid, distinct)
   uint32_t errbits = 0;
   for (int t = tid; t < T; t += kGroupThreads) {
-    const int32_t* row = a.ids_in + (int64_t)t * k;
+    int rv[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      rv[j] = j < k ? (lds_ids ? (int)sid[t * k + j] : a.ids_in[(int64_t)t * k + j]) : -1;
     bool bad = false, dup = false;
-    for (int j = 0; j < k; ++j) {
-      const int e = row[j];
-      if (e < 0 || e >= E) bad = true;
-      for (int jj = 0; jj < j; ++jj)
-        if (row[jj] == e) dup = true;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k) {
+        bad |= rv[j] < 0 || rv[j] >= E;
+#pragma unroll
+        for (int jj = 0; jj < j; ++jj) dup |= rv[jj] == rv[j];
+      }
     }
     if (bad) errbits |= kErrBadId;
     if (dup) errbits |= kErrDupId;
-    for (int j = 0; j < k; ++j) a.ids_s[(int64_t)t * k + j] = (bad || dup) ? j : row[j];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k) break;
+      const int v = (bad || dup) ? j : rv[j];
+      if (lds_ids)
+        sid[t * k + j] = (int16_t)v;
+      else
+        a.ids_s[(int64_t)t * k + j] = v;
+    }
   }
   if (errbits) atomic_or_err(a.err, errbits);
   __syncthreads();
-  for (int p = tid; p < P; p += kGroupThreads) atomicAdd(&cnt[a.ids_s[p]], 1);
+  for (int p = tid; p < P; p += kGroupThreads) atomicAdd(&cnt[get_id(p)], 1);
   __syncthreads();
 
   // offsets and the active list (ascending expert id); E <= 1024 = one per thread
   const int c = (tid < E) ? cnt[tid] : 0;
-  const int off = block_exclusive_scan(c, sh_warp, &sh_total);
   const int mtiles = c >= a.mfma_min ? (c + kMfmaTileTokens - 1) / kMfmaTileTokens : 0;
-  const int moff = block_exclusive_scan(mtiles, sh_warp, &sh_total);
-  const int mtotal = sh_total;
-  const int act = block_exclusive_scan(c > 0 ? 1 : 0, sh_warp, &sh_total);
-  if (c > 0) a.mtile_off[act] = moff;
-  if (tid == 0) a.mtile_off[sh_total] = mtotal;
+  const int sv[3] = {c, mtiles, c > 0 ? 1 : 0};
+  int sx[3], st[3];
+  block_exclusive_scan<3>(sv, sx, st, sh_warp, sh_tot);
+  const int off = sx[0], moff = sx[1], mtotal = st[1], act = sx[2], nact = st[2];
+  int slot = 0;
   if (tid < E) {
     base[tid] = off;
     if (c > 0) {
-      int slot = a.slot_map ? a.slot_map[tid] : tid;
+      slot = a.slot_map ? a.slot_map[tid] : tid;
       if (slot < 0) {
         atomic_or_err(a.err, kErrNotResident);
         slot = 0;
       }
-      a.active[act] = ActiveExpert{tid, slot, c, off};
     }
   }
-  if (tid == 0) *a.n_active = sh_total;
+  for (int i = tid; i < kRounds * kMaxExperts; i += kGroupThreads) (&mask[0][0])[i] = 0ull;
   __syncthreads();
 
-  // stable placement: within an expert, positions follow token order
-  for (int t0 = 0; t0 < T; t0 += kChunk) {
-    for (int e = tid; e < E; e += kGroupThreads) mask[e] = 0ull;
-    __syncthreads();
-    const int nt = min(kChunk, T - t0);
-    const int np = nt * k;
-    int e = -1, tl = 0, p = 0;
+  // stable placement: within an expert, positions follow token order.  One
+  // round places R consecutive chunks of 64 tokens (R * 64 * k <= 1024 pairs):
+  // a pair's position is its expert's base, plus the expert's pairs in the
+  // round's earlier chunks, plus its earlier tokens within its own chunk.
+  const int R = max(1, min(kRounds, kGroupThreads / (kChunk * k)));
+  for (int t0 = 0; t0 < T; t0 += R * kChunk) {
+    const int np = min(R * kChunk, T - t0) * k;
+    int e = -1, tl = 0, ci = 0, p = 0;
     if (tid < np) {
       p = t0 * k + tid;
-      tl = tid / k;
-      e = a.ids_s[p];
-      atomicOr(&mask[e], 1ull << tl);
+      const int tr = tid / k;  // token within the round
+      ci = tr / kChunk;
+      tl = tr - ci * kChunk;
+      e = get_id(p);
+      atomicOr(&mask[ci][e], 1ull << tl);
     }
     __syncthreads();
     if (e >= 0) {
-      const int pos = base[e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
-      a.perm_tok[pos] = t0 + tl;
-      a.pos_of[p] = pos;
+      int pos = base[e] + __popcll(mask[ci][e] & ((1ull << tl) - 1ull));
+      for (int cc = 0; cc < ci; ++cc) pos += __popcll(mask[cc][e]);
+      const int t = t0 + ci * kChunk + tl;
+      if (lds_ids) {
+        sperm[pos] = (int16_t)t;
+        spos[p] = (int16_t)pos;
+      } else {
+        a.perm_tok[pos] = t;
+        a.pos_of[p] = pos;
+      }
     }
     __syncthreads();
-    for (int ee = tid; ee < E; ee += kGroupThreads) base[ee] += __popcll(mask[ee]);
+    for (int ee = tid; ee < E; ee += kGroupThreads) {
+      int add = 0;
+      for (int cc = 0; cc < R; ++cc) {
+        add += __popcll(mask[cc][ee]);
+        mask[cc][ee] = 0ull;
+      }
+      base[ee] += add;
+    }
     __syncthreads();
+  }
+
+  // global results
+  if (lds_ids) {
+    for (int p = tid; p < P; p += kGroupThreads) {
+      a.perm_tok[p] = sperm[p];
+      a.pos_of[p] = spos[p];
+    }
+  }
+  if (c > 0) {
+    a.mtile_off[act] = moff;
+    a.active[act] = ActiveExpert{tid, slot, c, off};
+  }
+  if (tid == 0) {
+    a.mtile_off[nact] = mtotal;
+    *a.n_active = nact;
   }
 }
 
