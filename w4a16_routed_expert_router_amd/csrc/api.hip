@@ -238,7 +238,8 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
                        : all_mfma ? 1
                        : (stream_gu ? kStreamTokens + 1 : kMfmaMinTokens);
   GroupArgs ga{ids, T, g.top_k, g.n_experts, L.map, c->ids_s, c->active, c->n_active,
-               c->perm_tok, c->pos_of, c->err, mfma_min, c->mtile_off};
+               c->perm_tok, c->pos_of, c->err, mfma_min, c->mtile_off,
+               c->active + g.n_experts, c->n_active + 1};
   {
     ScopedTimer tm(c, kKindGroup, s);
     launch_group(ga, s);
@@ -253,6 +254,8 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   ea.lay = c->lay;
   ea.active = c->active;
   ea.n_active = c->n_active;
+  ea.small = c->active + g.n_experts;
+  ea.n_small = c->n_active + 1;
   ea.max_active = max_active(c, T);
   ea.H = g.hidden;
   ea.I = g.inter;
@@ -377,8 +380,9 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ok = ok && dalloc((void**)&c->ids, (size_t)P * 4);
   ok = ok && dalloc((void**)&c->w, (size_t)P * 4);
   ok = ok && dalloc((void**)&c->ids_s, (size_t)P * 4);
-  ok = ok && dalloc((void**)&c->active, (size_t)g.n_experts * sizeof(ActiveExpert));
-  ok = ok && dalloc((void**)&c->n_active, 4);
+  // active list, then the list of the experts the few-token kernel takes
+  ok = ok && dalloc((void**)&c->active, (size_t)2 * g.n_experts * sizeof(ActiveExpert));
+  ok = ok && dalloc((void**)&c->n_active, 2 * 4);
   ok = ok && dalloc((void**)&c->perm_tok, (size_t)P * 4);
   ok = ok && dalloc((void**)&c->pos_of, (size_t)P * 4);
   ok = ok && dalloc((void**)&c->mtile_off, (size_t)(g.n_experts + 1) * 4);

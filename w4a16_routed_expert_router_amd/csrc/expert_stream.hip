@@ -79,51 +79,29 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   const int N = MODE == 0 ? a.I : a.H;
   const int ntn = N / ROWS;
 
-  // ---- the call's experts with at most 16 tokens (and below the MFMA threshold)
-  if (a.fixed_blob) {
-    if (tid == 0) {
-      s.slot[0] = 0;
-      s.count[0] = a.fixed_count;
-      s.offset[0] = a.fixed_offset;
-      s.ns = 1;
-    }
-  } else {
-    const int na = *a.n_active;
-    int base = 0;
-    for (int c0 = 0; c0 < na; c0 += kSW * kWave) {  // uniform
-      const int ai = c0 + tid;
-      ActiveExpert ae{0, 0, 0, 0};
-      bool take = false;
-      if (ai < na) {
-        ae = a.active[ai];
-        take = ae.count > 0 && ae.count <= kTok && ae.count < a.mfma_min;
-      }
-      const uint64_t m = __ballot(take);
-      const int before = __popcll(m & ((1ull << lane) - 1ull));
-      if (lane == 0) s.scan[wv] = __popcll(m);
-      __syncthreads();
-      int wbase = base;
-      for (int w = 0; w < wv; ++w) wbase += s.scan[w];
-      int tot = 0;
-      for (int w = 0; w < kSW; ++w) tot += s.scan[w];
-      if (take) {
-        const int p = wbase + before;
-        s.slot[p] = ae.slot;
-        s.count[p] = ae.count;
-        s.offset[p] = ae.offset;
-      }
-      base += tot;
-      __syncthreads();
-    }
-    if (tid == 0) s.ns = base;
-  }
-  __syncthreads();
-  const int items = s.ns * ntn;
+  // ---- the call's experts with at most 16 tokens (and below the MFMA
+  // threshold), listed by the grouping; the block takes a contiguous run of
+  // items (expert, row tile) and keeps the list entries of its experts in LDS
+  const int ns = a.fixed_blob ? 1 : *a.n_small;
+  const int items = ns * ntn;
   const int per = (items + gridDim.x - 1) / gridDim.x;
   const int lo = blockIdx.x * per;
   const int hi = min(items, lo + per);
   if (lo >= hi) return;  // uniform over the block
   const int nv = (hi - lo) * NG;  // units of every wave
+  const int se0 = lo / ntn;       // first expert of the block (list index)
+  if (tid <= (hi - 1) / ntn - se0) {
+    if (a.fixed_blob) {
+      s.slot[0] = 0;
+      s.count[0] = a.fixed_count;
+      s.offset[0] = a.fixed_offset;
+    } else {
+      const ActiveExpert e = a.small[se0 + tid];
+      s.slot[tid] = e.slot;
+      s.count[tid] = e.count;
+      s.offset[tid] = e.offset;
+    }
+  }
 
   // ---- weight stream: unit v = (item lo + v / NG, scale group v % NG)
   // The unit loads are issued as inline assembly and waited for explicitly:
@@ -138,7 +116,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   auto load_unit = [&](int v, int slot_) __attribute__((always_inline)) {
     const int it = lo + v / NG, g = v - (v / NG) * NG;
     const int se = it / ntn, nt = it - se * ntn;
-    const uint8_t* blob = a.fixed_blob ? a.fixed_blob : a.blobs + (int64_t)s.slot[se] * a.blob_stride;
+    const uint8_t* blob = a.fixed_blob ? a.fixed_blob : a.blobs + (int64_t)s.slot[se - se0] * a.blob_stride;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int mat = MODE == 0 ? j : 2;
@@ -155,17 +133,14 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
                  : "n"((kRing - 1) * kUnitLoads)
                  : "memory");
   };
-#pragma unroll
-  for (int u = 0; u < kRing - 1; ++u) load_unit(min(u, nv - 1), u);
-
   // ---- activation tile of one expert: rows = its tokens, zero past the count
   int cur = -1;  // small-expert index whose tile is in LDS
   auto load_tile = [&](int se) __attribute__((always_inline)) {
-    __syncthreads();  // every wave is done with the previous tile
-    const int cnt = s.count[se];
+    __syncthreads();  // every wave is done with the previous tile (and the list is in LDS)
+    const int cnt = s.count[se - se0], off = s.offset[se - se0];
     if (tid < kTok) {
       int v = -1;
-      if (tid < cnt) v = a.fixed_blob ? tid : (MODE == 0 ? a.perm_tok[s.offset[se] + tid] : s.offset[se] + tid);
+      if (tid < cnt) v = a.fixed_blob ? tid : (MODE == 0 ? a.perm_tok[off + tid] : off + tid);
       s.tok[tid] = v;
     }
     __syncthreads();
@@ -177,7 +152,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
         const int t = s.tok[r];
         // gate/up reads token rows of x; down reads the rows of hbuf at the
         // expert's positions (the shared expert: positions offset + t)
-        const int64_t src_row = MODE == 0 ? (int64_t)t : (a.fixed_blob ? (int64_t)s.offset[se] + t : (int64_t)t);
+        const int64_t src_row = MODE == 0 ? (int64_t)t : (a.fixed_blob ? (int64_t)off + t : (int64_t)t);
         v = *reinterpret_cast<const u4*>(src + src_row * K + col);
       }
       *reinterpret_cast<u4*>(&s.a[r * LD + col]) = v;
@@ -185,6 +160,11 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
     __syncthreads();
     cur = se;
   };
+  // the first expert's tile is loaded before the weight stream starts: its
+  // loads would otherwise queue behind (and wait for) the ring's
+  load_tile(se0);
+#pragma unroll
+  for (int u = 0; u < kRing - 1; ++u) load_unit(min(u, nv - 1), u);
 
   f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
   uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u;
@@ -208,7 +188,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
     if (g == NG - 1) {
       // item done: lane holds D[token 4q + r][row n] of both sub-tiles
       const int nt = it - se * ntn;
-      const int cnt = s.count[se], off = s.offset[se];
+      const int cnt = s.count[se - se0], off = s.offset[se - se0];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tr = 4 * q + r;

@@ -56,8 +56,8 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int base[kMaxExperts];
   __shared__ unsigned long long mask[kRounds][kMaxExperts];
-  __shared__ int sh_warp[3][16];
-  __shared__ int sh_tot[3];
+  __shared__ int sh_warp[4][16];
+  __shared__ int sh_tot[4];
   __shared__ int16_t sid[kLdsPairs];    // ids by pair (validated in place)
   __shared__ int16_t sperm[kLdsPairs];  // token at each sorted position
   __shared__ int16_t spos[kLdsPairs];   // sorted position of each pair
@@ -117,10 +117,12 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
   // offsets and the active list (ascending expert id); E <= 1024 = one per thread
   const int c = (tid < E) ? cnt[tid] : 0;
   const int mtiles = c >= a.mfma_min ? (c + kMfmaTileTokens - 1) / kMfmaTileTokens : 0;
-  const int sv[3] = {c, mtiles, c > 0 ? 1 : 0};
-  int sx[3], st[3];
-  block_exclusive_scan<3>(sv, sx, st, sh_warp, sh_tot);
+  const bool small = c > 0 && c <= kStreamTokens && c < a.mfma_min;
+  const int sv[4] = {c, mtiles, c > 0 ? 1 : 0, small ? 1 : 0};
+  int sx[4], st[4];
+  block_exclusive_scan<4>(sv, sx, st, sh_warp, sh_tot);
   const int off = sx[0], moff = sx[1], mtotal = st[1], act = sx[2], nact = st[2];
+  const int sidx = sx[3], nsmall = st[3];
   int slot = 0;
   if (tid < E) {
     base[tid] = off;
@@ -187,9 +189,11 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
     a.mtile_off[act] = moff;
     a.active[act] = ActiveExpert{tid, slot, c, off};
   }
+  if (small) a.small[sidx] = ActiveExpert{tid, slot, c, off};
   if (tid == 0) {
     a.mtile_off[nact] = mtotal;
     *a.n_active = nact;
+    *a.n_small = nsmall;
   }
 }
 

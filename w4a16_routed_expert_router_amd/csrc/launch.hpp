@@ -34,6 +34,8 @@ struct GroupArgs {
   uint32_t* err;
   int mfma_min;             // experts with at least this many tokens take the MFMA path
   int32_t* mtile_off;       // [E+1] MFMA token-tile offsets over the active list
+  ActiveExpert* small;      // [E] active experts with at most kStreamTokens tokens (below mfma_min)
+  int32_t* n_small;         // [1]
 };
 void launch_group(const GroupArgs& a, hipStream_t stream);
 
@@ -72,6 +74,8 @@ struct ExpertArgs {
   uint16_t* hbuf;             // [positions, I] fp16
   float* ybuf;                // [positions, H] fp32
   int mfma_min;               // routed experts with count >= this are skipped (MFMA path)
+  const ActiveExpert* small;  // routed experts with at most kStreamTokens tokens, below mfma_min
+  const int32_t* n_small;
 };
 void launch_gateup_gemv(const ExpertArgs& a, hipStream_t stream);
 // Persistent weight-streaming expert kernel (expert_stream.hip) for experts with
