@@ -184,6 +184,24 @@ __device__ __forceinline__ float wave_max(float x) {
   return bcast63(x);
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp32<0x111, 0xf>(x, 0u));
+  x = max(x, dpp32<0x112, 0xf>(x, 0u));
+  x = max(x, dpp32<0x114, 0xf>(x, 0u));
+  x = max(x, dpp32<0x118, 0xf>(x, 0u));
+  x = max(x, dpp32<0x142, 0xa>(x, 0u));
+  x = max(x, dpp32<0x143, 0xc>(x, 0u));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+// Largest 64-bit key of the wave: the largest high half, then the largest
+// low half among the lanes holding that high half.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  const uint32_t hi = (uint32_t)(x >> 32);
+  const uint32_t hm = wave_max_u32(hi);
+  const uint32_t lm = wave_max_u32(hi == hm ? (uint32_t)x : 0u);
+  return ((uint64_t)hm << 32) | lm;
+}
+
 // Inclusive prefix sum over the lanes of a wave, on the same DPP network.
 __device__ __forceinline__ int wave_incl_scan(int x) {
   x += (int)dpp32<0x111, 0xf>((uint32_t)x, 0u);

@@ -151,12 +151,12 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict
     v[i] = (e < E) ? lg[e] : -INFINITY;
     mx = fmaxf(mx, v[i]);
   }
-  for (int o = kWave / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  mx = wave_max(mx);
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < kMaxV; ++i)
     if (i * kWave + lane < E) s += expf(v[i] - mx);
-  s = wave_sum_xor(s, kWave);
+  s = wave_sum(s);
 
   int my_id = 0;
   if (forced) {
@@ -186,10 +186,7 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict
           best = key > best ? key : best;
         }
       }
-      for (int o = kWave / 2; o > 0; o >>= 1) {
-        const uint64_t other = __shfl_xor(best, o, kWave);
-        best = other > best ? other : best;
-      }
+      best = wave_max_u64(best);  // DPP network: no LDS round trips
       const int id = (int)(~(uint32_t)best);
       if (lane == (id & (kWave - 1))) removed |= 1u << (id / kWave);
       if (lane == r) my_id = id;
@@ -198,7 +195,7 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict
   float my_w = 0.0f;
   if (lane < k) my_w = expf(lg[my_id] - mx) / s;
   if (renorm) {
-    const float tot = wave_sum_xor(lane < k ? my_w : 0.0f, kWave);
+    const float tot = wave_sum(lane < k ? my_w : 0.0f);
     my_w = my_w / tot;
   }
   if (lane < k) {
