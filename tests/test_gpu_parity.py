@@ -211,3 +211,46 @@ def test_layer_small_forced_expert_path(moe, T, path):
 def test_layer_olmoe_forced_mfma(moe, olmoe_layer, T):
     say(f"test_layer_olmoe_forced_mfma T={T}")
     _layer_case(moe, fx.OLMOE, "olmoe-layer", T, flags=moe.MOE_FLAG_FORCE_MFMA, wts=olmoe_layer)
+
+
+def _skewed_ids(T, E, k, heads, seed):
+    """Forced routing with a few crowded experts: expert j of `heads` takes the
+    first heads[j] tokens; the other slots of each token are distinct random
+    experts from the rest."""
+    rng = np.random.default_rng(seed)
+    ids = np.zeros((T, k), dtype=np.int32)
+    rest = np.arange(len(heads), E)
+    for t in range(T):
+        own = [j for j, c in enumerate(heads) if t < c][:k]
+        fill = rng.choice(rest, k - len(own), replace=False)
+        row = np.array(own + list(fill), dtype=np.int32)
+        ids[t] = row[rng.permutation(k)]
+    return ids
+
+
+@pytest.mark.parametrize("shape_name", ["olmoe", "small"])
+def test_layer_crowded_experts_mfma(moe, olmoe_layer, shape_name):
+    """Grouped GEMM with token tiles of every size: an expert holding every
+    token (several full 128-token tiles and a ragged one) and experts with
+    120, 100, 90, 40, 20 and 5 tokens next to evenly spread ones.  The small
+    shape runs the down projection with two weight sub-tiles per wave."""
+    say(f"test_layer_crowded_experts_mfma {shape_name}")
+    if shape_name == "olmoe":
+        shape, wts, T = fx.OLMOE, olmoe_layer, 512
+    else:
+        shape, T = SMALL, 300
+        wts = gpu_layer(shape, "gpu-crowded", 0)
+    heads = [T, 120, 100, 90, 40, 20, 5][:shape.top_k]
+    forced = _skewed_ids(T, shape.n_experts, shape.top_k, heads, 7)
+    ctx = moe.MoEContext(shape, n_layers=1, max_tokens=T, flags=moe.MOE_FLAG_FORCE_MFMA)
+    ctx.register_layer(0, wts)
+    x = fx.activations(("crowded", shape_name), T, shape.hidden).numpy()
+    xg = to_gpu(x)
+    ids, w = ctx.route(0, xg, forced_ids=to_gpu(forced))
+    out = ctx.expert_forward(0, xg, ids, w)
+    torch.cuda.synchronize()
+    assert ctx.check_device_errors() == 0
+    ref = ora.moe_layer(x, wts, shape, forced_ids=forced)
+    np.testing.assert_array_equal(ids.cpu().numpy(), forced)
+    assert_close(out.float().cpu().numpy(), ref["out"], f"crowded {shape_name}")
+    ctx.close()

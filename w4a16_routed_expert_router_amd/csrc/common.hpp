@@ -98,6 +98,15 @@ __device__ __forceinline__ void dequant8_v(uint32_t d, h2 out[4], uint32_t mlo, 
   out[3] = hi1 * k16th + km72;
 }
 
+// SwiGLU of one gate/up pair: silu(g) * u = g * u / (1 + e^-g), with the
+// hardware base-2 exponential and reciprocal (about one ulp each, far below
+// the FP16 rounding of the result).  Large negative g gives e^-g = inf and a
+// zero result, as the limit has it.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 __device__ __forceinline__ float dot2(h2 a, h2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }

@@ -701,7 +701,7 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         if (m < T) {
           const float gsum = s.red[wv][m][n] + s.red[wv + 1][m][n];
           const float usum = s.red[wv][m][n + 8] + s.red[wv + 1][m][n + 8];
-          hv = gsum / (1.0f + expf(-gsum)) * usum;
+          hv = swiglu(gsum, usum);
         }
         const float hn = __shfl_down(hv, 1, kWave);
         if (m < T && (n & 1) == 0) {

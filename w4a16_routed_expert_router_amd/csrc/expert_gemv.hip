@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void gateup_gemv_kernel(ExpertArgs a) {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         const int r = row0 + i * RPL + rsub;
-        const float hv = g[i] / (1.0f + expf(-g[i])) * u[i];
+        const float hv = swiglu(g[i], u[i]);
         reinterpret_cast<_Float16*>(a.hbuf)[(int64_t)pos * a.I + r] = (_Float16)hv;
       }
     }

@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
           if (MODE == 0) {
             const int row = nt * ROWS + wv * 16 + n;
             const float gv = acc[0][r], uv = acc[1][r];
-            reinterpret_cast<_Float16*>(a.hbuf)[pos * a.I + row] = (_Float16)(gv / (1.0f + expf(-gv)) * uv);
+            reinterpret_cast<_Float16*>(a.hbuf)[pos * a.I + row] = (_Float16)swiglu(gv, uv);
           } else {
 #pragma unroll
             for (int j = 0; j < 2; ++j) a.ybuf[pos * a.H + nt * ROWS + wv * 32 + j * 16 + n] = acc[j][r];
