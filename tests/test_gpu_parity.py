@@ -69,7 +69,7 @@ def test_route_ties_pick_lowest_id(moe):
 @pytest.mark.parametrize("flags", [0, 1])
 def test_route_olmoe_qwen_shapes(moe, flags):
     say(f"test_route_olmoe_qwen_shapes flags={flags}")
-    for shape, T in ((fx.OLMOE, 64), (fx.QWEN_NEXT, 16)):
+    for shape, T in ((fx.OLMOE, 64), (fx.OLMOE, 512), (fx.QWEN_NEXT, 16)):
         router = fx.router_only(shape, "gpu-route", 0, device="cuda").cpu().numpy()
         wts = {"router": router}
         ctx = moe.MoEContext(shape, n_layers=1, max_tokens=T, flags=flags)
@@ -102,6 +102,33 @@ def test_route_wide_range_inputs_exact(moe):
     ctx = _ctx(moe, SMALL)
     ctx.register_layer(0, wts)
     _check_route(ctx, wts, SMALL, x)
+
+
+def test_route_midpoint_logits_round_to_even(moe):
+    """Exact sums on an FP32 rounding midpoint: no FP64 error interval can be
+    certified there, so these logits take the exact tier and must round to even."""
+    say("test_route_midpoint_logits_round_to_even")
+    wts = gpu_layer(SMALL, "gpu-mid", 0)
+    H = SMALL.hidden
+    router = np.zeros((SMALL.n_experts, H), np.float16)
+    router[:, 0] = 1.0
+    router[:, 1] = np.float16(2.0 ** -24)              # smallest FP16 subnormal
+    router[:, 2] = np.arange(SMALL.n_experts) % 4      # 0..3 ulps of 1.0 at 2^-23
+    wts["router"] = router
+    x = np.zeros((3, H), np.float16)
+    x[:, 0] = 1.0
+    x[:, 1] = 1.0                                      # + 2^-24: half an ulp of 1.0
+    x[:, 2] = np.float16(2.0 ** -23)
+    x[1, 0] = 2.0                                      # 2 + 2^-24: a quarter ulp, not a midpoint
+    x[2, 3] = 1.0                                      # unused column
+    ctx = _ctx(moe, SMALL)
+    ctx.register_layer(0, wts)
+    _check_route(ctx, wts, SMALL, x)
+    _, _, lg = ctx.route(0, to_gpu(x), want_logits=True)
+    lg = lg.cpu().numpy()
+    # token 0, expert 0: 1 + 2^-24 rounds to even (1.0); expert 1: 1 + 2^-23 + 2^-24 rounds up
+    assert lg[0, 0] == np.float32(1.0)
+    assert lg[0, 1] == np.float32(1.0 + 2.0 ** -22)
 
 
 def test_route_forced_ids_gather_softmax(moe):
@@ -254,3 +281,33 @@ def test_layer_crowded_experts_mfma(moe, olmoe_layer, shape_name):
     np.testing.assert_array_equal(ids.cpu().numpy(), forced)
     assert_close(out.float().cpu().numpy(), ref["out"], f"crowded {shape_name}")
     ctx.close()
+
+
+def test_layer_crowded_experts_stream(moe, olmoe_layer):
+    """Batched decode with skewed routing: experts with 40 (grouped GEMM), 32,
+    31 and 17 tokens (two 16-token sub-tiles in the streaming kernel) and 16,
+    15, 2 and 1 (one sub-tile) next to evenly spread ones."""
+    say("test_layer_crowded_experts_stream")
+    shape, T = fx.OLMOE, 64
+    heads = [40, 32, 31, 17, 16, 15, 2, 1]
+    forced = _skewed_ids(T, shape.n_experts, shape.top_k, heads, 11)
+    ctx = moe.MoEContext(shape, n_layers=1, max_tokens=T)
+    ctx.register_layer(0, olmoe_layer)
+    x = fx.activations(("crowded-stream",), T, shape.hidden).numpy()
+    xg = to_gpu(x)
+    ids, w = ctx.route(0, xg, forced_ids=to_gpu(forced))
+    out = ctx.expert_forward(0, xg, ids, w)
+    torch.cuda.synchronize()
+    assert ctx.check_device_errors() == 0
+    ref = ora.moe_layer(x, olmoe_layer, shape, forced_ids=forced)
+    assert_close(out.float().cpu().numpy(), ref["out"], "crowded stream")
+    ctx.close()
+
+
+@pytest.mark.parametrize("T", [17, 32])
+def test_layer_shared_expert_two_subtiles(moe, T):
+    """A shared expert that sees every token of a 17- or 32-token batch runs
+    with two 16-token sub-tiles in the streaming kernel."""
+    say(f"test_layer_shared_expert_two_subtiles T={T}")
+    shape = fx.MoEShape(hidden=2048, n_experts=16, inter=512, top_k=2, renorm=True, shared_inter=512)
+    _layer_case(moe, shape, "gpu-shared-2sub", T)

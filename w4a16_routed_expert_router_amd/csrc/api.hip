@@ -55,6 +55,7 @@ struct moe_ctx {
   BlobLayout lay{}, shared_lay{};
   std::vector<LayerState> layers;
   float* logits = nullptr;
+  double* rscratch = nullptr;  // FP64 partial logits and norms of the matrix-core router
   int32_t* ids = nullptr;
   float* w = nullptr;
   int32_t* ids_s = nullptr;
@@ -211,6 +212,7 @@ int max_active(const moe_ctx* c, int T) {
 void run_router(moe_ctx* c, const RouterArgs& ra, hipStream_t s) {
   {
     ScopedTimer tm(c, kKindLogits, s);
+    if (launch_router(ra, c->rscratch, s)) return;
     launch_router_logits(ra, s);
   }
   ScopedTimer tm(c, kKindTopk, s);
@@ -228,10 +230,11 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   // shapes allow it (then every expert with up to kStreamTokens tokens), else
   // the GEMV kernels
   const bool force_gemv = (g.flags & MOE_FLAG_FORCE_GEMV) != 0;
-  // with at least kStreamTokens pairs per expert on average (prefill) every
-  // expert runs on the grouped GEMM and the few-token kernels are not launched
+  // with at least kPrefillPairsPerExpert pairs per expert on average (prefill)
+  // every expert runs on the grouped GEMM and the few-token kernels are not
+  // launched
   const bool all_mfma = !force_gemv && ((g.flags & MOE_FLAG_FORCE_MFMA) ||
-                                        (int64_t)T * g.top_k >= (int64_t)kStreamTokens * g.n_experts);
+                                        (int64_t)T * g.top_k >= (int64_t)kPrefillPairsPerExpert * g.n_experts);
   const bool stream_gu = !force_gemv && stream_supported(0, g.hidden, g.inter);
   const bool stream_dn = !force_gemv && stream_supported(1, g.inter, g.hidden);
   const int mfma_min = force_gemv ? INT32_MAX
@@ -377,6 +380,8 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   const int64_t P = (int64_t)g.max_tokens * g.top_k;
   const int Imax = g.inter;
   ok = ok && dalloc((void**)&c->logits, (size_t)g.max_tokens * g.n_experts * 4);
+  if (const size_t rb = router_scratch_bytes(g.max_tokens, g.n_experts, g.hidden))
+    ok = ok && dalloc((void**)&c->rscratch, rb);
   ok = ok && dalloc((void**)&c->ids, (size_t)P * 4);
   ok = ok && dalloc((void**)&c->w, (size_t)P * 4);
   ok = ok && dalloc((void**)&c->ids_s, (size_t)P * 4);
@@ -445,7 +450,7 @@ void moe_destroy(moe_ctx* c) {
       (void)hipEventDestroy(p.second);
     }
   }
-  void* bufs[] = {c->logits, c->ids,  c->w,    c->ids_s,   c->active,  c->n_active, c->perm_tok,
+  void* bufs[] = {c->logits, c->rscratch, c->ids,  c->w,    c->ids_s,   c->active,  c->n_active, c->perm_tok,
                   c->pos_of, c->hbuf, c->ybuf, c->xbuf,    c->err,     c->hshared,  c->yshared,
                   c->dlayers, c->mtile_off, c->xh, c->xlg, c->xhb, c->xgate, c->epoch};
   for (void* p : bufs) (void)hipFree(p);

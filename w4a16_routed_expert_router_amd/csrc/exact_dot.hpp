@@ -47,23 +47,34 @@ __device__ inline float round_i128_to_f32(__int128 S, int exp2) {
   return neg ? -f : f;
 }
 
-// Exact dot product of FP16 rows a, b of length H, over the whole wave.
-// Every lane returns the correctly rounded FP32 result.  b is in global memory.
+// Exact dot product of FP16 rows a, b of length H (a multiple of 8), over the
+// whole wave.  Every lane returns the correctly rounded FP32 result.  b is in
+// global memory.  Each lane loads up to four 8-element chunks before it uses
+// any, so the row costs one or two memory round trips.
 __device__ inline float exact_dot_wave(const uint16_t* a, const uint16_t* b, int H, int lane) {
+  constexpr int kAhead = 4;
   __int128 acc = 0;
-  for (int k = lane * 8; k < H; k += kWave * 8) {
-    const uint4 av = *reinterpret_cast<const uint4*>(a + k);
-    const uint4 bv = ldg_u4(b + k);
-    const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
-    const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+  for (int k0 = lane * 8; k0 < H; k0 += kAhead * kWave * 8) {
+    uint4 av[kAhead], bv[kAhead];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint16_t ah = (uint16_t)(aw[i >> 1] >> (16 * (i & 1)));
-      const uint16_t bh = (uint16_t)(bw[i >> 1] >> (16 * (i & 1)));
-      int32_t ma, sa, mb, sb;
-      f16_fixed(ah, ma, sa);
-      f16_fixed(bh, mb, sb);
-      acc += ((__int128)(ma * mb)) << (sa + sb);
+    for (int c = 0; c < kAhead; ++c) {
+      const int k = k0 + c * kWave * 8;
+      av[c] = k < H ? *reinterpret_cast<const uint4*>(a + k) : make_uint4(0u, 0u, 0u, 0u);
+      bv[c] = k < H ? ldg_u4(b + k) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int c = 0; c < kAhead; ++c) {
+      const uint32_t aw[4] = {av[c].x, av[c].y, av[c].z, av[c].w};
+      const uint32_t bw[4] = {bv[c].x, bv[c].y, bv[c].z, bv[c].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint16_t ah = (uint16_t)(aw[i >> 1] >> (16 * (i & 1)));
+        const uint16_t bh = (uint16_t)(bw[i >> 1] >> (16 * (i & 1)));
+        int32_t ma, sa, mb, sb;
+        f16_fixed(ah, ma, sa);
+        f16_fixed(bh, mb, sb);
+        acc += ((__int128)(ma * mb)) << (sa + sb);  // a zero chunk adds zero
+      }
     }
   }
   uint64_t lo = (uint64_t)acc;
@@ -80,46 +91,73 @@ __device__ inline float exact_dot_wave(const uint16_t* a, const uint16_t* b, int
 }
 
 
-// Certified tier: products of FP16 values are exact in FP32; they are summed in
-// FP64 with sum |p|, which bounds the FP64 error (each product passes through at
-// most `depth` additions).  Returns the FP32 rounding when the whole error
-// interval lies strictly between the two rounding midpoints of that value, so
-// it equals the rounding of the exact sum; otherwise falls back to the exact
-// tier.  All lanes of the wave must call it and get the same result.
-__device__ inline float certified_dot_wave(const uint16_t* a, const uint16_t* b, int H, int lane,
-                                           int exact_always) {
-  if (!exact_always) {
-    double acc = 0.0, asum = 0.0;
-    for (int k = lane * 8; k < H; k += kWave * 8) {
-      const uint4 av = *reinterpret_cast<const uint4*>(a + k);
-      const uint4 bv = *reinterpret_cast<const uint4*>(b + k);
-      const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
-      const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+
+// Compensated tier between the FP64 sum and the exact one.  Each product is
+// exact in FP64; they are added with TwoSum (Knuth), which returns the rounded
+// sum and its exact rounding error, the errors being summed separately, first
+// within a lane and then over the lanes' tree.  The pair (s, c) then differs
+// from the exact sum only by the rounding of the error sum: at most
+// (depth + 2) 2^-53 * sum|e| with sum|e| <= (H + 64) 2^-53 * S (one error
+// per product and per tree addition, each at most half an ulp of a partial
+// sum bounded by S), where S bounds
+// sum |x_i w_i| (the caller's `S`).  The FP32 rounding of s + c is returned
+// with *ok set when the exact sum, so bounded, lies strictly inside that
+// value's rounding interval; every lane returns the same result.
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  const double bp = s - a;
+  e = (a - (s - bp)) + (b - bp);
+}
+__device__ inline float compensated_dot_wave(const uint16_t* a, const uint16_t* b, int H, int lane, double S,
+                                             bool* ok) {
+  constexpr int kAhead = 4;
+  double s = 0.0, c = 0.0;
+  int n_local = 0;
+  for (int k0 = lane * 8; k0 < H; k0 += kAhead * kWave * 8) {
+    uint4 av[kAhead], bv[kAhead];
+#pragma unroll
+    for (int q = 0; q < kAhead; ++q) {
+      const int k = k0 + q * kWave * 8;
+      av[q] = k < H ? *reinterpret_cast<const uint4*>(a + k) : make_uint4(0u, 0u, 0u, 0u);
+      bv[q] = k < H ? ldg_u4(b + k) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int q = 0; q < kAhead; ++q) {
+      const uint32_t aw[4] = {av[q].x, av[q].y, av[q].z, av[q].w};
+      const uint32_t bw[4] = {bv[q].x, bv[q].y, bv[q].z, bv[q].w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float x = half_bits_to_float((uint16_t)(aw[i >> 1] >> (16 * (i & 1))));
-        const float y = half_bits_to_float((uint16_t)(bw[i >> 1] >> (16 * (i & 1))));
-        const double p = (double)(x * y);
-        acc += p;
-        asum += fabs(p);
+        const double x = (double)half_bits_to_float((uint16_t)(aw[i >> 1] >> (16 * (i & 1))));
+        const double y = (double)half_bits_to_float((uint16_t)(bw[i >> 1] >> (16 * (i & 1))));
+        double e;
+        two_sum(s, x * y, s, e);  // x * y exact: 22 significant bits
+        c += e;
       }
     }
-    // xor butterfly: every lane ends with bit-identical sums
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-      acc += __shfl_xor(acc, o, kWave);
-      asum += __shfl_xor(asum, o, kWave);
-    }
-    const int depth = 8 * ((H + 511) / 512) + 6;
-    const double eps = (double)(depth + 2) * 0x1p-52 * asum;
-    const float r = (float)acc;
-    if (r != 0.0f && isfinite(r) && isfinite(acc)) {
-      const double rd = (double)r;
-      const double m_lo = 0.5 * (rd + (double)nextafterf(r, -INFINITY));
-      const double m_hi = 0.5 * (rd + (double)nextafterf(r, INFINITY));
-      if (acc - eps > m_lo && acc + eps < m_hi) return r;
-    }
+    n_local += kAhead * 8;
   }
-  return exact_dot_wave(a, b, H, lane);
+  // xor butterfly: every lane ends with the same (s, c)
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const double s2 = __shfl_xor(s, o, kWave);
+    const double c2 = __shfl_xor(c, o, kWave);
+    double e;
+    two_sum(s, s2, s, e);
+    c = (c + c2) + e;
+  }
+  const int depth = n_local + 2 * 6;  // additions any error term went through
+  const double eps = (double)(depth + 2) * 0x1p-53 * ((double)(H + 64) * 0x1p-53 * S) * (1.0 + 0x1p-20);
+  const double sd = s + c;
+  const float r = (float)sd;
+  *ok = false;
+  if (r != 0.0f && isfinite(r) && isfinite(sd)) {
+    const double rd = (double)r;
+    const double m_lo = 0.5 * (rd + (double)nextafterf(r, -INFINITY));
+    const double m_hi = 0.5 * (rd + (double)nextafterf(r, INFINITY));
+    // distances to the midpoints, each off by a few roundings of itself at
+    // most: demand twice the bound
+    *ok = ((s - m_lo) + c) > 2.0 * eps && ((m_hi - s) - c) > 2.0 * eps;
+  }
+  return r;
 }
 
 }  // namespace moe

@@ -4,7 +4,7 @@
 //
 // The experts run straight from packed INT4 codes with FP16 group scales and
 // FP16 activations; weights are never expanded in memory ("Horizon RunMap",
-// "Architecture invariants").  With at most 16 tokens per expert the work is
+// "Architecture invariants").  With at most 32 tokens per expert the work is
 // bound by streaming the weights, so the kernel is shaped for that:
 //   * one block per compute unit takes a contiguous run of work items
 //     (expert, tile of output rows), so consecutive items are mostly row tiles
@@ -14,8 +14,9 @@
 //     ring runs across item boundaries, so the weight stream never drains
 //     between items and no barrier stops it (a barrier is taken only when the
 //     next item belongs to another expert and its activations are loaded);
-//   * the tokens of the expert (<= 16, zero-padded) are the A operand of
-//     v_mfma_f32_16x16x32_f16; INT4 codes are decoded in registers to the
+//   * the tokens of the expert (<= 32, zero-padded to one or two 16-token
+//     sub-tiles; the second only when the expert has more than 16) are the A
+//     operand of v_mfma_f32_16x16x32_f16; INT4 codes are decoded in registers to the
 //     exact FP16 values q - 8, and each 128-wide group's FP32 MFMA result is
 //     multiplied by its FP16 scale before it is added to the accumulator.
 // MFMA operand layout (gfx950): lane l holds A[l%16][8*(l/16)+e],
@@ -36,7 +37,7 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSW = 8;          // waves per block
 constexpr int kRing = 8;        // weight units in flight per wave
-constexpr int kTok = 16;        // tokens per expert handled here
+constexpr int kTok = 32;        // tokens per expert handled here (two sub-tiles of 16)
 constexpr int kPad = 8;         // LDS row padding (halves)
 constexpr int kMaxList = 1024;  // experts per call
 
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   const int N = MODE == 0 ? a.I : a.H;
   const int ntn = N / ROWS;
 
-  // ---- the call's experts with at most 16 tokens (and below the MFMA
+  // ---- the call's experts with at most 32 tokens (and below the MFMA
   // threshold), listed by the grouping; the block takes a contiguous run of
   // items (expert, row tile) and keeps the list entries of its experts in LDS
   const int ns = a.fixed_blob ? 1 : *a.n_small;
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   };
   // ---- activation tile of one expert: rows = its tokens, zero past the count
   int cur = -1;  // small-expert index whose tile is in LDS
+  bool two = false;  // its tile has a second 16-token sub-tile (uniform)
   auto load_tile = [&](int se) __attribute__((always_inline)) {
     __syncthreads();  // every wave is done with the previous tile (and the list is in LDS)
     const int cnt = s.count[se - se0], off = s.offset[se - se0];
@@ -145,7 +147,9 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
     }
     __syncthreads();
     const uint16_t* src = MODE == 0 ? a.x : a.hbuf;
-    for (int c = tid; c < kTok * (K / 8); c += kSW * kWave) {
+    // rows of the sub-tiles the MFMAs read; past the count they are zero
+    const int rows = cnt > 16 ? kTok : 16;
+    for (int c = tid; c < rows * (K / 8); c += kSW * kWave) {
       const int r = c / (K / 8), col = (c - r * (K / 8)) * 8;
       u4 v = u4{0u, 0u, 0u, 0u};
       if (r < cnt) {
@@ -159,6 +163,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
     }
     __syncthreads();
     cur = se;
+    two = cnt > 16;
   };
   // the first expert's tile is loaded before the weight stream starts: its
   // loads would otherwise queue behind (and wait for) the ring's
@@ -166,7 +171,9 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
 #pragma unroll
   for (int u = 0; u < kRing - 1; ++u) load_unit(min(u, nv - 1), u);
 
-  f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+  f4 acc[2][2];  // [sub-tile][weight sub-tile]
+#pragma unroll
+  for (int m = 0; m < 2; ++m) acc[m][0] = acc[m][1] = f4{0.f, 0.f, 0.f, 0.f};
   uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u;
   asm("" : "+v"(mlo), "+v"(mhi));  // the decode masks live in VGPRs
   auto step = [&](int v, auto uc) __attribute__((always_inline)) {
@@ -176,35 +183,57 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
     if (g == 0 && se != cur) load_tile(se);  // uniform: same v sequence in every wave
     load_unit(min(v + kRing - 1, nv - 1), (U + kRing - 1) % kRing);
     wait_unit(U);
-    f4 ag[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+    f4 ag[2][2];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const h8 af = *reinterpret_cast<const h8*>(&s.a[n * LD + g * kGroup + 32 * q + 8 * st]);
-      ag[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, decode_unscaled(bq[U][0][st], mlo, mhi), ag[0], 0, 0, 0);
-      ag[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, decode_unscaled(bq[U][1][st], mlo, mhi), ag[1], 0, 0, 0);
+    for (int m = 0; m < 2; ++m) ag[m][0] = ag[m][1] = f4{0.f, 0.f, 0.f, 0.f};
+    if (two) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const h8 b0 = decode_unscaled(bq[U][0][st], mlo, mhi), b1 = decode_unscaled(bq[U][1][st], mlo, mhi);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const h8 af = *reinterpret_cast<const h8*>(&s.a[(16 * m + n) * LD + g * kGroup + 32 * q + 8 * st]);
+          ag[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b0, ag[m][0], 0, 0, 0);
+          ag[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b1, ag[m][1], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const h8 af = *reinterpret_cast<const h8*>(&s.a[n * LD + g * kGroup + 32 * q + 8 * st]);
+        ag[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, decode_unscaled(bq[U][0][st], mlo, mhi), ag[0][0], 0, 0, 0);
+        ag[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, decode_unscaled(bq[U][1][st], mlo, mhi), ag[0][1], 0, 0, 0);
+      }
     }
-    acc[0] += ag[0] * half_bits_to_float((uint16_t)bs[U][0]);
-    acc[1] += ag[1] * half_bits_to_float((uint16_t)bs[U][1]);
+    const float s0 = half_bits_to_float((uint16_t)bs[U][0]), s1 = half_bits_to_float((uint16_t)bs[U][1]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      acc[m][0] += ag[m][0] * s0;
+      acc[m][1] += ag[m][1] * s1;
+    }
     if (g == NG - 1) {
-      // item done: lane holds D[token 4q + r][row n] of both sub-tiles
+      // item done: lane holds D[token 16m + 4q + r][row n] of both weight sub-tiles
       const int nt = it - se * ntn;
       const int cnt = s.count[se - se0], off = s.offset[se - se0];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tr = 4 * q + r;
-        if (tr < cnt) {
-          const int64_t pos = off + tr;
-          if (MODE == 0) {
-            const int row = nt * ROWS + wv * 16 + n;
-            const float gv = acc[0][r], uv = acc[1][r];
-            reinterpret_cast<_Float16*>(a.hbuf)[pos * a.I + row] = (_Float16)swiglu(gv, uv);
-          } else {
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) a.ybuf[pos * a.H + nt * ROWS + wv * 32 + j * 16 + n] = acc[j][r];
+        for (int r = 0; r < 4; ++r) {
+          const int tr = 16 * m + 4 * q + r;
+          if (tr < cnt) {
+            const int64_t pos = off + tr;
+            if (MODE == 0) {
+              const int row = nt * ROWS + wv * 16 + n;
+              const float gv = acc[m][0][r], uv = acc[m][1][r];
+              reinterpret_cast<_Float16*>(a.hbuf)[pos * a.I + row] = (_Float16)swiglu(gv, uv);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 2; ++j) a.ybuf[pos * a.H + nt * ROWS + wv * 32 + j * 16 + n] = acc[m][j][r];
+            }
           }
         }
-      }
-      acc[0] = acc[1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) acc[m][0] = acc[m][1] = f4{0.f, 0.f, 0.f, 0.f};
     }
   };
   for (int v0 = 0; v0 < nv; v0 += kRing) {

@@ -20,6 +20,11 @@ struct RouterArgs {
   int exact_always;
 };
 void launch_router_logits(const RouterArgs& a, hipStream_t stream);
+// logits + softmax/top-k on the FP64 matrix cores, using `scratch` of
+// router_scratch_bytes(); returns false, launching nothing, when the shape or
+// the flags do not take that path (then launch_router_logits + _topk)
+bool launch_router(const RouterArgs& a, double* scratch, hipStream_t stream);
+size_t router_scratch_bytes(int max_tokens, int E, int H);
 void launch_router_topk(const RouterArgs& a, hipStream_t stream);
 
 struct GroupArgs {
@@ -80,7 +85,10 @@ struct ExpertArgs {
 void launch_gateup_gemv(const ExpertArgs& a, hipStream_t stream);
 // Persistent weight-streaming expert kernel (expert_stream.hip) for experts with
 // at most kStreamTokens tokens (and below mfma_min); mode 0 gate/up, 1 down.
-constexpr int kStreamTokens = 16;
+constexpr int kStreamTokens = 32;
+// with at least this many (token, expert) pairs per expert on average (a
+// prefill) every expert takes the grouped GEMM
+constexpr int kPrefillPairsPerExpert = 16;
 bool stream_supported(int mode, int K, int rows);
 void launch_stream_expert(const ExpertArgs& a, int mode, int grid, hipStream_t stream);
 void launch_down_gemv(const ExpertArgs& a, hipStream_t stream);

@@ -9,11 +9,13 @@
 // logit[t,e] is defined as the FP32 value nearest (ties to even) to the exact
 // real dot product of the FP16 inputs, so the selected experts do not depend on
 // summation order.  It is reached in two tiers:
-//   1. every FP16 x FP16 product is exact in FP32; products are summed in FP64
-//      together with sum |p|, which bounds the FP64 error; the FP64 sum is
-//      rounded to FP32 and accepted when the whole error interval rounds to the
-//      same FP32 value (it lies strictly between that value's two rounding
-//      midpoints);
+//   1. every FP16 x FP16 product is exact in FP32 (and FP64); products are
+//      summed in FP64 together with a bound on sum |p| (the sum itself, or the
+//      product of the two rows' norms), which bounds the FP64 error; the FP64
+//      sum is rounded to FP32 and accepted when the whole error interval
+//      rounds to the same FP32 value (it lies strictly between that value's
+//      two rounding midpoints).  Shapes with a multiple of 16 experts run this
+//      tier on the FP64 matrix cores;
 //   2. otherwise (about one logit in 10^6) the wave recomputes the sum exactly
 //      as a 128-bit fixed-point integer (unit 2^-48) and rounds it once.
 #include "common.hpp"
@@ -132,21 +134,17 @@ __device__ __forceinline__ uint64_t rank_key(float v, int id) {
   return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)id);
 }
 
-// grid T, block 64: softmax + top-k (or forced ids) for one token per wave.
-__global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict__ logits, int T,
-                                                         int E, int k, int renorm,
-                                                         const int32_t* __restrict__ forced,
-                                                         int32_t* __restrict__ ids,
-                                                         float* __restrict__ w,
-                                                         uint32_t* __restrict__ err) {
-  constexpr int kMaxV = 16;  // E <= 1024
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x;
-  const float* lg = logits + (int64_t)t * E;
-  float v[kMaxV];
+// Softmax + top-k (or the forced ids) of one token, by one wave.  lg holds the
+// token's E logits (global memory or LDS); KV = ceil(E / 64) logits per lane.
+template <int KV>
+__device__ __forceinline__ void topk_token(const float* lg, int t, int E, int k, int renorm,
+                                           const int32_t* __restrict__ forced,
+                                           int32_t* __restrict__ ids, float* __restrict__ w,
+                                           uint32_t* __restrict__ err, int lane) {
+  float v[KV];
   float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kMaxV; ++i) {
+  for (int i = 0; i < KV; ++i) {
     const int e = i * kWave + lane;
     v[i] = (e < E) ? lg[e] : -INFINITY;
     mx = fmaxf(mx, v[i]);
@@ -154,7 +152,7 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict
   mx = wave_max(mx);
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kMaxV; ++i)
+  for (int i = 0; i < KV; ++i)
     if (i * kWave + lane < E) s += expf(v[i] - mx);
   s = wave_sum(s);
 
@@ -179,7 +177,7 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict
     for (int r = 0; r < k; ++r) {
       uint64_t best = 0;
 #pragma unroll
-      for (int i = 0; i < kMaxV; ++i) {
+      for (int i = 0; i < KV; ++i) {
         const int e = i * kWave + lane;
         if (e < E && !((removed >> i) & 1u)) {
           const uint64_t key = rank_key(v[i], e);
@@ -202,6 +200,233 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict
     ids[(int64_t)t * k + lane] = my_id;
     w[(int64_t)t * k + lane] = my_w;
   }
+}
+
+// grid T, block 64: softmax + top-k (or forced ids) for one token per wave.
+__global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int k, int renorm,
+                                                         const int32_t* __restrict__ forced,
+                                                         int32_t* __restrict__ ids,
+                                                         float* __restrict__ w,
+                                                         uint32_t* __restrict__ err) {
+  (void)T;
+  const int t = blockIdx.x;
+  topk_token<16>(logits + (int64_t)t * E, t, E, k, renorm, forced, ids, w, err, threadIdx.x);  // E <= 1024
+}
+
+// ---- FP64 matrix-core logits -----------------------------------------------------
+// The certified tier on v_mfma_f64_16x16x4_f64, in two launches.
+//
+// router_partial_kernel: every FP16 value is exact in FP64 and so is every
+// product (22 significant bits), so the only rounding is in the accumulation.
+// Block (x, y, z) covers the 16x16 tile of tokens 16y.., experts 16x.. over
+// the K range [z*4*KR, (z+1)*4*KR); its wave w takes the KR-wide part w of
+// that range.  Lane (r, q) = (lane % 16, lane / 16) loads 8 consecutive K of
+// token row r and of expert row r; MFMA (c, e) takes K index 32c + 8q + e from
+// lane group q for both operands, so A and B see the same permutation of K
+// and the tile is the plain dot product.  The four wave tiles are added in
+// LDS in wave order and written as the block's FP64 partial, together with
+// the squared norms of the token and expert rows over the same K range.
+//
+// router_select_kernel (one wave per token): adds the partials of the K
+// blocks in order and certifies each logit.  An output is reached through at
+// most KR / 2 roundings in each of its wave's two chains (one per product),
+// the addition of the two chains, 3 additions in the block and KB - 1 over
+// the K blocks (together below KR + KB + 4), each with a relative error of at most 2^-53 of a partial sum
+// bounded by S = sum |x_i w_i|; by Cauchy-Schwarz S <= |x| |w|, from the
+// squared norms (their own relative error, below H * 2^-53, is covered by the
+// factor 1 + 2^-20).  The logit is certified when the interval of half-width
+// (KR + KB + 4) * 2^-52 * |x| |w| around the FP64 sum lies strictly between
+// the rounding midpoints of its FP32 rounding; the wave recomputes the others
+// with compensated FP64 sums (certified the same way against a bound about
+// 2^-52 times smaller) and, where that still fails (an exact sum on or next
+// to a midpoint), exactly.  Softmax and top-k follow.
+typedef double d4 __attribute__((ext_vector_type(4)));
+constexpr int kRmTile = 16;  // tokens and experts per MFMA tile
+constexpr int kRmWaves = 4;  // K parts per block
+constexpr int kRmMaxKB = 8;  // K blocks
+
+template <int KR>
+__global__ __launch_bounds__(kRmWaves * kWave) void router_partial_kernel(RouterArgs a, double* __restrict__ part,
+                                                                          double* __restrict__ nrm_x,
+                                                                          double* __restrict__ nrm_w) {
+  __shared__ double sp[kRmWaves][kRmTile * kRmTile];
+  __shared__ double sn[kRmWaves][2 * kRmTile];  // token norms, then expert norms
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int T = a.T, E = a.E, H = a.H;
+  const int e0 = blockIdx.x * kRmTile, t0 = blockIdx.y * kRmTile, kb = blockIdx.z;
+  const int k0 = (kb * kRmWaves + wv) * KR;
+  const int tr = min(t0 + r, T - 1);
+  const uint16_t* xa = a.x + (int64_t)tr * H + k0 + 8 * q;
+  const uint16_t* wb = a.wr + (int64_t)(e0 + r) * H + k0 + 8 * q;
+  constexpr int NC = KR / 32;  // 32-wide K chunks, all loaded up front
+  uint4 av[NC], bv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    av[c] = *reinterpret_cast<const uint4*>(xa + 32 * c);
+    bv[c] = ldg_u4(wb + 32 * c);
+  }
+  // two independent accumulation chains (even and odd e), added at the end
+  d4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+  double sx = 0.0, sw = 0.0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint32_t au[4] = {av[c].x, av[c].y, av[c].z, av[c].w};
+    const uint32_t bu[4] = {bv[c].x, bv[c].y, bv[c].z, bv[c].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double xv = (double)half_bits_to_float((uint16_t)(au[e >> 1] >> (16 * (e & 1))));
+      const double wvv = (double)half_bits_to_float((uint16_t)(bu[e >> 1] >> (16 * (e & 1))));
+      sx = fma(xv, xv, sx);
+      sw = fma(wvv, wvv, sw);
+      if (e & 1)
+        acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(xv, wvv, acc1, 0, 0, 0);
+      else
+        acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(xv, wvv, acc0, 0, 0, 0);
+    }
+  }
+  const d4 acc = acc0 + acc1;
+  // squared norms of the wave's K range: sum over the four lane groups
+  sx += __shfl_xor(sx, 16, kWave);
+  sx += __shfl_xor(sx, 32, kWave);
+  sw += __shfl_xor(sw, 16, kWave);
+  sw += __shfl_xor(sw, 32, kWave);
+  if (q == 0) {
+    sn[wv][r] = sx;
+    sn[wv][kRmTile + r] = sw;
+  }
+  // lane holds D[token q + 4i][expert r] (the FP64 layout; the FP16 MFMAs
+  // put rows 4q + i in a lane instead)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sp[wv][(q + 4 * i) * kRmTile + r] = acc[i];
+  __syncthreads();
+  // one output per thread: tid = 16 * token + expert
+  {
+    const int ti = tid >> 4, ei = tid & 15;
+    const double s = ((sp[0][tid] + sp[1][tid]) + sp[2][tid]) + sp[3][tid];
+    if (t0 + ti < T) part[((int64_t)kb * T + t0 + ti) * E + e0 + ei] = s;
+  }
+  if (tid < kRmTile) {
+    const double nx = ((sn[0][tid] + sn[1][tid]) + sn[2][tid]) + sn[3][tid];
+    if (blockIdx.x == 0 && t0 + tid < T) nrm_x[(int64_t)kb * T + t0 + tid] = nx;
+  } else if (tid < 2 * kRmTile) {
+    const int i = tid - kRmTile;
+    const double nw = ((sn[0][tid] + sn[1][tid]) + sn[2][tid]) + sn[3][tid];
+    if (blockIdx.y == 0) nrm_w[(int64_t)kb * E + e0 + i] = nw;
+  }
+}
+
+// grid T, block 64.  KV = ceil(E / 64) experts per lane (expert i*64 + lane).
+template <int KV>
+__global__ __launch_bounds__(64) void router_select_kernel(RouterArgs a, const double* __restrict__ part,
+                                                           const double* __restrict__ nrm_x,
+                                                           const double* __restrict__ nrm_w, int KB, int KR) {
+  __shared__ float slg[KV * kWave];
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const int T = a.T, E = a.E;
+  // every partial is loaded before any is added (at most kRmMaxKB of each)
+  double pv[kRmMaxKB];
+#pragma unroll
+  for (int kb = 0; kb < kRmMaxKB; ++kb) pv[kb] = kb < KB ? nrm_x[(int64_t)kb * T + t] : 0.0;
+  double nx = 0.0;
+#pragma unroll
+  for (int kb = 0; kb < kRmMaxKB; ++kb)
+    if (kb < KB) nx += pv[kb];  // fixed order
+  uint64_t todo[KV];
+#pragma unroll
+  for (int i = 0; i < KV; ++i) {
+    const int e = i * kWave + lane;
+    const int ec = min(e, E - 1);
+    double sv[kRmMaxKB], wv[kRmMaxKB];
+#pragma unroll
+    for (int kb = 0; kb < kRmMaxKB; ++kb) {
+      sv[kb] = kb < KB ? part[((int64_t)kb * T + t) * E + ec] : 0.0;
+      wv[kb] = kb < KB ? nrm_w[(int64_t)kb * E + ec] : 0.0;
+    }
+    bool certified = false;
+    if (e < E) {
+      double s = 0.0, nw = 0.0;
+#pragma unroll
+      for (int kb = 0; kb < kRmMaxKB; ++kb)
+        if (kb < KB) {  // fixed order
+          s += sv[kb];
+          nw += wv[kb];
+        }
+      const float rr = (float)s;  // round to nearest even
+      if (rr != 0.0f && isfinite(rr) && isfinite(s)) {
+        const double bound = sqrt(nx) * sqrt(nw) * (1.0 + 0x1p-20);
+        const double eps = (double)(KR + KB + 4) * 0x1p-52 * bound;
+        const double rd = (double)rr;
+        const double m_lo = 0.5 * (rd + (double)nextafterf(rr, -INFINITY));
+        const double m_hi = 0.5 * (rd + (double)nextafterf(rr, INFINITY));
+        certified = s - eps > m_lo && s + eps < m_hi;
+      }
+      if (certified) slg[e] = rr;
+    }
+    todo[i] = __ballot(e < E && !certified);
+  }
+  // compensated, then exact tier for the logits that were not certified
+#pragma unroll
+  for (int i = 0; i < KV; ++i) {
+    uint64_t m = todo[i];
+    while (m) {
+      const int e = i * kWave + __builtin_ctzll(m);
+      m &= m - 1;
+      const uint16_t* xr = a.x + (int64_t)t * a.H;
+      const uint16_t* wr = a.wr + (int64_t)e * a.H;
+      double nw = 0.0;
+      for (int kb = 0; kb < KB; ++kb) nw += nrm_w[(int64_t)kb * E + e];
+      bool ok;
+      float rr = compensated_dot_wave(xr, wr, a.H, lane, sqrt(nx) * sqrt(nw) * (1.0 + 0x1p-20), &ok);
+      if (!ok) rr = exact_dot_wave(xr, wr, a.H, lane);
+      if (lane == 0) slg[e] = rr;
+    }
+  }
+  __syncthreads();
+  for (int e = lane; e < E; e += kWave) a.logits[(int64_t)t * E + e] = slg[e];
+  topk_token<KV>(slg, t, E, a.k, a.renorm, a.forced, a.ids, a.w, a.err, lane);
+}
+
+// K per wave of the matrix-core router (0: the shape does not take it).
+static int mfma_router_kr(int H, int E) {
+  if (E % kRmTile != 0 || E > 1024) return 0;
+  for (int kr = 128; kr >= 64; kr /= 2)
+    if (H % (kRmWaves * kr) == 0 && H / (kRmWaves * kr) <= kRmMaxKB) return kr;
+  return 0;
+}
+
+size_t router_scratch_bytes(int max_tokens, int E, int H) {
+  const int kr = mfma_router_kr(H, E);
+  if (!kr) return 0;
+  const int64_t KB = H / (kRmWaves * kr);
+  return (size_t)(KB * ((int64_t)max_tokens * E + max_tokens + E) * 8);
+}
+
+// Logits + softmax/top-k.  Returns false (nothing launched) when the shape
+// does not take the matrix-core router.
+bool launch_router(const RouterArgs& a, double* scratch, hipStream_t stream) {
+  const int kr = mfma_router_kr(a.H, a.E);
+  if (a.exact_always || !kr || !scratch) return false;
+  const int KB = a.H / (kRmWaves * kr);
+  double* part = scratch;
+  double* nrm_x = part + (int64_t)KB * a.T * a.E;
+  double* nrm_w = nrm_x + (int64_t)KB * a.T;
+  dim3 g(a.E / kRmTile, (a.T + kRmTile - 1) / kRmTile, KB);
+  if (kr == 128)
+    hipLaunchKernelGGL((router_partial_kernel<128>), g, dim3(kRmWaves * kWave), 0, stream, a, part, nrm_x, nrm_w);
+  else
+    hipLaunchKernelGGL((router_partial_kernel<64>), g, dim3(kRmWaves * kWave), 0, stream, a, part, nrm_x, nrm_w);
+  const int kv = (a.E + kWave - 1) / kWave;
+  if (kv == 1)
+    hipLaunchKernelGGL((router_select_kernel<1>), dim3(a.T), dim3(kWave), 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+  else if (kv <= 2)
+    hipLaunchKernelGGL((router_select_kernel<2>), dim3(a.T), dim3(kWave), 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+  else if (kv <= 8)
+    hipLaunchKernelGGL((router_select_kernel<8>), dim3(a.T), dim3(kWave), 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+  else
+    hipLaunchKernelGGL((router_select_kernel<16>), dim3(a.T), dim3(kWave), 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+  return true;
 }
 
 void launch_router_logits(const RouterArgs& a, hipStream_t stream) {
