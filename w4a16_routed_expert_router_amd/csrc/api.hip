@@ -266,6 +266,17 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   ea.perm_tok = c->perm_tok;
   ea.hbuf = c->hbuf;
   ea.ybuf = c->ybuf;
+  // a shared expert of the routed experts' shape rides along in the streaming
+  // launches as one more list entry (one weight stream over the whole chip
+  // instead of two launches of its own)
+  const bool shared_in_stream = g.shared_inter == g.inter && !all_mfma && stream_gu && stream_dn &&
+                                T <= kStreamTokens;
+  if (shared_in_stream) {
+    ea.shared_blob = L.shared;
+    ea.shared_count = T;
+    ea.shared_h = c->hshared;
+    ea.shared_y = c->yshared;
+  }
   if (!all_mfma) {
     ScopedTimer tm(c, kKindGateUp, s);
     if (stream_gu) launch_stream_expert(ea, 0, c->ncu, s);
@@ -284,8 +295,9 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
     ScopedTimer tm(c, kKindMfmaDown, s);
     launch_mfma_down(ma, mfma_max_tiles(T, g.top_k, g.n_experts, g.hidden, 1), s);
   }
-  if (g.shared_inter) {
+  if (g.shared_inter && !shared_in_stream) {
     ExpertArgs sa = ea;
+    sa.shared_blob = nullptr;
     sa.lay = c->shared_lay;
     sa.fixed_blob = L.shared;
     sa.fixed_count = T;
@@ -564,7 +576,7 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t layer_begin, int32_t layer_end,
     fa.exact_always = (int)(g.flags & MOE_FLAG_ROUTER_EXACT_ALWAYS);
     fa.lay = c->lay;
     fa.blob_stride = c->lay.total();
-    fa.lg_reps = T * g.n_experts <= 512 ? kFLogitReps : 1;
+    fa.lg_reps = T * g.n_experts <= 256 ? kFLogitReps : 1;
     {
       // split each logit over up to 4 waves while every wave of a replica
       // still has at most one item

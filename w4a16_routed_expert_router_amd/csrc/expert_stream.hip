@@ -81,9 +81,12 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   const int ntn = N / ROWS;
 
   // ---- the call's experts with at most 32 tokens (and below the MFMA
-  // threshold), listed by the grouping; the block takes a contiguous run of
-  // items (expert, row tile) and keeps the list entries of its experts in LDS
-  const int ns = a.fixed_blob ? 1 : *a.n_small;
+  // threshold), listed by the grouping, then the shared expert if it rides
+  // along; the block takes a contiguous run of items (expert, row tile) and
+  // keeps the list entries of its experts in LDS (slot -1 marks the shared
+  // expert)
+  const int nrouted = a.fixed_blob ? 1 : *a.n_small;
+  const int ns = nrouted + (a.shared_blob ? 1 : 0);
   const int items = ns * ntn;
   const int per = (items + gridDim.x - 1) / gridDim.x;
   const int lo = blockIdx.x * per;
@@ -96,6 +99,10 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
       s.slot[0] = 0;
       s.count[0] = a.fixed_count;
       s.offset[0] = a.fixed_offset;
+    } else if (se0 + tid == nrouted) {
+      s.slot[tid] = -1;
+      s.count[tid] = a.shared_count;
+      s.offset[tid] = 0;
     } else {
       const ActiveExpert e = a.small[se0 + tid];
       s.slot[tid] = e.slot;
@@ -117,7 +124,10 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   auto load_unit = [&](int v, int slot_) __attribute__((always_inline)) {
     const int it = lo + v / NG, g = v - (v / NG) * NG;
     const int se = it / ntn, nt = it - se * ntn;
-    const uint8_t* blob = a.fixed_blob ? a.fixed_blob : a.blobs + (int64_t)s.slot[se - se0] * a.blob_stride;
+    const int sl = s.slot[se - se0];
+    const uint8_t* blob = a.fixed_blob ? a.fixed_blob
+                          : sl < 0    ? a.shared_blob
+                                      : a.blobs + (int64_t)sl * a.blob_stride;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int mat = MODE == 0 ? j : 2;
@@ -140,13 +150,14 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   auto load_tile = [&](int se) __attribute__((always_inline)) {
     __syncthreads();  // every wave is done with the previous tile (and the list is in LDS)
     const int cnt = s.count[se - se0], off = s.offset[se - se0];
+    const bool shared = s.slot[se - se0] < 0;  // uniform
     if (tid < kTok) {
       int v = -1;
-      if (tid < cnt) v = a.fixed_blob ? tid : (MODE == 0 ? a.perm_tok[off + tid] : off + tid);
+      if (tid < cnt) v = (a.fixed_blob || shared) ? tid : (MODE == 0 ? a.perm_tok[off + tid] : off + tid);
       s.tok[tid] = v;
     }
     __syncthreads();
-    const uint16_t* src = MODE == 0 ? a.x : a.hbuf;
+    const uint16_t* src = MODE == 0 ? a.x : (shared ? a.shared_h : a.hbuf);
     // rows of the sub-tiles the MFMAs read; past the count they are zero
     const int rows = cnt > 16 ? kTok : 16;
     for (int c = tid; c < rows * (K / 8); c += kSW * kWave) {
@@ -215,6 +226,9 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
       // item done: lane holds D[token 16m + 4q + r][row n] of both weight sub-tiles
       const int nt = it - se * ntn;
       const int cnt = s.count[se - se0], off = s.offset[se - se0];
+      const bool shared = s.slot[se - se0] < 0;  // uniform
+      _Float16* hout = reinterpret_cast<_Float16*>(shared ? a.shared_h : a.hbuf);
+      float* yout = shared ? a.shared_y : a.ybuf;
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -225,10 +239,10 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
             if (MODE == 0) {
               const int row = nt * ROWS + wv * 16 + n;
               const float gv = acc[m][0][r], uv = acc[m][1][r];
-              reinterpret_cast<_Float16*>(a.hbuf)[pos * a.I + row] = (_Float16)swiglu(gv, uv);
+              hout[pos * a.I + row] = (_Float16)swiglu(gv, uv);
             } else {
 #pragma unroll
-              for (int j = 0; j < 2; ++j) a.ybuf[pos * a.H + nt * ROWS + wv * 32 + j * 16 + n] = acc[m][j][r];
+              for (int j = 0; j < 2; ++j) yout[pos * a.H + nt * ROWS + wv * 32 + j * 16 + n] = acc[m][j][r];
             }
           }
         }

@@ -81,6 +81,13 @@ struct ExpertArgs {
   int mfma_min;               // routed experts with count >= this are skipped (MFMA path)
   const ActiveExpert* small;  // routed experts with at most kStreamTokens tokens, below mfma_min
   const int32_t* n_small;
+  // streaming kernel, routed mode: the shared expert taken as one more list
+  // entry after the small experts (null: none); its tokens are 0..T-1 and its
+  // rows live in shared_h / shared_y
+  const uint8_t* shared_blob;
+  int shared_count;
+  uint16_t* shared_h;         // [T, I] fp16
+  float* shared_y;            // [T, H] fp32
 };
 void launch_gateup_gemv(const ExpertArgs& a, hipStream_t stream);
 // Persistent weight-streaming expert kernel (expert_stream.hip) for experts with

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict
 // LDS in wave order and written as the block's FP64 partial, together with
 // the squared norms of the token and expert rows over the same K range.
 //
-// router_select_kernel (one wave per token): adds the partials of the K
+// router_select_kernel (one block per token, one wave per 64 experts): adds the partials of the K
 // blocks in order and certifies each logit.  An output is reached through at
 // most KR / 2 roundings in each of its wave's two chains (one per product),
 // the addition of the two chains, 3 additions in the block and KB - 1 over
@@ -317,75 +317,65 @@ __global__ __launch_bounds__(kRmWaves * kWave) void router_partial_kernel(Router
   }
 }
 
-// grid T, block 64.  KV = ceil(E / 64) experts per lane (expert i*64 + lane).
+// grid T, block 64 * ceil(E / 64): wave w certifies experts 64w .. 64w + 63 of
+// the token, then wave 0 does softmax and top-k over all of them (KV =
+// ceil(E / 64) logits per lane there).
 template <int KV>
-__global__ __launch_bounds__(64) void router_select_kernel(RouterArgs a, const double* __restrict__ part,
-                                                           const double* __restrict__ nrm_x,
-                                                           const double* __restrict__ nrm_w, int KB, int KR) {
+__global__ __launch_bounds__(KV * 64) void router_select_kernel(RouterArgs a, const double* __restrict__ part,
+                                                                const double* __restrict__ nrm_x,
+                                                                const double* __restrict__ nrm_w, int KB, int KR) {
   __shared__ float slg[KV * kWave];
-  const int t = blockIdx.x, lane = threadIdx.x;
+  const int t = blockIdx.x, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int T = a.T, E = a.E;
+  const int e = wv * kWave + lane;
+  const int ec = min(e, E - 1);
   // every partial is loaded before any is added (at most kRmMaxKB of each)
-  double pv[kRmMaxKB];
+  double pv[kRmMaxKB], sv[kRmMaxKB], wn[kRmMaxKB];
 #pragma unroll
-  for (int kb = 0; kb < kRmMaxKB; ++kb) pv[kb] = kb < KB ? nrm_x[(int64_t)kb * T + t] : 0.0;
-  double nx = 0.0;
+  for (int kb = 0; kb < kRmMaxKB; ++kb) {
+    pv[kb] = kb < KB ? nrm_x[(int64_t)kb * T + t] : 0.0;
+    sv[kb] = kb < KB ? part[((int64_t)kb * T + t) * E + ec] : 0.0;
+    wn[kb] = kb < KB ? nrm_w[(int64_t)kb * E + ec] : 0.0;
+  }
+  double nx = 0.0, s = 0.0, nw = 0.0;
 #pragma unroll
   for (int kb = 0; kb < kRmMaxKB; ++kb)
-    if (kb < KB) nx += pv[kb];  // fixed order
-  uint64_t todo[KV];
-#pragma unroll
-  for (int i = 0; i < KV; ++i) {
-    const int e = i * kWave + lane;
-    const int ec = min(e, E - 1);
-    double sv[kRmMaxKB], wv[kRmMaxKB];
-#pragma unroll
-    for (int kb = 0; kb < kRmMaxKB; ++kb) {
-      sv[kb] = kb < KB ? part[((int64_t)kb * T + t) * E + ec] : 0.0;
-      wv[kb] = kb < KB ? nrm_w[(int64_t)kb * E + ec] : 0.0;
+    if (kb < KB) {  // fixed order
+      nx += pv[kb];
+      s += sv[kb];
+      nw += wn[kb];
     }
-    bool certified = false;
-    if (e < E) {
-      double s = 0.0, nw = 0.0;
-#pragma unroll
-      for (int kb = 0; kb < kRmMaxKB; ++kb)
-        if (kb < KB) {  // fixed order
-          s += sv[kb];
-          nw += wv[kb];
-        }
-      const float rr = (float)s;  // round to nearest even
-      if (rr != 0.0f && isfinite(rr) && isfinite(s)) {
-        const double bound = sqrt(nx) * sqrt(nw) * (1.0 + 0x1p-20);
-        const double eps = (double)(KR + KB + 4) * 0x1p-52 * bound;
-        const double rd = (double)rr;
-        const double m_lo = 0.5 * (rd + (double)nextafterf(rr, -INFINITY));
-        const double m_hi = 0.5 * (rd + (double)nextafterf(rr, INFINITY));
-        certified = s - eps > m_lo && s + eps < m_hi;
-      }
-      if (certified) slg[e] = rr;
+  bool certified = false;
+  if (e < E) {
+    const float rr = (float)s;  // round to nearest even
+    if (rr != 0.0f && isfinite(rr) && isfinite(s)) {
+      const double bound = sqrt(nx) * sqrt(nw) * (1.0 + 0x1p-20);
+      const double eps = (double)(KR + KB + 4) * 0x1p-52 * bound;
+      const double rd = (double)rr;
+      const double m_lo = 0.5 * (rd + (double)nextafterf(rr, -INFINITY));
+      const double m_hi = 0.5 * (rd + (double)nextafterf(rr, INFINITY));
+      certified = s - eps > m_lo && s + eps < m_hi;
     }
-    todo[i] = __ballot(e < E && !certified);
+    if (certified) slg[e] = rr;
   }
-  // compensated, then exact tier for the logits that were not certified
-#pragma unroll
-  for (int i = 0; i < KV; ++i) {
-    uint64_t m = todo[i];
-    while (m) {
-      const int e = i * kWave + __builtin_ctzll(m);
-      m &= m - 1;
-      const uint16_t* xr = a.x + (int64_t)t * a.H;
-      const uint16_t* wr = a.wr + (int64_t)e * a.H;
-      double nw = 0.0;
-      for (int kb = 0; kb < KB; ++kb) nw += nrm_w[(int64_t)kb * E + e];
-      bool ok;
-      float rr = compensated_dot_wave(xr, wr, a.H, lane, sqrt(nx) * sqrt(nw) * (1.0 + 0x1p-20), &ok);
-      if (!ok) rr = exact_dot_wave(xr, wr, a.H, lane);
-      if (lane == 0) slg[e] = rr;
-    }
+  // compensated, then exact tier for the wave's logits that were not certified
+  uint64_t m = __ballot(e < E && !certified);
+  const double bnd_x = sqrt(nx);
+  while (m) {
+    const int l = __builtin_ctzll(m);
+    m &= m - 1;
+    const int ee = wv * kWave + l;
+    const double nwe = __shfl(nw, l, kWave);
+    const uint16_t* xr = a.x + (int64_t)t * a.H;
+    const uint16_t* wr = a.wr + (int64_t)ee * a.H;
+    bool ok;
+    float rr = compensated_dot_wave(xr, wr, a.H, lane, bnd_x * sqrt(nwe) * (1.0 + 0x1p-20), &ok);
+    if (!ok) rr = exact_dot_wave(xr, wr, a.H, lane);
+    if (lane == 0) slg[ee] = rr;
   }
   __syncthreads();
-  for (int e = lane; e < E; e += kWave) a.logits[(int64_t)t * E + e] = slg[e];
-  topk_token<KV>(slg, t, E, a.k, a.renorm, a.forced, a.ids, a.w, a.err, lane);
+  if (e < E) a.logits[(int64_t)t * E + e] = slg[e];
+  if (wv == 0) topk_token<KV>(slg, t, E, a.k, a.renorm, a.forced, a.ids, a.w, a.err, lane);
 }
 
 // K per wave of the matrix-core router (0: the shape does not take it).
@@ -418,14 +408,17 @@ bool launch_router(const RouterArgs& a, double* scratch, hipStream_t stream) {
   else
     hipLaunchKernelGGL((router_partial_kernel<64>), g, dim3(kRmWaves * kWave), 0, stream, a, part, nrm_x, nrm_w);
   const int kv = (a.E + kWave - 1) / kWave;
+  const dim3 gs(a.T), bs(kWave * kv);
   if (kv == 1)
-    hipLaunchKernelGGL((router_select_kernel<1>), dim3(a.T), dim3(kWave), 0, stream, a, part, nrm_x, nrm_w, KB, kr);
-  else if (kv <= 2)
-    hipLaunchKernelGGL((router_select_kernel<2>), dim3(a.T), dim3(kWave), 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+    hipLaunchKernelGGL((router_select_kernel<1>), gs, bs, 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+  else if (kv == 2)
+    hipLaunchKernelGGL((router_select_kernel<2>), gs, bs, 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+  else if (kv <= 4)
+    hipLaunchKernelGGL((router_select_kernel<4>), gs, bs, 0, stream, a, part, nrm_x, nrm_w, KB, kr);
   else if (kv <= 8)
-    hipLaunchKernelGGL((router_select_kernel<8>), dim3(a.T), dim3(kWave), 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+    hipLaunchKernelGGL((router_select_kernel<8>), gs, bs, 0, stream, a, part, nrm_x, nrm_w, KB, kr);
   else
-    hipLaunchKernelGGL((router_select_kernel<16>), dim3(a.T), dim3(kWave), 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+    hipLaunchKernelGGL((router_select_kernel<16>), gs, bs, 0, stream, a, part, nrm_x, nrm_w, KB, kr);
   return true;
 }
 
