@@ -382,3 +382,93 @@ class CacheSim:
             if self.policy == LRU_FREQ and self.misses % (2 * self.capacity) == 0:
                 self.sfreq = [f * 0.75 for f in self.sfreq]
         return [self.slot_of[int(e)] for e in group]
+
+
+# ----------------------------------------------------------------------------
+# Offline policy analysis over routing traces ([F51] "The simulator": captured
+# router traces are replayed through candidate cache policies offline and the
+# hit rate reported per capacity; [MS] "What the numbers say": LRU and LFU hit
+# rates at a fixed cache size; [F51] "Layer 1 - expert persistence cache":
+# the static top-50% share).  A trace is a list of routed groups (one per
+# step) of one layer.
+#
+# Readings (the pages name the analyses, not their definitions):
+#  * OPT is Belady's rule carried over to groups: every expert of the step's
+#    group must be resident at once; a miss fills the lowest free slot, else
+#    evicts the resident expert outside the group whose next use (first later
+#    step naming it) is farthest away, never-used-again counting as infinitely
+#    far, ties to the lowest id.  It is pinned against brute force over every
+#    eviction choice on tiny traces.
+#  * skew: share of all selections that fall on the most-selected ceil(p*E)
+#    experts (ties to the lower id) for p = 10%, 20%, 30%; entropy in bits of
+#    the selection frequencies; coverage(C) = that share for the top C experts,
+#    which is the hit rate a static pin of those C experts would get.
+# ----------------------------------------------------------------------------
+
+
+def opt_hits(groups, capacity: int):
+    """(hits, misses) of Belady's farthest-next-use rule over a group trace."""
+    gs = [sorted(set(int(e) for e in g)) for g in groups]
+    resident = set()
+    hits = misses = 0
+
+    def next_use(x, t):
+        for u in range(t + 1, len(gs)):
+            if x in gs[u]:
+                return u
+        return math.inf
+
+    for t, g in enumerate(gs):
+        if len(g) > capacity:
+            raise ValueError("group larger than capacity")
+        for e in g:
+            if e in resident:
+                hits += 1
+        for e in g:
+            if e in resident:
+                continue
+            misses += 1
+            if len(resident) >= capacity:
+                cands = [x for x in resident if x not in g]
+                victim = min(cands, key=lambda x: (-next_use(x, t), x))
+                resident.remove(victim)
+            resident.add(e)
+    return hits, misses
+
+
+def policy_hits(policy: str, groups, n_experts: int, capacity: int):
+    """(hits, misses) of one online policy (CacheSim) over a group trace."""
+    sim = CacheSim(policy, n_experts, capacity)
+    for step, g in enumerate(groups):
+        sim.ensure(g, step)
+    return sim.hits, sim.misses
+
+
+def selection_counts(groups, n_experts: int) -> np.ndarray:
+    c = np.zeros(n_experts, dtype=np.int64)
+    for g in groups:
+        for e in set(int(x) for x in g):
+            c[e] += 1
+    return c
+
+
+def top_share(counts: np.ndarray, n_top: int) -> float:
+    """Share of all selections on the n_top most-selected experts (ties to the lower id)."""
+    order = sorted(range(len(counts)), key=lambda e: (-int(counts[e]), e))
+    total = int(counts.sum())
+    return float(sum(int(counts[e]) for e in order[:n_top])) / total if total else 0.0
+
+
+def skew_report(groups, n_experts: int) -> dict:
+    c = selection_counts(groups, n_experts)
+    total = int(c.sum())
+    ent = 0.0
+    for v in c:
+        if v:
+            p = float(v) / total
+            ent -= p * math.log2(p)
+    return {"top10": top_share(c, math.ceil(0.1 * n_experts)),
+            "top20": top_share(c, math.ceil(0.2 * n_experts)),
+            "top30": top_share(c, math.ceil(0.3 * n_experts)),
+            "entropy_bits": ent,
+            "distinct": int((c > 0).sum())}

@@ -416,3 +416,84 @@ def test_group_larger_than_capacity_rejected():
     sim = ora.CacheSim(ora.LRU, 16, 2)
     with pytest.raises(ValueError):
         sim.ensure([1, 2, 3])
+
+
+# ---------------------------------------------------------------------------
+# Offline policy analysis: OPT bound and router skew
+# ---------------------------------------------------------------------------
+
+def _brute_max_hits(groups, C):
+    """Largest hit count over every eviction choice (free slots always used first)."""
+    from functools import lru_cache
+    gs = [tuple(sorted(set(g))) for g in groups]
+
+    @lru_cache(maxsize=None)
+    def go(t, res):
+        if t == len(gs):
+            return 0
+        g = gs[t]
+        hits = sum(1 for e in g if e in res)
+        missing = [e for e in g if e not in res]
+
+        def place(i, cur):
+            if i == len(missing):
+                return go(t + 1, cur)
+            e = missing[i]
+            if len(cur) < C:
+                return place(i + 1, cur | frozenset([e]))
+            best = -1
+            for v in cur:
+                if v not in g:
+                    best = max(best, place(i + 1, (cur - frozenset([v])) | frozenset([e])))
+            return best
+
+        return hits + place(0, res)
+
+    return go(0, frozenset())
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_opt_equals_brute_force_on_tiny_traces(seed):
+    rng = np.random.default_rng(100 + seed)
+    E, C, steps = 6, 2 + seed % 2, 9
+    groups = [rng.choice(E, size=int(rng.integers(1, C + 1)), replace=False).tolist() for _ in range(steps)]
+    h, m = ora.opt_hits(groups, C)
+    assert h == _brute_max_hits(groups, C)
+    assert h + m == sum(len(g) for g in groups)
+
+
+@pytest.mark.parametrize("C", [16, 32, 48])
+def test_online_policies_never_beat_opt_on_group_traces(C):
+    tr = fx.zipf_trace("pin-opt", 200, 1, 64, 8)
+    groups = [tr[s, 0].tolist() for s in range(tr.shape[0])]
+    oh, om = ora.opt_hits(groups, C)
+    for policy in (ora.LRU, ora.LFU, ora.LRU_FREQ):
+        h, m = ora.policy_hits(policy, groups, 64, C)
+        assert h <= oh and h + m == oh + om
+
+
+def test_opt_working_set_within_capacity_misses_once():
+    rng = np.random.default_rng(5)
+    ws = rng.choice(64, size=10, replace=False)
+    groups = [rng.choice(ws, size=4, replace=False).tolist() for _ in range(40)]
+    _, m = ora.opt_hits(groups, 10)
+    assert m == len(set(np.concatenate(groups).tolist()))
+
+
+def test_skew_closed_forms():
+    E = 20
+    uniform = [[e] for e in range(E)] * 3          # every expert equally often
+    r = ora.skew_report(uniform, E)
+    assert r["entropy_bits"] == pytest.approx(np.log2(E), abs=1e-12)
+    assert r["top10"] == pytest.approx(2 / E) and r["top30"] == pytest.approx(6 / E)
+    assert r["distinct"] == E
+    single = [[7]] * 5
+    r = ora.skew_report(single, E)
+    assert r["entropy_bits"] == 0.0 and r["top10"] == 1.0 and r["distinct"] == 1
+    # counts 3, 1 over E = 10: top-10% (1 expert) = 3/4, entropy of (3/4, 1/4)
+    r = ora.skew_report([[2], [2], [2], [5]], 10)
+    assert r["top10"] == pytest.approx(0.75)
+    assert r["entropy_bits"] == pytest.approx(-(0.75 * np.log2(0.75) + 0.25 * np.log2(0.25)), abs=1e-12)
+    # a tie for the top place goes to the lower id
+    c = np.array([0, 4, 0, 4, 1])
+    assert ora.top_share(c, 1) == pytest.approx(4 / 9)

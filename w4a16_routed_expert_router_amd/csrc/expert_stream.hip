@@ -158,29 +158,44 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
     }
     __syncthreads();
     const uint16_t* src = MODE == 0 ? a.x : (shared ? a.shared_h : a.hbuf);
-    // rows of the sub-tiles the MFMAs read; past the count they are zero
+    // rows of the sub-tiles the MFMAs read; past the count they are zero.
+    // Each thread loads a batch of four 16-byte chunks before it stores any,
+    // so a tile costs at most four memory round trips.
     const int rows = cnt > 16 ? kTok : 16;
-    for (int c = tid; c < rows * (K / 8); c += kSW * kWave) {
-      const int r = c / (K / 8), col = (c - r * (K / 8)) * 8;
-      u4 v = u4{0u, 0u, 0u, 0u};
-      if (r < cnt) {
-        const int t = s.tok[r];
-        // gate/up reads token rows of x; down reads the rows of hbuf at the
-        // expert's positions (the shared expert: positions offset + t)
-        const int64_t src_row = MODE == 0 ? (int64_t)t : (a.fixed_blob ? (int64_t)off + t : (int64_t)t);
-        v = *reinterpret_cast<const u4*>(src + src_row * K + col);
+    constexpr int kB = 4;  // chunks per thread and batch
+    for (int c0 = 0; c0 < rows * (K / 8); c0 += kB * kSW * kWave) {
+      u4 v[kB];
+#pragma unroll
+      for (int i = 0; i < kB; ++i) {
+        const int c = c0 + i * kSW * kWave + tid;
+        const int r = c / (K / 8), col = (c - r * (K / 8)) * 8;
+        v[i] = u4{0u, 0u, 0u, 0u};
+        if (r < cnt) {
+          const int t = s.tok[r];
+          // gate/up reads token rows of x; down reads the rows of hbuf at the
+          // expert's positions (the shared expert: positions offset + t)
+          const int64_t src_row = MODE == 0 ? (int64_t)t : (a.fixed_blob ? (int64_t)off + t : (int64_t)t);
+          v[i] = *reinterpret_cast<const u4*>(src + src_row * K + col);
+        }
       }
-      *reinterpret_cast<u4*>(&s.a[r * LD + col]) = v;
+#pragma unroll
+      for (int i = 0; i < kB; ++i) {
+        const int c = c0 + i * kSW * kWave + tid;
+        const int r = c / (K / 8), col = (c - r * (K / 8)) * 8;
+        if (r < rows) *reinterpret_cast<u4*>(&s.a[r * LD + col]) = v[i];
+      }
     }
     __syncthreads();
     cur = se;
     two = cnt > 16;
   };
-  // the first expert's tile is loaded before the weight stream starts: its
-  // loads would otherwise queue behind (and wait for) the ring's
-  load_tile(se0);
+  // the weight stream starts as soon as the block's list is in LDS; the first
+  // expert's tile is loaded while it is in flight (its data arrives with the
+  // ring's first units, which the first step needs anyway)
+  __syncthreads();
 #pragma unroll
   for (int u = 0; u < kRing - 1; ++u) load_unit(min(u, nv - 1), u);
+  load_tile(se0);
 
   f4 acc[2][2];  // [sub-tile][weight sub-tile]
 #pragma unroll
