@@ -266,6 +266,48 @@ def extra_pool(moe, fx, dev, stream, steps=256, layers=16):
     return res
 
 
+def extra_trace_analysis(moe, fx, steps=256):
+    """Offline policy sweep over seeded Zipf(1.1) routing traces (host engine of the
+    library): per capacity C the hit rates of LRU / LFU / LRU-FREQ and of Belady's
+    OPT for groups, the gap to OPT, H2D copies per token, and the hit rate of a
+    static pin of the C most-selected experts; per trace the top-10/20/30 % shares
+    and the entropy of the selection frequencies (means over layers)."""
+    import numpy as np
+    res = {}
+    for name, shape, layers, caps in (("olmoe16", fx.OLMOE, 16, (16, 32, 48, 64)),
+                                      ("qwen_next_like48", fx.QWEN_NEXT, 48, (16, 32, 64, 128, 256))):
+        E, k = shape.n_experts, shape.top_k
+        tr = fx.zipf_trace("bench-pool-zipf" if name == "olmoe16" else "bench-qwen-zipf",
+                           steps, layers, E, k, s=1.1)
+        accesses = steps * layers * k
+        sk = [moe.trace_skew(tr[:, l, :], E) for l in range(layers)]
+        out = {"steps": steps, "layers": layers, "experts": E, "top_k": k,
+               "skew": {key: round(float(np.mean([r[key] for r in sk])), 4)
+                        for key in ("top10", "top20", "top30", "entropy_bits")}}
+        out["skew"]["entropy_uniform_bits"] = round(float(np.log2(E)), 4)
+        for C in caps:
+            row = {}
+            tot = {}
+            for pol in ("lru", "lfu", "lru_freq", "opt"):
+                h = m = 0
+                for l in range(layers):
+                    hh, mm = (moe.trace_opt(tr[:, l, :], E, C) if pol == "opt"
+                              else moe.trace_policy(pol, tr[:, l, :], E, C))
+                    h += hh
+                    m += mm
+                tot[pol] = (h, m)
+                row[f"{pol}_hit_rate"] = round(h / accesses, 4)
+            for pol in ("lru", "lfu", "lru_freq"):
+                row[f"{pol}_gap_to_opt"] = round((tot["opt"][0] - tot[pol][0]) / accesses, 4)
+                row[f"{pol}_h2d_copies_per_token"] = round(tot[pol][1] / steps, 2)
+            row["opt_h2d_copies_per_token"] = round(tot["opt"][1] / steps, 2)
+            row["static_pin_hit_rate"] = round(float(np.mean(
+                [moe.trace_top_share(tr[:, l, :], E, C) for l in range(layers)])), 4)
+            out[f"C{C}"] = row
+        res[name] = out
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -414,6 +456,8 @@ def main():
         print(f"[bench] qwen extras done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
         extra["partial_residency_olmoe16"] = extra_pool(moe, fx, dev, stream)
         print(f"[bench] pool extras done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
+        extra["policy_sweep_zipf"] = extra_trace_analysis(moe, fx)
+        print(f"[bench] policy sweep done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
         out["extra"] = extra
     if not args.no_cpu_baseline:
         h0_np = [h0[i].cpu().numpy().astype(np.float16) for i in range(N_INPUTS)]

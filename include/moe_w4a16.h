@@ -306,6 +306,44 @@ moe_status moe_policy_access(moe_policy_engine* p, const int32_t* experts, int32
 int32_t moe_policy_event_count(const moe_policy_engine* p);
 int32_t moe_policy_events(const moe_policy_engine* p, moe_cache_event* buf, int32_t cap);
 
+/* ---- offline routing-trace analysis (host only, no device needed) -------------
+ * Captured router traces replayed through cache policies offline, hit rate per
+ * capacity ("F51 Nitro / Nitro-MoE", "The simulator"); LRU against LFU at a fixed
+ * cache size ("An expert-offloading engine, from scratch", "What the numbers
+ * say"); the share a static pin of the most popular experts serves ("F51 Nitro /
+ * Nitro-MoE", "Layer 1 - expert persistence cache").
+ *
+ * A trace is one layer's routed groups: `ids` host int32 row-major
+ * [n_steps, width], read only, owned by the caller.  An entry < 0 is padding; an
+ * expert named twice in one row counts once; an entry >= n_experts is
+ * MOE_E_ARG.  Nothing is kept after the call returns. */
+
+/* Belady's rule for groups: every expert of a step's group must be resident at
+ * once; a miss takes a free slot, else evicts the resident expert outside the
+ * group whose next use is farthest (never again = infinitely far; ties to the
+ * lower id).  Hits of a step are counted before its misses are filled.
+ * hits/misses out.  MOE_E_CAPACITY when a group has more than `capacity`
+ * distinct experts. */
+moe_status moe_trace_opt(const int32_t* ids, int32_t n_steps, int32_t width, int32_t n_experts,
+                         int32_t capacity, int64_t* hits, int64_t* misses);
+/* The online policy (MOE_POLICY_LRU / _LFU / _LRU_FREQ) of moe_cache_ensure,
+ * one access per row (the same engine as moe_policy_access). */
+moe_status moe_trace_policy(int32_t policy, const int32_t* ids, int32_t n_steps, int32_t width,
+                            int32_t n_experts, int32_t capacity, int64_t* hits, int64_t* misses);
+/* Share of all selections (selection = a row naming an expert) that fall on the
+ * n_top most-selected experts, ties to the lower id: the hit rate of a static
+ * pin of those experts.  0 for an empty trace. */
+moe_status moe_trace_top_share(const int32_t* ids, int32_t n_steps, int32_t width, int32_t n_experts,
+                               int32_t n_top, double* share);
+typedef struct moe_skew_report {
+  double top10, top20, top30;  /* top shares of ceil(p*E) experts, p = 10/20/30 %   */
+  double entropy_bits;         /* entropy of the selection frequencies (log2)       */
+  int32_t distinct;            /* experts selected at least once                    */
+  int64_t selections;          /* all selections                                    */
+} moe_skew_report;
+moe_status moe_trace_skew(const int32_t* ids, int32_t n_steps, int32_t width, int32_t n_experts,
+                          moe_skew_report* out);
+
 #ifdef __cplusplus
 }
 #endif

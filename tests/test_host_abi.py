@@ -93,3 +93,86 @@ def test_policy_engine_rejects_bad_groups():
         with pytest.raises(MoEError):
             eng.access(g)
     assert eng.events() == []
+
+
+# ---- offline routing-trace analysis: native engine against the oracle -----------
+
+def _oracle_groups(trace):
+    """Rows of a [steps, width] trace as the oracle takes them: padding (< 0)
+    dropped, repeats named once."""
+    return [sorted(set(int(e) for e in row if e >= 0)) for row in trace]
+
+
+def _mixed_trace(seed, steps, width, n_experts, pad_frac=0.15):
+    rng = np.random.default_rng(seed)
+    hot = rng.permutation(n_experts)[: max(2, n_experts // 4)]
+    t = np.where(rng.random((steps, width)) < 0.6, rng.choice(hot, size=(steps, width)),
+                 rng.integers(0, n_experts, size=(steps, width)))
+    t[rng.random((steps, width)) < pad_frac] = -1
+    return t.astype(np.int32)
+
+
+@pytest.mark.parametrize("C", [8, 16, 32])
+def test_trace_opt_and_policies_match_oracle_on_zipf_trace(C):
+    import w4a16_routed_expert_router_amd as moe
+    tr = fx.zipf_trace("abi-trace", 96, 2, 64, 8)
+    for layer in range(2):
+        rows = tr[:, layer, :]
+        groups = _oracle_groups(rows)
+        assert moe.trace_opt(rows, 64, C) == ora.opt_hits(groups, C)
+        for pol in ("lru", "lfu", "lru_freq"):
+            got = moe.trace_policy(pol, rows, 64, C)
+            assert got == ora.policy_hits(pol, groups, 64, C)
+            assert got[0] <= moe.trace_opt(rows, 64, C)[0]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_trace_analysis_matches_oracle_with_padding_and_repeats(seed):
+    import w4a16_routed_expert_router_amd as moe
+    E, width = 24, 6
+    rows = _mixed_trace(seed, 80, width, E)
+    groups = _oracle_groups(rows)
+    for C in (width, 9, 16):
+        assert moe.trace_opt(rows, E, C) == ora.opt_hits(groups, C)
+        for pol in ("lru", "lfu", "lru_freq"):
+            assert moe.trace_policy(pol, rows, E, C) == ora.policy_hits(pol, groups, E, C)
+    for n_top in (0, 1, 3, E, E + 5):
+        assert moe.trace_top_share(rows, E, n_top) == ora.top_share(ora.selection_counts(groups, E), n_top)
+    got = moe.trace_skew(rows, E)
+    want = ora.skew_report(groups, E)
+    for key in ("top10", "top20", "top30"):
+        assert got[key] == want[key]
+    assert got["distinct"] == want["distinct"]
+    assert got["selections"] == int(ora.selection_counts(groups, E).sum())
+    assert abs(got["entropy_bits"] - want["entropy_bits"]) <= 1e-12 * max(1.0, want["entropy_bits"])
+
+
+def test_trace_skew_matches_oracle_on_qwen_like_zipf_trace():
+    import w4a16_routed_expert_router_amd as moe
+    tr = fx.zipf_trace("abi-trace-qwen", 64, 1, 512, 10)[:, 0, :]
+    groups = _oracle_groups(tr)
+    got, want = moe.trace_skew(tr, 512), ora.skew_report(groups, 512)
+    for key in ("top10", "top20", "top30", "distinct"):
+        assert got[key] == want[key]
+    assert abs(got["entropy_bits"] - want["entropy_bits"]) <= 1e-12 * want["entropy_bits"]
+    assert moe.trace_opt(tr, 512, 40) == ora.opt_hits(groups, 40)
+
+
+def test_trace_analysis_rejects_bad_traces():
+    import w4a16_routed_expert_router_amd as moe
+    from w4a16_routed_expert_router_amd import MoEError, capi
+    rows = np.array([[0, 1, 2], [3, 4, 5]], dtype=np.int32)
+    with pytest.raises(MoEError) as e:
+        moe.trace_opt(rows, 5, 4)                 # id 5 out of range
+    assert e.value.status == capi.MOE_E_ARG
+    with pytest.raises(MoEError) as e:
+        moe.trace_opt(rows, 8, 2)                 # a group of 3 in 2 slots
+    assert e.value.status == capi.MOE_E_CAPACITY
+    with pytest.raises(MoEError) as e:
+        moe.trace_policy("lru", rows, 8, 2)
+    assert e.value.status == capi.MOE_E_CAPACITY
+    # an empty trace: nothing selected, no hits or misses
+    empty = np.full((3, 4), -1, dtype=np.int32)
+    assert moe.trace_opt(empty, 8, 1) == (0, 0)
+    assert moe.trace_top_share(empty, 8, 2) == 0.0
+    assert moe.trace_skew(empty, 8)["selections"] == 0

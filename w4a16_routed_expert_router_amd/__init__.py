@@ -240,3 +240,58 @@ class PolicyEngine:
         if getattr(self, "_h", None):
             self._free(self._h)
             self._h = None
+
+
+# ---- offline routing-trace analysis (host only) ---------------------------------
+
+def _trace(ids):
+    a = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    if a.ndim == 1:
+        a = a.reshape(-1, 1)
+    if a.ndim != 2:
+        raise ValueError("a trace is [n_steps, width]")
+    return a
+
+
+def trace_opt(ids, n_experts, capacity):
+    """(hits, misses) of Belady's rule for groups over one layer's trace."""
+    a = _trace(ids)
+    h, m = C.c_int64(), C.c_int64()
+    st = _lib.moe_trace_opt(a.ctypes.data, a.shape[0], a.shape[1], n_experts, capacity,
+                            C.byref(h), C.byref(m))
+    if st != capi.MOE_OK:
+        raise MoEError(st, "trace_opt rejected the trace")
+    return h.value, m.value
+
+
+def trace_policy(policy, ids, n_experts, capacity):
+    """(hits, misses) of an online slot-pool policy replayed over one layer's trace."""
+    a = _trace(ids)
+    p = POLICIES[policy] if isinstance(policy, str) else int(policy)
+    h, m = C.c_int64(), C.c_int64()
+    st = _lib.moe_trace_policy(p, a.ctypes.data, a.shape[0], a.shape[1], n_experts, capacity,
+                               C.byref(h), C.byref(m))
+    if st != capi.MOE_OK:
+        raise MoEError(st, "trace_policy rejected the trace")
+    return h.value, m.value
+
+
+def trace_top_share(ids, n_experts, n_top):
+    """Share of selections on the n_top most-selected experts (static-pin hit rate)."""
+    a = _trace(ids)
+    v = C.c_double()
+    st = _lib.moe_trace_top_share(a.ctypes.data, a.shape[0], a.shape[1], n_experts, n_top, C.byref(v))
+    if st != capi.MOE_OK:
+        raise MoEError(st, "trace_top_share rejected the trace")
+    return v.value
+
+
+def trace_skew(ids, n_experts):
+    """Top-10/20/30 % shares, entropy (bits), distinct experts and selections of a trace."""
+    a = _trace(ids)
+    r = capi.moe_skew_report()
+    st = _lib.moe_trace_skew(a.ctypes.data, a.shape[0], a.shape[1], n_experts, C.byref(r))
+    if st != capi.MOE_OK:
+        raise MoEError(st, "trace_skew rejected the trace")
+    return {"top10": r.top10, "top20": r.top20, "top30": r.top30, "entropy_bits": r.entropy_bits,
+            "distinct": r.distinct, "selections": r.selections}

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_w4a16.so")
 
 SOURCES = ["api.hip", "router.hip", "group.hip", "expert_gemv.hip", "expert_mfma.hip", "expert_stream.hip",
-           "decode_fused.hip", "policy.cpp"]
+           "decode_fused.hip", "policy.cpp", "trace_analysis.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",
@@ -43,7 +43,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, "-shared", "-o", tmp,
            "-I", os.path.join(ROOT, "include"), *srcs, "-lpthread"]
-    # policy.cpp has no device code; hipcc compiles it as host C++.
+    # policy.cpp and trace_analysis.cpp have no device code; hipcc compiles them as host C++.
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

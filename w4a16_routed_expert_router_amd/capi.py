@@ -39,6 +39,11 @@ class moe_cache_counters(C.Structure):
                 ("failures", C.c_uint64), ("h2d_seconds", C.c_double)]
 
 
+class moe_skew_report(C.Structure):
+    _fields_ = [("top10", C.c_double), ("top20", C.c_double), ("top30", C.c_double),
+                ("entropy_bits", C.c_double), ("distinct", C.c_int32), ("selections", C.c_int64)]
+
+
 class moe_cache_event(C.Structure):
     _fields_ = [("step", C.c_int32), ("layer", C.c_int32), ("expert", C.c_int32),
                 ("hit", C.c_int32), ("slot", C.c_int32), ("victim", C.c_int32)]
@@ -71,6 +76,10 @@ SIGNATURES = {
     "moe_policy_access": (_I, [_P, _P, _I, _I, _P]),
     "moe_policy_event_count": (_I, [_P]),
     "moe_policy_events": (_I, [_P, C.POINTER(moe_cache_event), _I]),
+    "moe_trace_opt": (_I, [_P, _I, _I, _I, _I, C.POINTER(C.c_int64), C.POINTER(C.c_int64)]),
+    "moe_trace_policy": (_I, [_I, _P, _I, _I, _I, _I, C.POINTER(C.c_int64), C.POINTER(C.c_int64)]),
+    "moe_trace_top_share": (_I, [_P, _I, _I, _I, _I, C.POINTER(C.c_double)]),
+    "moe_trace_skew": (_I, [_P, _I, _I, _I, C.POINTER(moe_skew_report)]),
 }
 
 _lib = None
