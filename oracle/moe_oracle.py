@@ -296,9 +296,27 @@ def stack_forward(h0: np.ndarray, layers: list, shape, forced_ids=None) -> dict:
 #        LRU-FREQ  (sfreq*1000 - (clock - last), id), sfreq = 1 on fill,
 #                  +1 per hit, float64
 #  * LRU-FREQ: after every 2*C misses of the layer, all sfreq *= 0.75.
+#
+# Next-layer prefetch ([MS] "What the numbers say" and "Method": the next
+# layer's experts are guessed by running that layer's router on the current
+# state and their copies start while the current layer computes; a guess that
+# is used saves its copy, one that is not costs a transfer and a slot, and
+# nothing may change the outputs).  Readings:
+#  * prefetch(guess) neither ticks the clock nor counts as a use: experts of
+#    the guess that are resident are left untouched;
+#  * each guessed expert that is not resident (ascending id) is filled like a
+#    miss -- lowest free slot, else the minimum-key resident expert outside
+#    the guess -- with last = the current clock, its LFU count unchanged,
+#    sfreq = 1; it is "pending" until an ensure() names it;
+#  * prefetch fills are not misses (they do not advance the LRU-FREQ decay);
+#  * an ensure() that names a pending expert counts a hit and marks the first
+#    use of the prefetched copy.
+# Event codes (the `hit` field): 0 miss, 1 hit, 2 prefetch fill, 3 hit on a
+# prefetched copy (its first use).
 # ----------------------------------------------------------------------------
 
 LRU, LFU, LRU_FREQ = "lru", "lfu", "lru_freq"
+EV_MISS, EV_HIT, EV_PREFETCH, EV_PREFETCH_HIT = 0, 1, 2, 3
 
 
 @dataclass
@@ -306,7 +324,7 @@ class CacheEvent:
     step: int
     layer: int
     expert: int
-    hit: bool
+    hit: int             # EV_MISS, EV_HIT, EV_PREFETCH or EV_PREFETCH_HIT
     slot: int
     victim: int          # evicted expert, -1 if none
 
@@ -329,6 +347,9 @@ class CacheSim:
     count: dict = field(default_factory=dict)
     sfreq: list = field(default_factory=list)
     events: list = field(default_factory=list)
+    pending: set = field(default_factory=set)        # prefetched, not yet named by ensure()
+    prefetches: int = 0
+    prefetch_used: int = 0
 
     def __post_init__(self):
         assert self.policy in (LRU, LFU, LRU_FREQ)
@@ -360,7 +381,12 @@ class CacheSim:
                 self.count[e] = self.count.get(e, 0) + 1
                 self.sfreq[s] += 1.0
                 self.hits += 1
-                self.events.append(CacheEvent(step, self.layer, e, True, s, -1))
+                code = EV_HIT
+                if e in self.pending:
+                    self.pending.discard(e)
+                    self.prefetch_used += 1
+                    code = EV_PREFETCH_HIT
+                self.events.append(CacheEvent(step, self.layer, e, code, s, -1))
         for e in g:
             if e in self.slot_of:
                 continue
@@ -372,16 +398,47 @@ class CacheSim:
                 cands = [x for x in self.slot_of if x not in in_group]
                 victim = min(cands, key=self._key)
                 s = self.slot_of.pop(victim)
+                self.pending.discard(victim)
             self.expert_in[s] = e
             self.slot_of[e] = s
             self.last[e] = self.clock
             self.count[e] = self.count.get(e, 0) + 1
             self.sfreq[s] = 1.0
             self.misses += 1
-            self.events.append(CacheEvent(step, self.layer, e, False, s, victim))
+            self.events.append(CacheEvent(step, self.layer, e, EV_MISS, s, victim))
             if self.policy == LRU_FREQ and self.misses % (2 * self.capacity) == 0:
                 self.sfreq = [f * 0.75 for f in self.sfreq]
         return [self.slot_of[int(e)] for e in group]
+
+    def prefetch(self, group, step: int = 0) -> None:
+        """Speculative fill of the guessed experts that are not resident (no
+        clock tick, no use); appends one EV_PREFETCH event per fill."""
+        g = sorted(set(int(e) for e in group))
+        if len(g) != len(list(group)):
+            raise ValueError("group has repeated experts")
+        if len(g) > self.capacity:
+            raise ValueError("group larger than capacity")
+        in_group = set(g)
+        for e in g:
+            if e in self.slot_of:
+                continue
+            victim = -1
+            free = [s for s in range(self.capacity) if self.expert_in[s] < 0]
+            if free:
+                s = free[0]
+            else:
+                cands = [x for x in self.slot_of if x not in in_group]
+                victim = min(cands, key=self._key)
+                s = self.slot_of.pop(victim)
+                self.pending.discard(victim)
+            self.expert_in[s] = e
+            self.slot_of[e] = s
+            self.last[e] = self.clock
+            self.count[e] = self.count.get(e, 0)
+            self.sfreq[s] = 1.0
+            self.pending.add(e)
+            self.prefetches += 1
+            self.events.append(CacheEvent(step, self.layer, e, EV_PREFETCH, s, victim))
 
 
 # ----------------------------------------------------------------------------

@@ -497,3 +497,83 @@ def test_skew_closed_forms():
     # a tie for the top place goes to the lower id
     c = np.array([0, 4, 0, 4, 1])
     assert ora.top_share(c, 1) == pytest.approx(4 / 9)
+
+
+# ---- next-layer prefetch in the slot-pool simulator (hand-worked traces) ----------
+
+def _ev(sim):
+    return [(e.step, e.expert, int(e.hit), e.slot, e.victim) for e in sim.events]
+
+
+def test_prefetch_lru_hand_worked_trace():
+    # C=3, LRU.  step 0 fills 1, 2; a guess {2, 5} fills only 5 (2 is resident,
+    # untouched); step 1 uses 5 (first use of a prefetched copy) and misses 3,
+    # evicting 1 (last 1, lower id than 2); a guess {4} evicts 2 (last 1);
+    # step 2 hits 3 and misses 2, evicting the unused prefetched 4 (last 1)
+    # rather than 5 (last 2).
+    sim = ora.CacheSim(ora.LRU, 8, 3)
+    sim.ensure([1, 2], step=0)
+    sim.prefetch([2, 5], step=1)
+    sim.ensure([3, 5], step=1)
+    sim.prefetch([4], step=2)
+    sim.ensure([2, 3], step=2)
+    M, H, PF, PH = ora.EV_MISS, ora.EV_HIT, ora.EV_PREFETCH, ora.EV_PREFETCH_HIT
+    assert _ev(sim) == [(0, 1, M, 0, -1), (0, 2, M, 1, -1), (1, 5, PF, 2, -1), (1, 5, PH, 2, -1),
+                        (1, 3, M, 0, 1), (2, 4, PF, 1, 2), (2, 3, H, 0, -1), (2, 2, M, 1, 4)]
+    assert (sim.hits, sim.misses, sim.prefetches, sim.prefetch_used) == (2, 4, 2, 1)
+    assert sim.pending == set()
+
+
+def test_prefetch_is_not_a_use_for_lfu():
+    # 1 was used once; 3 is prefetched and never used: its count stays 0, so the
+    # next miss evicts 3, not 1 (had the prefetch counted, keys would tie on
+    # (count 1, last 1) and the lower id 1 would go)
+    sim = ora.CacheSim(ora.LFU, 8, 2)
+    sim.ensure([1], step=0)
+    sim.prefetch([3], step=1)
+    sim.ensure([4], step=1)
+    assert _ev(sim)[-1] == (1, 4, ora.EV_MISS, 1, 3)
+
+
+def test_prefetch_fills_do_not_advance_lru_freq_decay():
+    # C=2: the decay comes after every 4 misses.  A prefetch of 0, then misses
+    # 1, 2, 3, 4 (hit on 0 in between): the decay runs right after the 4th
+    # miss, so sfreq = [2 * 0.75, 1 * 0.75]; counting the prefetch as a miss
+    # would have decayed after miss 3 and left [1.5, 1.0].
+    sim = ora.CacheSim(ora.LRU_FREQ, 8, 2)
+    sim.prefetch([0], step=0)
+    sim.ensure([1], step=0)
+    sim.ensure([0], step=1)
+    sim.ensure([2], step=2)
+    sim.ensure([3], step=3)
+    sim.ensure([4], step=4)
+    assert [e.victim for e in sim.events if e.hit == ora.EV_MISS] == [-1, 1, 2, 3]
+    assert sim.sfreq == [1.5, 0.75]
+    assert sim.misses == 4 and sim.prefetches == 1 and sim.prefetch_used == 1
+
+
+@pytest.mark.parametrize("policy", [ora.LRU, ora.LFU, ora.LRU_FREQ])
+def test_prefetch_of_the_exact_next_group_leaves_no_demand_miss(policy):
+    # after prefetch(G) every expert of G is resident (a fill never evicts a
+    # member of the guess), so ensure(G) right after it has no miss and uses
+    # every prefetched copy
+    trace = fx.zipf_trace("pin-prefetch", 60, 1, 32, 6)[:, 0, :]
+    sim = ora.CacheSim(policy, 32, 8)
+    sim.ensure(trace[0], step=0)
+    first = sim.misses
+    for t in range(1, len(trace)):
+        sim.prefetch(trace[t], step=t)
+        sim.ensure(trace[t], step=t)
+    assert sim.misses == first
+    assert sim.prefetch_used == sim.prefetches
+
+
+@pytest.mark.parametrize("policy", [ora.LRU, ora.LFU, ora.LRU_FREQ])
+def test_empty_prefetch_changes_nothing(policy):
+    trace = fx.zipf_trace("pin-prefetch-empty", 40, 1, 24, 5)[:, 0, :]
+    a, b = ora.CacheSim(policy, 24, 7), ora.CacheSim(policy, 24, 7)
+    for t, g in enumerate(trace):
+        a.ensure(g, step=t)
+        b.prefetch([], step=t)
+        b.ensure(g, step=t)
+    assert _ev(a) == _ev(b)
