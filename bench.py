@@ -266,6 +266,52 @@ def extra_pool(moe, fx, dev, stream, steps=256, layers=16):
     return res
 
 
+def extra_prefetch(moe, fx, dev, stream, steps=64, layers=16):
+    """Partial residency with natural routing (the router picks the experts; ids
+    are read back per layer) on OLMoE shapes, batch 1, with and without
+    next-layer prefetch (the next layer's router run on the current x guesses
+    its experts, whose copies start while the current layer computes)."""
+    import torch
+    shape = fx.OLMOE
+    lw = [{k: v.cpu().numpy() for k, v in
+           fx.layer_weights(shape, "bench-prefetch", l, device="cuda", batched=True).items()}
+          for l in range(layers)]
+    h0s = torch.stack([fx.activations(("bench-prefetch-h0", i), 1, shape.hidden, device="cuda").float()
+                       for i in range(32)])
+    res = {"steps": steps, "layers": layers, "routing": "natural (router of each layer)"}
+    for policy, C in (("lru", 16), ("lfu", 32), ("lfu", 48)):
+        outs = {}
+        for pf in (False, True):
+            ctx = moe.MoEContext(shape, n_layers=layers, max_tokens=1, policy=policy, slots=C)
+            for l, w in enumerate(lw):
+                ctx.register_layer(l, w)
+            out = torch.empty((steps, 1, shape.hidden), dtype=torch.float32, device=dev)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            with torch.cuda.stream(stream):
+                for s_ in range(steps):
+                    out[s_].copy_(h0s[s_ % 32])
+                    ctx.stack_forward_pooled(out[s_], step=s_, prefetch=pf, stream=stream)
+            stream.synchronize()
+            dt = time.perf_counter() - t0
+            st = [ctx.cache_stats(l) for l in range(layers)]
+            assert ctx.check_device_errors(stream) == 0
+            ctx.close()
+            acc = sum(x["accesses"] for x in st)
+            pfs = sum(x["prefetches"] for x in st)
+            row = {"tokens_per_s": round(steps / dt, 1),
+                   "hit_rate": round(sum(x["hits"] for x in st) / max(acc, 1), 4),
+                   "demand_misses_per_token": round(sum(x["misses"] for x in st) / steps, 2),
+                   "h2d_gb": round(sum(x["h2d_bytes"] for x in st) / 1e9, 3)}
+            if pf:
+                row["prefetches_per_token"] = round(pfs / steps, 2)
+                row["prefetch_used_frac"] = round(sum(x["prefetch_used"] for x in st) / max(pfs, 1), 4)
+            outs[pf] = out
+            res[f"{policy}_C{C}_{'prefetch' if pf else 'no_prefetch'}"] = row
+        res[f"{policy}_C{C}_bit_identical"] = bool(torch.equal(outs[True], outs[False]))
+    return res
+
+
 def extra_trace_analysis(moe, fx, steps=256):
     """Offline policy sweep over seeded Zipf(1.1) routing traces (host engine of the
     library): per capacity C the hit rates of LRU / LFU / LRU-FREQ and of Belady's
@@ -456,6 +502,8 @@ def main():
         print(f"[bench] qwen extras done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
         extra["partial_residency_olmoe16"] = extra_pool(moe, fx, dev, stream)
         print(f"[bench] pool extras done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
+        extra["prefetch_natural_routing_olmoe16"] = extra_prefetch(moe, fx, dev, stream)
+        print(f"[bench] prefetch extras done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
         extra["policy_sweep_zipf"] = extra_trace_analysis(moe, fx)
         print(f"[bench] policy sweep done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
         out["extra"] = extra

@@ -121,15 +121,20 @@ typedef struct moe_cache_counters {
   uint64_t h2d_bytes;      /* bytes copied host -> device for misses              */
   uint64_t d2h_bytes;      /* expert bytes copied device -> host: always 0        */
   uint64_t failures;       /* transfers that failed                               */
-  double h2d_seconds;      /* side-stream busy time of completed miss copies,
-                              summed from events by moe_cache_stats (syncs them)  */
+  double h2d_seconds;      /* side-stream busy time of completed miss and prefetch
+                              copies, summed from events by moe_cache_stats
+                              (syncs them)                                        */
+  uint64_t prefetches;     /* experts copied by moe_cache_prefetch (also counted
+                              in h2d_bytes)                                       */
+  uint64_t prefetch_used;  /* prefetched copies later named by moe_cache_ensure   */
 } moe_cache_counters;
 
 typedef struct moe_cache_event {
-  int32_t step;            /* value of the ensure call's `step` argument          */
+  int32_t step;            /* value of the ensure / prefetch call's `step`        */
   int32_t layer;
   int32_t expert;
-  int32_t hit;             /* 1 hit, 0 miss                                       */
+  int32_t hit;             /* 0 miss, 1 hit, 2 prefetch fill (moe_cache_prefetch),
+                              3 hit on a prefetched copy (its first use)          */
   int32_t slot;            /* slot the expert occupies after the call             */
   int32_t victim;          /* expert evicted from that slot, -1 if none           */
 } moe_cache_event;
@@ -271,6 +276,54 @@ moe_status moe_fused_phase_stamps(moe_ctx* ctx, uint64_t* dev_buf, int64_t count
 moe_status moe_cache_ensure(moe_ctx* ctx, int32_t layer, const int32_t* experts, int32_t n,
                             int32_t* slots, int32_t step, void* stream);
 
+/* Next-layer prefetch ("An expert-offloading engine, from scratch", "Terms used
+ * here" and "What the numbers say": the next layer's experts are guessed by
+ * running its router on the current state, and their reads start early so that
+ * they overlap with computing).  experts: host int32 [n], distinct, the guessed
+ * group of `layer`, n <= C.  Guessed experts already resident are left as they
+ * are (no use is counted).  Each other one is filled like a miss -- lowest free
+ * slot, else the policy's victim among resident experts outside the guess --
+ * without a clock tick, with its LFU count unchanged, and not counted as a miss
+ * (nor for the LRU-FREQ decay); its copy from the pinned backing is enqueued on
+ * the side stream after the layer's last reader has retired.  Nothing is
+ * published: the expert->slot map entry of a prefetched expert is written by
+ * the first moe_cache_ensure that names it (after the copy completes, in that
+ * call's stream order; the event log then records a hit of kind 3), and a guess
+ * never used costs only its transfer and slot.  Victims' map entries are set to
+ * -1 in `stream` order.  Outputs never depend on prefetching.  Returns
+ * MOE_E_ARG / MOE_E_CAPACITY as moe_cache_ensure; MOE_E_TRANSFER when a copy
+ * cannot be enqueued (the pool is left as it was).  With MOE_RESIDENT_ALL it
+ * does nothing. */
+moe_status moe_cache_prefetch(moe_ctx* ctx, int32_t layer, const int32_t* experts, int32_t n,
+                              int32_t step, void* stream);
+
+/* Residual stack with natural routing over the slot pools (partial residency):
+ * for each layer l in [layer_begin, layer_end): x_l = fp16(RMSNorm(h)); route
+ * layer l on x_l; when `prefetch` != 0 and l + 1 < layer_end, also route layer
+ * l + 1 on x_l (the guess); read both id sets back to the host (this
+ * synchronises `stream`); moe_cache_ensure(l, distinct ids of the T tokens);
+ * moe_cache_prefetch(l + 1, distinct guessed ids) when the guess fits the pool;
+ * then the layer itself (as moe_stack_forward over [l, l + 1) with the routed
+ * ids forced), so the guessed experts' copies run while layer l computes
+ * ("An expert-offloading engine, from scratch", "What the numbers say").  The
+ * result equals moe_stack_forward's with natural routing and full residency,
+ * whatever is prefetched.  h: dev FP32 [T,H], updated in place; step: the
+ * label of the event-log entries.  ids_trace (dev int32 [L,T,k]) receives each
+ * layer's routed ids and guess_trace (dev int32 [L,T,k]) at row l + 1 the ids
+ * guessed for layer l + 1, when non-NULL (indexed by absolute layer; rows not
+ * written are left as they are).  Needs a slot pool (MOE_E_ARG otherwise) and
+ * every layer's distinct routed experts within C (MOE_E_CAPACITY).  Returns
+ * after the last layer is enqueued. */
+moe_status moe_stack_forward_pooled(moe_ctx* ctx, int32_t layer_begin, int32_t layer_end, float* h,
+                                    int32_t T, int32_t prefetch, int32_t step, int32_t* ids_trace,
+                                    int32_t* guess_trace, void* stream);
+
+/* The stack's normalisation on its own: x = fp16(h / sqrt(mean(h^2) + 1e-5)),
+ * unit weight, per token.  h: dev FP32 [T,H]; x: dev FP16 [T,H] out;
+ * 1 <= T <= max_tokens.  Lets a caller route a layer (moe_route) before its
+ * group is made resident, and guess the next layer's group from the same x. */
+moe_status moe_rmsnorm(moe_ctx* ctx, const float* h, int32_t T, void* x, void* stream);
+
 moe_status moe_cache_stats(moe_ctx* ctx, int32_t layer, moe_cache_counters* out);
 
 /* Copies up to `cap` events of `layer` (oldest first) into buf; *n = number
@@ -303,6 +356,9 @@ void moe_policy_free(moe_policy_engine* p);
  * slots [n] out in the order of `experts`; events appended to the engine's log. */
 moe_status moe_policy_access(moe_policy_engine* p, const int32_t* experts, int32_t n,
                              int32_t step, int32_t* slots);
+/* The decision part of moe_cache_prefetch (same rules and return codes). */
+moe_status moe_policy_prefetch(moe_policy_engine* p, const int32_t* experts, int32_t n,
+                               int32_t step);
 int32_t moe_policy_event_count(const moe_policy_engine* p);
 int32_t moe_policy_events(const moe_policy_engine* p, moe_cache_event* buf, int32_t cap);
 

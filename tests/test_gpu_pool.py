@@ -161,3 +161,97 @@ def test_pool_resident_all_ensure_is_identity(moe, olmoe_layers):
     assert ctx.cache_ensure(0, g).tolist() == [5, 1, 9]
     assert ctx.cache_events(0) == []
     ctx.close()
+
+
+# ---- natural routing over the pools, with and without next-layer prefetch ---------
+
+NAT_STEPS = 12
+
+
+def _run_natural(ctx, h0s, prefetch, steps=NAT_STEPS):
+    outs, ids, gs = [], [], []
+    for s in range(steps):
+        h = h0s[s % len(h0s)].clone()
+        i, g = ctx.stack_forward_pooled(h, step=s, prefetch=prefetch, trace=True)
+        outs.append(h)
+        ids.append(i.cpu().numpy())
+        gs.append(g.cpu().numpy())
+    torch.cuda.synchronize()
+    assert ctx.check_device_errors() == 0
+    return torch.stack(outs), np.stack(ids), np.stack(gs)
+
+
+def _replay(policy, C, ids, gs, prefetch, layer):
+    """The oracle's decisions for one layer over the same routed groups and guesses."""
+    sim = ora.CacheSim(POLICY_ORACLE[policy], fx.OLMOE.n_experts, C, layer=layer)
+    for s in range(ids.shape[0]):
+        if prefetch and layer > 0:
+            guess = sorted(set(int(e) for e in gs[s, layer].ravel()))
+            if len(guess) <= C:
+                sim.prefetch(guess, s)
+        sim.ensure(sorted(set(int(e) for e in ids[s, layer].ravel())), s)
+    return sim
+
+
+@pytest.mark.parametrize("policy,C", [("lru", 16), ("lfu", 32)])
+def test_pool_natural_routing_prefetch_never_changes_outputs(moe, olmoe_layers, h0s, policy, C):
+    say(f"test_pool_natural policy={policy} C={C}")
+    runs = {}
+    for pf in (False, True):
+        ctx = _ctx(moe, olmoe_layers, policy=policy, slots=C)
+        out, ids, gs = _run_natural(ctx, h0s, pf)
+        blob = fx.OLMOE.blob_bytes
+        used = issued = 0
+        for l in range(L):
+            sim = _replay(policy, C, ids, gs, pf, l)
+            assert ctx.cache_events(l) == [e.as_tuple() for e in sim.events], f"layer {l} prefetch={pf}"
+            st = ctx.cache_stats(l)
+            assert st["hits"] == sim.hits and st["misses"] == sim.misses
+            assert st["prefetches"] == sim.prefetches and st["prefetch_used"] == sim.prefetch_used
+            assert st["h2d_bytes"] == (sim.misses + sim.prefetches) * blob
+            assert st["d2h_bytes"] == 0 and st["failures"] == 0
+            used += sim.prefetch_used
+            issued += sim.prefetches
+        if pf:
+            assert issued > 0
+            say(f"  prefetched {issued}, used {used} ({used / issued:.3f})")
+        runs[pf] = (out, ids)
+        ctx.close()
+    # prefetching never changes what is computed
+    assert torch.equal(runs[True][0], runs[False][0]), "prefetch changed the output"
+    assert np.array_equal(runs[True][1], runs[False][1])
+
+
+def test_pool_natural_routing_matches_resident_stack(moe, olmoe_layers, h0s):
+    # the pooled per-layer loop against the whole-stack call with every expert
+    # resident: the same routing on (nearly) the same x, outputs within tolerance
+    from gpu_util import rel_l2
+    ctx = _ctx(moe, olmoe_layers, policy="lru", slots=16)
+    pooled, ids, _ = _run_natural(ctx, h0s, True, steps=4)
+    ctx.close()
+    ctx = _ctx(moe, olmoe_layers)
+    for s in range(4):
+        h = h0s[s].clone()
+        _, rids, _ = ctx.stack_forward(h, trace=True)
+        agree = float(np.mean(rids.cpu().numpy() == ids[s]))
+        err = rel_l2(pooled[s].cpu().numpy(), h.cpu().numpy())
+        say(f"  step {s}: ids agree {agree:.4f}, rel-L2 {err:.2e}")
+        assert agree >= 0.99 and err <= 2e-3
+    ctx.close()
+
+
+def test_pool_prefetch_argument_errors(moe, olmoe_layers):
+    from w4a16_routed_expert_router_amd import MoEError, capi
+    ctx = _ctx(moe, olmoe_layers[:L], policy="lru", slots=8)
+    for bad, code in (([3, 3], capi.MOE_E_ARG), ([64], capi.MOE_E_ARG), (list(range(9)), capi.MOE_E_CAPACITY)):
+        with pytest.raises(MoEError) as e:
+            ctx.cache_prefetch(1, bad)
+        assert e.value.status == code
+    assert ctx.cache_events(1) == []
+    ctx.close()
+    res = _ctx(moe, olmoe_layers)
+    res.cache_prefetch(1, [1, 2, 3])      # full residency: nothing to do
+    with pytest.raises(MoEError) as e:
+        res.stack_forward_pooled(h=torch.zeros((1, fx.OLMOE.hidden), device="cuda"))
+    assert e.value.status == capi.MOE_E_ARG
+    res.close()

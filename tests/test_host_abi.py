@@ -176,3 +176,48 @@ def test_trace_analysis_rejects_bad_traces():
     assert moe.trace_opt(empty, 8, 1) == (0, 0)
     assert moe.trace_top_share(empty, 8, 2) == 0.0
     assert moe.trace_skew(empty, 8)["selections"] == 0
+
+
+def _noisy_guess(rng, group, n_experts, p_wrong):
+    """The next group with each expert replaced, with probability p_wrong, by a
+    random expert not in it (a guess that is partly right)."""
+    g = [int(e) for e in group]
+    out = []
+    for e in g:
+        if rng.random() < p_wrong:
+            cand = [x for x in range(n_experts) if x not in g and x not in out]
+            out.append(int(rng.choice(cand)))
+        else:
+            out.append(e)
+    return sorted(set(out))
+
+
+@pytest.mark.parametrize("policy", ["lru", "lfu", "lru_freq"])
+@pytest.mark.parametrize("C", [8, 16, 24])
+def test_policy_engine_prefetch_matches_oracle(policy, C):
+    from w4a16_routed_expert_router_amd import PolicyEngine
+    rng = np.random.default_rng(C)
+    tr = fx.zipf_trace("abi-prefetch", 120, 1, 64, 8)[:, 0, :]
+    eng = PolicyEngine(policy, 64, C, layer=2)
+    sim = ora.CacheSim(policy, 64, C, layer=2)
+    for t in range(len(tr)):
+        if t > 0 and rng.random() < 0.8:
+            guess = _noisy_guess(rng, tr[t], 64, 0.3)
+            eng.prefetch(guess, step=t)
+            sim.prefetch(guess, step=t)
+        eng.access(tr[t], step=t)
+        sim.ensure(tr[t], step=t)
+    assert eng.events() == [e.as_tuple() for e in sim.events]
+    kinds = [e[3] for e in eng.events()]
+    assert kinds.count(ora.EV_PREFETCH) == sim.prefetches > 0
+    assert kinds.count(ora.EV_PREFETCH_HIT) == sim.prefetch_used > 0
+
+
+def test_policy_engine_prefetch_rejects_bad_guesses():
+    from w4a16_routed_expert_router_amd import MoEError, PolicyEngine, capi
+    eng = PolicyEngine("lru", 16, 4)
+    for bad, code in (([1, 1], capi.MOE_E_ARG), ([16], capi.MOE_E_ARG), ([0, 1, 2, 3, 4], capi.MOE_E_CAPACITY)):
+        with pytest.raises(MoEError) as e:
+            eng.prefetch(bad)
+        assert e.value.status == code
+    assert eng.events() == []

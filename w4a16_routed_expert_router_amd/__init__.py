@@ -168,6 +168,41 @@ class MoEContext:
                                           slots.ctypes.data, step, _stream(stream, self.device)))
         return slots
 
+    def cache_prefetch(self, layer, experts, step=0, stream=None):
+        e = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+        self._check(_lib.moe_cache_prefetch(self._h, layer, e.ctypes.data, e.size, step,
+                                            _stream(stream, self.device)))
+
+    def stack_forward_pooled(self, h, step=0, prefetch=True, layer_begin=0, layer_end=None, trace=False,
+                             stream=None):
+        """Natural routing over the slot pools; h: FP32 [T,H] CUDA tensor, updated in place.
+        With trace=True returns (ids [L,T,k], guesses [L,T,k]; -1 where not written)."""
+        sh = self.shape
+        T = h.shape[0]
+        L = self.n_layers
+        layer_end = L if layer_end is None else layer_end
+        hp = _dev(h, torch.float32, (T, sh.hidden), self.device, "h")
+        ids = gs = None
+        if trace:
+            ids = torch.full((L, T, sh.top_k), -1, dtype=torch.int32, device=h.device)
+            gs = torch.full((L, T, sh.top_k), -1, dtype=torch.int32, device=h.device)
+        self._check(_lib.moe_stack_forward_pooled(
+            self._h, layer_begin, layer_end, hp, T, int(bool(prefetch)), step,
+            None if ids is None else C.c_void_p(ids.data_ptr()),
+            None if gs is None else C.c_void_p(gs.data_ptr()),
+            _stream(stream, self.device)))
+        return (ids, gs) if trace else None
+
+    def rmsnorm(self, h, out=None, stream=None):
+        sh = self.shape
+        T = h.shape[0]
+        hp = _dev(h, torch.float32, (T, sh.hidden), self.device, "h")
+        if out is None:
+            out = torch.empty((T, sh.hidden), dtype=torch.float16, device=h.device)
+        op = _dev(out, torch.float16, (T, sh.hidden), self.device, "out")
+        self._check(_lib.moe_rmsnorm(self._h, hp, T, op, _stream(stream, self.device)))
+        return out
+
     def cache_stats(self, layer):
         st = capi.moe_cache_counters()
         self._check(_lib.moe_cache_stats(self._h, layer, C.byref(st)))
@@ -229,6 +264,12 @@ class PolicyEngine:
         if st != capi.MOE_OK:
             raise MoEError(st, "policy access rejected")
         return slots
+
+    def prefetch(self, experts, step=0):
+        e = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+        st = _lib.moe_policy_prefetch(self._h, e.ctypes.data, e.size, step)
+        if st != capi.MOE_OK:
+            raise MoEError(st, "policy prefetch rejected")
 
     def events(self):
         n = _lib.moe_policy_event_count(self._h)

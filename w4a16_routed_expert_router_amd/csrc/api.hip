@@ -43,6 +43,8 @@ struct LayerState {
   std::unique_ptr<PolicyEngine> policy;
   hipEvent_t retired = nullptr;
   hipEvent_t ready = nullptr;
+  hipEvent_t pf_ready = nullptr;  // after the latest prefetch copies of the layer
+  bool pf_recorded = false;
   moe_cache_counters stats{};
   std::vector<std::pair<hipEvent_t, hipEvent_t>> timing;
   int inject = 0;  // test hook: 1 fail before publication, 2 fail after it
@@ -84,6 +86,12 @@ struct moe_ctx {
   int grid = 0;
   int ncu = 1;                 // compute units (grid of the streaming kernel)
   uint64_t* stamps = nullptr;  // caller-owned phase-timestamp buffer or null
+  // natural routing over slot pools (moe_stack_forward_pooled)
+  uint16_t* pool_x = nullptr;   // dev FP16 [max_tokens, H]: x of the current layer
+  int32_t* pool_ids = nullptr;  // dev [n_layers, T, k] (room for max_tokens): routed ids, forced ids of the layer calls
+  float* pool_w = nullptr;      // dev [max_tokens, k]
+  int32_t* pool_gids = nullptr; // dev [max_tokens, k]: next layer's guessed ids
+  int32_t* pool_ids_h = nullptr;   // pinned host [2, max_tokens, k]: routed + guessed ids
   // kernel timer
   int timer_kind = -1;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> timer_events;
@@ -385,7 +393,8 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     }
     if (ok) {
       if (hipEventCreateWithFlags(&L.retired, hipEventDisableTiming) != hipSuccess ||
-          hipEventCreateWithFlags(&L.ready, hipEventDisableTiming) != hipSuccess)
+          hipEventCreateWithFlags(&L.ready, hipEventDisableTiming) != hipSuccess ||
+          hipEventCreateWithFlags(&L.pf_ready, hipEventDisableTiming) != hipSuccess)
         ok = false;
     }
   }
@@ -432,6 +441,17 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     ok = ok && dalloc((void**)&c->hshared, (size_t)g.max_tokens * g.shared_inter * 2);
     ok = ok && dalloc((void**)&c->yshared, (size_t)g.max_tokens * g.hidden * 4);
   }
+  if (g.policy != MOE_RESIDENT_ALL) {
+    ok = ok && dalloc((void**)&c->pool_x, (size_t)g.max_tokens * g.hidden * 2);
+    ok = ok && dalloc((void**)&c->pool_ids, (size_t)g.n_layers * P * 4);
+    ok = ok && dalloc((void**)&c->pool_w, (size_t)P * 4);
+    ok = ok && dalloc((void**)&c->pool_gids, (size_t)P * 4);
+    if (ok && hipHostMalloc((void**)&c->pool_ids_h, (size_t)2 * P * 4, hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      c->pool_ids_h = nullptr;
+      ok = false;
+    }
+  }
   if (ok && hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess) ok = false;
   if (ok) {
     const uint32_t zero = 0;
@@ -457,6 +477,7 @@ void moe_destroy(moe_ctx* c) {
     if (L.backing) (void)hipHostFree(L.backing);
     if (L.retired) (void)hipEventDestroy(L.retired);
     if (L.ready) (void)hipEventDestroy(L.ready);
+    if (L.pf_ready) (void)hipEventDestroy(L.pf_ready);
     for (auto& p : L.timing) {
       (void)hipEventDestroy(p.first);
       (void)hipEventDestroy(p.second);
@@ -464,8 +485,10 @@ void moe_destroy(moe_ctx* c) {
   }
   void* bufs[] = {c->logits, c->rscratch, c->ids,  c->w,    c->ids_s,   c->active,  c->n_active, c->perm_tok,
                   c->pos_of, c->hbuf, c->ybuf, c->xbuf,    c->err,     c->hshared,  c->yshared,
-                  c->dlayers, c->mtile_off, c->xh, c->xlg, c->xhb, c->xgate, c->epoch};
+                  c->dlayers, c->mtile_off, c->xh, c->xlg, c->xhb, c->xgate, c->epoch,
+                  c->pool_x, c->pool_ids, c->pool_w, c->pool_gids};
   for (void* p : bufs) (void)hipFree(p);
+  if (c->pool_ids_h) (void)hipHostFree(c->pool_ids_h);
   if (c->side) (void)hipStreamDestroy(c->side);
   for (auto& p : c->timer_events) {
     (void)hipEventDestroy(p.first);
@@ -655,12 +678,22 @@ moe_status moe_cache_ensure(moe_ctx* c, int32_t layer, const int32_t* experts, i
   if (rc == 1) return fail(c, MOE_E_ARG, "repeated expert in group");
   if (rc == 2) return fail(c, MOE_E_CAPACITY, "routed group larger than the slot pool");
   const int64_t blob = c->lay.total();
-  int nmiss = 0, nevict = 0;
-  for (const auto& d : dec)
+  int nmiss = 0, nevict = 0, nfirst = 0;
+  for (const auto& d : dec) {
     if (!d.hit) {
       ++nmiss;
       if (d.victim >= 0) ++nevict;
     }
+    if (d.kind == PolicyEngine::kPrefetchHit) ++nfirst;
+  }
+  // a prefetched copy is published on its first use, after its transfer
+  // (ordered before any copy of this call is enqueued)
+  if (nfirst > 0 && L.pf_recorded && hipStreamWaitEvent(s, L.pf_ready, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    *L.policy = saved;
+    L.stats.failures += 1;
+    return fail(c, MOE_E_TRANSFER, "could not order the first use of a prefetched copy");
+  }
   if (nmiss > 0) {
     // transport: side stream waits for the last reader of this layer's slots
     bool good = L.inject != 1;
@@ -686,26 +719,26 @@ moe_status moe_cache_ensure(moe_ctx* c, int32_t layer, const int32_t* experts, i
       return fail(c, MOE_E_TRANSFER, "miss transfer failed before publication");
     }
     L.timing.emplace_back(t0, t1);
+  }
+  if (nmiss > 0 || nfirst > 0) {
     // publication in stream order, after the copies
     PublishArgs pa{};
     pa.map = L.map;
-    for (const auto& d : dec) {
-      if (d.hit) continue;
-      if (d.victim >= 0) {
-        if (pa.n == kMaxPublish) {
-          launch_publish(pa, s);
-          pa.n = 0;
-        }
-        pa.u[pa.n++] = PublishUpdate{d.victim, -1};
-      }
+    auto push = [&](int32_t e, int32_t slot) {
       if (pa.n == kMaxPublish) {
         launch_publish(pa, s);
         pa.n = 0;
       }
-      pa.u[pa.n++] = PublishUpdate{d.expert, d.slot};
+      pa.u[pa.n++] = PublishUpdate{e, slot};
+    };
+    for (const auto& d : dec) {
+      if (d.kind == PolicyEngine::kPrefetchHit) push(d.expert, d.slot);
+      if (d.hit) continue;
+      if (d.victim >= 0) push(d.victim, -1);
+      push(d.expert, d.slot);
     }
     if (pa.n) launch_publish(pa, s);
-    if (hipGetLastError() != hipSuccess || L.inject == 2) {
+    if (hipGetLastError() != hipSuccess || (nmiss > 0 && L.inject == 2)) {
       c->faulted = true;
       L.inject = 0;
       L.stats.failures += 1;
@@ -717,7 +750,141 @@ moe_status moe_cache_ensure(moe_ctx* c, int32_t layer, const int32_t* experts, i
   L.stats.misses += nmiss;
   L.stats.evictions += nevict;
   L.stats.h2d_bytes += (uint64_t)nmiss * blob;
+  L.stats.prefetch_used += nfirst;
   for (int i = 0; i < n; ++i) slots[i] = L.policy->slot_of(experts[i]);
+  return MOE_OK;
+}
+
+moe_status moe_cache_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int32_t step,
+                              void* stream) {
+  if (moe_status st = check_ctx(c)) return st;
+  if (moe_status st = check_layer(c, layer)) return st;
+  if (n < 0 || (n > 0 && !experts)) return fail(c, MOE_E_ARG, "bad experts");
+  const moe_config& g = c->cfg;
+  for (int i = 0; i < n; ++i)
+    if (experts[i] < 0 || experts[i] >= g.n_experts) return fail(c, MOE_E_ARG, "expert id out of range");
+  if (!pooled(c)) return MOE_OK;
+  LayerState& L = c->layers[layer];
+  if (n > g.slots_per_layer) return fail(c, MOE_E_CAPACITY, "guessed group larger than the slot pool");
+  hipStream_t s = (hipStream_t)stream;
+  const PolicyEngine saved = *L.policy;
+  std::vector<PolicyEngine::Decision> dec;
+  const int rc = L.policy->prefetch(experts, n, step, dec);
+  if (rc == 1) return fail(c, MOE_E_ARG, "repeated expert in guessed group");
+  if (rc == 2) return fail(c, MOE_E_CAPACITY, "guessed group larger than the slot pool");
+  if (dec.empty()) return MOE_OK;
+  const int64_t blob = c->lay.total();
+  // transport only: nothing is published until an ensure() names the expert
+  bool good = L.inject != 1;
+  hipEvent_t t0 = nullptr, t1 = nullptr;
+  good = good && hipEventCreate(&t0) == hipSuccess && hipEventCreate(&t1) == hipSuccess;
+  good = good && hipStreamWaitEvent(c->side, L.retired, 0) == hipSuccess;
+  good = good && hipEventRecord(t0, c->side) == hipSuccess;
+  for (const auto& d : dec) {
+    if (!good) break;
+    good = hipMemcpyAsync(L.store + (int64_t)d.slot * blob, L.backing + (int64_t)d.expert * blob,
+                          (size_t)blob, hipMemcpyHostToDevice, c->side) == hipSuccess;
+  }
+  good = good && hipEventRecord(t1, c->side) == hipSuccess;
+  good = good && hipEventRecord(L.pf_ready, c->side) == hipSuccess;
+  if (!good) {
+    (void)hipGetLastError();
+    if (t0) (void)hipEventDestroy(t0);
+    if (t1) (void)hipEventDestroy(t1);
+    *L.policy = saved;
+    L.inject = 0;
+    L.stats.failures += 1;
+    return fail(c, MOE_E_TRANSFER, "prefetch transfer failed; nothing was published");
+  }
+  L.pf_recorded = true;
+  L.timing.emplace_back(t0, t1);
+  // the victims' old copies are being overwritten: their map entries go to -1
+  // in `stream` order, so no later kernel can read a victim through a stale map
+  PublishArgs pa{};
+  pa.map = L.map;
+  int nevict = 0;
+  for (const auto& d : dec) {
+    if (d.victim < 0) continue;
+    ++nevict;
+    if (pa.n == kMaxPublish) {
+      launch_publish(pa, s);
+      pa.n = 0;
+    }
+    pa.u[pa.n++] = PublishUpdate{d.victim, -1};
+  }
+  if (pa.n) launch_publish(pa, s);
+  if (hipGetLastError() != hipSuccess) {
+    c->faulted = true;
+    L.stats.failures += 1;
+    return fail(c, MOE_E_FAULTED, "failure after a prefetch was enqueued: context faulted");
+  }
+  L.stats.prefetches += dec.size();
+  L.stats.evictions += nevict;
+  L.stats.h2d_bytes += (uint64_t)dec.size() * blob;
+  return MOE_OK;
+}
+
+moe_status moe_stack_forward_pooled(moe_ctx* c, int32_t layer_begin, int32_t layer_end, float* h, int32_t T,
+                                    int32_t prefetch, int32_t step, int32_t* ids_trace, int32_t* guess_trace,
+                                    void* stream) {
+  if (moe_status st = check_ctx(c)) return st;
+  const moe_config& g = c->cfg;
+  if (!pooled(c)) return fail(c, MOE_E_ARG, "moe_stack_forward_pooled needs a slot pool");
+  if (!h || T < 1 || T > g.max_tokens) return fail(c, MOE_E_ARG, "bad h/T");
+  if (layer_begin < 0 || layer_end > g.n_layers || layer_begin >= layer_end)
+    return fail(c, MOE_E_ARG, "bad layer range");
+  for (int l = layer_begin; l < layer_end; ++l)
+    if (moe_status st = check_layer(c, l)) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int k = g.top_k, P = T * k;
+  int32_t* ids_h = c->pool_ids_h;
+  int32_t* gids_h = c->pool_ids_h + (int64_t)g.max_tokens * k;
+  // distinct ids of T tokens, ascending
+  auto group_of = [&](const int32_t* v, std::vector<int32_t>& grp) {
+    grp.assign(v, v + P);
+    std::sort(grp.begin(), grp.end());
+    grp.erase(std::unique(grp.begin(), grp.end()), grp.end());
+  };
+  std::vector<int32_t> grp, guess, slots;
+  for (int l = layer_begin; l < layer_end; ++l) {
+    int32_t* ids_l = c->pool_ids + (int64_t)l * P;  // forced ids of the layer call: [L, T, k]
+    const bool guess_next = prefetch && l + 1 < layer_end;
+    if (moe_status st = moe_rmsnorm(c, h, T, c->pool_x, stream)) return st;
+    if (moe_status st = moe_route(c, l, c->pool_x, T, nullptr, ids_l, c->pool_w, nullptr, stream)) return st;
+    // the next layer's router on the current state guesses its experts
+    if (guess_next)
+      if (moe_status st = moe_route(c, l + 1, c->pool_x, T, nullptr, c->pool_gids, c->pool_w, nullptr, stream))
+        return st;
+    if (ids_trace) HIPCHK(c, hipMemcpyAsync(ids_trace + (int64_t)l * P, ids_l, (size_t)P * 4, hipMemcpyDeviceToDevice, s));
+    if (guess_next && guess_trace)
+      HIPCHK(c, hipMemcpyAsync(guess_trace + (int64_t)(l + 1) * P, c->pool_gids, (size_t)P * 4,
+                               hipMemcpyDeviceToDevice, s));
+    HIPCHK(c, hipMemcpyAsync(ids_h, ids_l, (size_t)P * 4, hipMemcpyDeviceToHost, s));
+    if (guess_next) HIPCHK(c, hipMemcpyAsync(gids_h, c->pool_gids, (size_t)P * 4, hipMemcpyDeviceToHost, s));
+    HIPCHK(c, hipStreamSynchronize(s));
+    group_of(ids_h, grp);
+    slots.resize(grp.size());
+    if (moe_status st = moe_cache_ensure(c, l, grp.data(), (int32_t)grp.size(), slots.data(), step, stream))
+      return st;
+    if (guess_next) {
+      group_of(gids_h, guess);
+      // a guess larger than the pool is not prefetched
+      if ((int32_t)guess.size() <= g.slots_per_layer)
+        if (moe_status st = moe_cache_prefetch(c, l + 1, guess.data(), (int32_t)guess.size(), step, stream))
+          return st;
+    }
+    // the layer itself, routed by the ids just read (the same router, the same x)
+    if (moe_status st = moe_stack_forward(c, l, l + 1, h, T, c->pool_ids, nullptr, nullptr, nullptr, stream))
+      return st;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_rmsnorm(moe_ctx* c, const float* h, int32_t T, void* x, void* stream) {
+  if (moe_status st = check_ctx(c)) return st;
+  if (!h || !x || T < 1 || T > c->cfg.max_tokens) return fail(c, MOE_E_ARG, "bad h/x/T");
+  launch_rmsnorm(h, T, c->cfg.hidden, 1e-5f, reinterpret_cast<uint16_t*>(x), (hipStream_t)stream);
+  HIPCHK(c, hipGetLastError());
   return MOE_OK;
 }
 

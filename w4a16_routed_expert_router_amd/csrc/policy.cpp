@@ -19,6 +19,15 @@
 //     that named the expert, kept across evictions; LRU-FREQ
 //     (sfreq*1000 - (clock - last), id) in double, sfreq = 1 on fill and +1 per
 //     hit, all sfreq *= 0.75 right after the miss that completes each 2*C.
+//
+// Next-layer prefetch: the next layer's experts are guessed by running its
+// router on the current state, and their reads start early so that they
+// overlap with computing ("An expert-offloading engine, from scratch", "Terms
+// used here" and "What the numbers say").  As implemented, a prefetch neither
+// ticks the clock nor counts as a use; each guessed expert that is not
+// resident is filled like a miss (last = the current clock, LFU count
+// unchanged, sfreq = 1), is not a miss for the LRU-FREQ decay, and stays
+// pending until an access names it, which counts a hit on the prefetched copy.
 #include "policy.hpp"
 
 #include <algorithm>
@@ -27,7 +36,7 @@ namespace moe {
 
 PolicyEngine::PolicyEngine(int policy, int n_experts, int capacity, int layer)
     : policy_(policy), E_(n_experts), C_(capacity), layer_(layer),
-      slot_of_(n_experts, -1), expert_in_(capacity, -1), last_(n_experts, 0),
+      pending_(n_experts, 0), slot_of_(n_experts, -1), expert_in_(capacity, -1), last_(n_experts, 0),
       count_(n_experts, 0), sfreq_(capacity, 0.0) {}
 
 #pragma clang fp contract(off)
@@ -56,19 +65,39 @@ bool PolicyEngine::less_key(int a, int b) const {
   }
 }
 
-int PolicyEngine::access(const int32_t* experts, int n, int step, std::vector<Decision>& out) {
-  out.clear();
+int PolicyEngine::check_group(const int32_t* experts, int n, std::vector<int32_t>& g) const {
   if (n < 0) return 1;
   if (n > C_) return 2;
-  std::vector<int32_t> g(experts, experts + n);
+  g.assign(experts, experts + n);
   for (int e : g)
     if (e < 0 || e >= E_) return 1;
   std::sort(g.begin(), g.end());
   for (int i = 1; i < n; ++i)
     if (g[i] == g[i - 1]) return 1;
+  return 0;
+}
+
+int PolicyEngine::take_slot(const std::vector<char>& in_group, int& victim) {
+  victim = -1;
+  for (int s = 0; s < C_; ++s)
+    if (expert_in_[s] < 0) return s;
+  for (int s = 0; s < C_; ++s) {
+    const int x = expert_in_[s];
+    if (in_group[x]) continue;
+    if (victim < 0 || less_key(x, victim)) victim = x;
+  }
+  const int slot = slot_of_[victim];
+  slot_of_[victim] = -1;
+  pending_[victim] = 0;
+  return slot;
+}
+
+int PolicyEngine::access(const int32_t* experts, int n, int step, std::vector<Decision>& out) {
+  out.clear();
+  std::vector<int32_t> g;
+  if (const int rc = check_group(experts, n, g)) return rc;
   std::vector<char> in_group(E_, 0);
   for (int e : g) in_group[e] = 1;
-
   ++clock_;
   std::vector<char> hit(n, 0);
   for (int i = 0; i < n; ++i) {
@@ -80,38 +109,55 @@ int PolicyEngine::access(const int32_t* experts, int n, int step, std::vector<De
     count_[e] += 1;
     sfreq_[s] += 1.0;
     ++hits_;
-    out.push_back(Decision{e, s, -1, true});
+    int kind = kHit;
+    if (pending_[e]) {
+      pending_[e] = 0;
+      ++prefetch_used_;
+      kind = kPrefetchHit;
+    }
+    out.push_back(Decision{e, s, -1, true, kind});
   }
   for (int i = 0; i < n; ++i) {
     if (hit[i]) continue;
     const int e = g[i];
-    int slot = -1, victim = -1;
-    for (int s = 0; s < C_; ++s)
-      if (expert_in_[s] < 0) {
-        slot = s;
-        break;
-      }
-    if (slot < 0) {
-      for (int s = 0; s < C_; ++s) {
-        const int x = expert_in_[s];
-        if (in_group[x]) continue;
-        if (victim < 0 || less_key(x, victim)) victim = x;
-      }
-      slot = slot_of_[victim];
-      slot_of_[victim] = -1;
-    }
+    int victim = -1;
+    const int slot = take_slot(in_group, victim);
     expert_in_[slot] = e;
     slot_of_[e] = slot;
     last_[e] = clock_;
     count_[e] += 1;
     sfreq_[slot] = 1.0;
     ++misses_;
-    out.push_back(Decision{e, slot, victim, false});
+    out.push_back(Decision{e, slot, victim, false, kMiss});
     if (policy_ == 3 && misses_ % (2 * (int64_t)C_) == 0)
       for (double& f : sfreq_) f *= 0.75;
   }
   for (const Decision& d : out)
-    log_.push_back(moe_cache_event{step, layer_, d.expert, d.hit ? 1 : 0, d.slot, d.victim});
+    log_.push_back(moe_cache_event{step, layer_, d.expert, d.kind, d.slot, d.victim});
+  return 0;
+}
+
+int PolicyEngine::prefetch(const int32_t* experts, int n, int step, std::vector<Decision>& out) {
+  out.clear();
+  std::vector<int32_t> g;
+  if (const int rc = check_group(experts, n, g)) return rc;
+  std::vector<char> in_group(E_, 0);
+  for (int e : g) in_group[e] = 1;
+  for (int i = 0; i < n; ++i) {
+    const int e = g[i];
+    if (slot_of_[e] >= 0) continue;
+    int victim = -1;
+    const int slot = take_slot(in_group, victim);
+    expert_in_[slot] = e;
+    slot_of_[e] = slot;
+    last_[e] = clock_;
+    sfreq_[slot] = 1.0;
+    pending_[e] = 1;
+    ++prefetches_;
+    out.push_back(Decision{e, slot, victim, false, kPrefetch});
+  }
+  for (const Decision& d : out)
+    log_.push_back(moe_cache_event{step, layer_, d.expert, d.kind, d.slot, d.victim});
   return 0;
 }
 
@@ -143,6 +189,14 @@ moe_status moe_policy_access(moe_policy_engine* p, const int32_t* experts, int32
   return MOE_OK;
 }
 
+moe_status moe_policy_prefetch(moe_policy_engine* p, const int32_t* experts, int32_t n, int32_t step) {
+  if (!p || (n > 0 && !experts)) return MOE_E_ARG;
+  std::vector<moe::PolicyEngine::Decision> d;
+  const int rc = p->eng.prefetch(experts, n, step, d);
+  if (rc == 1) return MOE_E_ARG;
+  if (rc == 2) return MOE_E_CAPACITY;
+  return MOE_OK;
+}
 int32_t moe_policy_event_count(const moe_policy_engine* p) {
   return p ? (int32_t)p->eng.log().size() : 0;
 }

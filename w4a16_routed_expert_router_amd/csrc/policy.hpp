@@ -11,11 +11,14 @@ namespace moe {
 
 class PolicyEngine {
  public:
+  // event kinds (the `hit` field of moe_cache_event)
+  enum Kind { kMiss = 0, kHit = 1, kPrefetch = 2, kPrefetchHit = 3 };
   struct Decision {
     int32_t expert;
     int32_t slot;
     int32_t victim;  // -1 if none
-    bool hit;
+    bool hit;        // resident when named (kHit or kPrefetchHit)
+    int kind;
   };
 
   PolicyEngine(int policy, int n_experts, int capacity, int layer);
@@ -24,18 +27,29 @@ class PolicyEngine {
   // 2 when n exceeds the capacity; on failure nothing changes.  `out` gets
   // the decisions in event order (hits ascending, then misses ascending).
   int access(const int32_t* experts, int n, int step, std::vector<Decision>& out);
+  // Speculative fill of a guessed group (no clock tick, no use): each guessed
+  // expert that is not resident is filled like a miss and stays pending until
+  // an access names it.  Same return codes; `out` gets the fills.
+  int prefetch(const int32_t* experts, int n, int step, std::vector<Decision>& out);
 
   int32_t slot_of(int e) const { return slot_of_[e]; }
   const std::vector<moe_cache_event>& log() const { return log_; }
   int64_t hits() const { return hits_; }
   int64_t misses() const { return misses_; }
+  int64_t prefetches() const { return prefetches_; }
+  int64_t prefetch_used() const { return prefetch_used_; }
   int capacity() const { return C_; }
 
  private:
   bool less_key(int a, int b) const;
+  int check_group(const int32_t* experts, int n, std::vector<int32_t>& g) const;
+  // slot for a fill of a non-resident expert outside `in_group`: the lowest
+  // free slot, else the victim's (which is evicted); victim out, -1 if none
+  int take_slot(const std::vector<char>& in_group, int& victim);
 
   int policy_, E_, C_, layer_;
-  int64_t clock_ = 0, misses_ = 0, hits_ = 0;
+  int64_t clock_ = 0, misses_ = 0, hits_ = 0, prefetches_ = 0, prefetch_used_ = 0;
+  std::vector<char> pending_;       // expert -> prefetched, not yet named by an access
   std::vector<int32_t> slot_of_;    // expert -> slot or -1
   std::vector<int32_t> expert_in_;  // slot -> expert or -1
   std::vector<int64_t> last_;       // expert -> clock of last use
