@@ -312,11 +312,22 @@ def stack_forward(h0: np.ndarray, layers: list, shape, forced_ids=None) -> dict:
 #  * an ensure() that names a pending expert counts a hit and marks the first
 #    use of the prefetched copy.
 # Event codes (the `hit` field): 0 miss, 1 hit, 2 prefetch fill, 3 hit on a
-# prefetched copy (its first use).
+# prefetched copy (its first use), 4 pin fill.
+#
+# Static / hybrid hot sets ([MS] "What the numbers say": a hot set measured on
+# one prompt did worse than LFU on another; [F51] "The simulator": static
+# per-layer and global hot sets against dynamic LRU, a static hot+warm sweep).
+# Readings:
+#  * pin(hot) on a cold pool puts the hot experts, in ascending id, into slots
+#    0 .. n-1; they are never victims; the other C - n slots stay dynamic under
+#    the policy;
+#  * hits on pinned experts are ordinary hits (they refresh last-use and
+#    counters like any hit);
+#  * a group fits when its experts outside the hot set number at most C - n.
 # ----------------------------------------------------------------------------
 
 LRU, LFU, LRU_FREQ = "lru", "lfu", "lru_freq"
-EV_MISS, EV_HIT, EV_PREFETCH, EV_PREFETCH_HIT = 0, 1, 2, 3
+EV_MISS, EV_HIT, EV_PREFETCH, EV_PREFETCH_HIT, EV_PIN = 0, 1, 2, 3, 4
 
 
 @dataclass
@@ -348,6 +359,7 @@ class CacheSim:
     sfreq: list = field(default_factory=list)
     events: list = field(default_factory=list)
     pending: set = field(default_factory=set)        # prefetched, not yet named by ensure()
+    pinned: set = field(default_factory=set)         # hot set: never evicted
     prefetches: int = 0
     prefetch_used: int = 0
 
@@ -370,8 +382,7 @@ class CacheSim:
         g = sorted(set(int(e) for e in group))
         if len(g) != len(list(group)):
             raise ValueError("group has repeated experts")
-        if len(g) > self.capacity:
-            raise ValueError("group larger than capacity")
+        self._check_fits(g)
         self.clock += 1
         in_group = set(g)
         for e in g:
@@ -395,7 +406,7 @@ class CacheSim:
             if free:
                 s = free[0]
             else:
-                cands = [x for x in self.slot_of if x not in in_group]
+                cands = [x for x in self.slot_of if x not in in_group and x not in self.pinned]
                 victim = min(cands, key=self._key)
                 s = self.slot_of.pop(victim)
                 self.pending.discard(victim)
@@ -410,14 +421,34 @@ class CacheSim:
                 self.sfreq = [f * 0.75 for f in self.sfreq]
         return [self.slot_of[int(e)] for e in group]
 
+    def _check_fits(self, g):
+        outside = [e for e in g if e not in self.pinned]
+        if len(outside) > self.capacity - len(self.pinned):
+            raise ValueError("group larger than capacity")
+
+    def pin(self, hot, step: int = 0) -> None:
+        """Hot set on a cold pool: slots 0 .. n-1 in ascending id, never evicted."""
+        h = sorted(set(int(e) for e in hot))
+        if len(h) != len(list(hot)):
+            raise ValueError("hot set has repeated experts")
+        if self.slot_of or self.clock or len(h) >= self.capacity:
+            raise ValueError("pin needs a cold pool and at least one dynamic slot")
+        for s, e in enumerate(h):
+            self.expert_in[s] = e
+            self.slot_of[e] = s
+            self.last[e] = 0
+            self.count[e] = 0
+            self.sfreq[s] = 1.0
+            self.pinned.add(e)
+            self.events.append(CacheEvent(step, self.layer, e, EV_PIN, s, -1))
+
     def prefetch(self, group, step: int = 0) -> None:
         """Speculative fill of the guessed experts that are not resident (no
         clock tick, no use); appends one EV_PREFETCH event per fill."""
         g = sorted(set(int(e) for e in group))
         if len(g) != len(list(group)):
             raise ValueError("group has repeated experts")
-        if len(g) > self.capacity:
-            raise ValueError("group larger than capacity")
+        self._check_fits(g)
         in_group = set(g)
         for e in g:
             if e in self.slot_of:
@@ -427,7 +458,7 @@ class CacheSim:
             if free:
                 s = free[0]
             else:
-                cands = [x for x in self.slot_of if x not in in_group]
+                cands = [x for x in self.slot_of if x not in in_group and x not in self.pinned]
                 victim = min(cands, key=self._key)
                 s = self.slot_of.pop(victim)
                 self.pending.discard(victim)
@@ -493,9 +524,12 @@ def opt_hits(groups, capacity: int):
     return hits, misses
 
 
-def policy_hits(policy: str, groups, n_experts: int, capacity: int):
-    """(hits, misses) of one online policy (CacheSim) over a group trace."""
+def policy_hits(policy: str, groups, n_experts: int, capacity: int, pinned=()):
+    """(hits, misses) of one online policy (CacheSim) over a group trace, with
+    an optional hot set pinned first."""
     sim = CacheSim(policy, n_experts, capacity)
+    if len(pinned):
+        sim.pin(pinned)
     for step, g in enumerate(groups):
         sim.ensure(g, step)
     return sim.hits, sim.misses

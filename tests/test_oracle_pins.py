@@ -577,3 +577,47 @@ def test_empty_prefetch_changes_nothing(policy):
         b.prefetch([], step=t)
         b.ensure(g, step=t)
     assert _ev(a) == _ev(b)
+
+
+# ---- static / hybrid hot sets in the slot-pool simulator -------------------------
+
+def test_pinned_expert_is_never_the_victim_lru():
+    # C=3 with expert 6 pinned in slot 0 (last-use 0, so LRU would drop it
+    # first were it not pinned): the miss of 3 evicts 1 instead (last 1,
+    # lower id than 2); a hit on 6 is an ordinary hit
+    sim = ora.CacheSim(ora.LRU, 8, 3)
+    sim.pin([6], step=0)
+    sim.ensure([1, 2], step=0)
+    sim.ensure([3], step=1)
+    sim.ensure([4, 6], step=2)
+    M, H, P = ora.EV_MISS, ora.EV_HIT, ora.EV_PIN
+    assert _ev(sim) == [(0, 6, P, 0, -1), (0, 1, M, 1, -1), (0, 2, M, 2, -1), (1, 3, M, 1, 1),
+                        (2, 6, H, 0, -1), (2, 4, M, 2, 2)]
+    assert (sim.hits, sim.misses) == (1, 4)
+
+
+def test_pinned_capacity_rules():
+    sim = ora.CacheSim(ora.LFU, 8, 3)
+    sim.pin([6, 7])
+    sim.ensure([1, 6, 7])              # one expert outside the hot set: fits one dynamic slot
+    with pytest.raises(ValueError):
+        sim.ensure([1, 2])             # two outside, one dynamic slot
+    with pytest.raises(ValueError):
+        ora.CacheSim(ora.LRU, 8, 3).pin([0, 1, 2])   # no dynamic slot left
+    warm = ora.CacheSim(ora.LRU, 8, 3)
+    warm.ensure([1])
+    with pytest.raises(ValueError):
+        warm.pin([2])                  # not a cold pool
+
+
+@pytest.mark.parametrize("policy", [ora.LRU, ora.LFU, ora.LRU_FREQ])
+def test_pinned_hot_set_always_hits(policy):
+    # every selection of a pinned expert is a hit, so hits >= those selections;
+    # pins are not misses
+    trace = fx.zipf_trace("pin-hot", 80, 1, 32, 6)[:, 0, :]
+    groups = [sorted(int(e) for e in g) for g in trace]
+    counts = ora.selection_counts(groups, 32)
+    hot = sorted(range(32), key=lambda e: (-int(counts[e]), e))[:8]
+    hits, misses = ora.policy_hits(policy, groups, 32, 14, pinned=hot)
+    assert hits >= int(sum(counts[e] for e in hot))
+    assert hits + misses == sum(len(g) for g in groups)
