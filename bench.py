@@ -312,6 +312,29 @@ def extra_prefetch(moe, fx, dev, stream, steps=64, layers=16):
     return res
 
 
+def hot_set_transfer(moe, fx, tr, E, k, C, steps, layers):
+    """Hybrid pools (half the slots pinned to a hot set, the rest LFU) and static
+    pools (all but k slots pinned) with the hot set calibrated on a trace with
+    the same popularity ranking ("same prompt") or another one ("other
+    prompt"); hit rates over the evaluation trace, means over layers."""
+    import numpy as np
+    same = fx.zipf_trace("bench-pool-zipf-calib", steps, layers, E, k, s=1.1, perm_cfg="bench-pool-zipf")
+    other = fx.zipf_trace("bench-pool-zipf-other", steps, layers, E, k, s=1.1)
+    accesses = steps * layers * k
+    res = {}
+    for n_hot, label in ((C // 2, "hybrid"), (C - k, "static")):
+        if n_hot <= 0:
+            continue
+        for calib, cname in ((same, "same_prompt"), (other, "other_prompt")):
+            h = 0
+            for l in range(layers):
+                cnt = np.bincount(calib[:, l, :].ravel(), minlength=E)
+                hot = sorted(sorted(range(E), key=lambda e: (-int(cnt[e]), e))[:n_hot])
+                h += moe.trace_policy_pinned("lfu", tr[:, l, :], E, C, hot)[0]
+            res[f"{label}{n_hot}_lfu_{cname}_hit_rate"] = round(h / accesses, 4)
+    return res
+
+
 def extra_trace_analysis(moe, fx, steps=256):
     """Offline policy sweep over seeded Zipf(1.1) routing traces (host engine of the
     library): per capacity C the hit rates of LRU / LFU / LRU-FREQ and of Belady's
@@ -349,6 +372,8 @@ def extra_trace_analysis(moe, fx, steps=256):
             row["opt_h2d_copies_per_token"] = round(tot["opt"][1] / steps, 2)
             row["static_pin_hit_rate"] = round(float(np.mean(
                 [moe.trace_top_share(tr[:, l, :], E, C) for l in range(layers)])), 4)
+            if name == "olmoe16" and C < E:
+                row.update(hot_set_transfer(moe, fx, tr, E, k, C, steps, layers))
             out[f"C{C}"] = row
         res[name] = out
     return res

@@ -127,6 +127,7 @@ typedef struct moe_cache_counters {
   uint64_t prefetches;     /* experts copied by moe_cache_prefetch (also counted
                               in h2d_bytes)                                       */
   uint64_t prefetch_used;  /* prefetched copies later named by moe_cache_ensure   */
+  uint64_t pinned;         /* experts of the hot set (moe_cache_pin)              */
 } moe_cache_counters;
 
 typedef struct moe_cache_event {
@@ -134,7 +135,8 @@ typedef struct moe_cache_event {
   int32_t layer;
   int32_t expert;
   int32_t hit;             /* 0 miss, 1 hit, 2 prefetch fill (moe_cache_prefetch),
-                              3 hit on a prefetched copy (its first use)          */
+                              3 hit on a prefetched copy (its first use),
+                              4 hot-set fill (moe_cache_pin)                      */
   int32_t slot;            /* slot the expert occupies after the call             */
   int32_t victim;          /* expert evicted from that slot, -1 if none           */
 } moe_cache_event;
@@ -302,7 +304,8 @@ moe_status moe_cache_prefetch(moe_ctx* ctx, int32_t layer, const int32_t* expert
  * layer l on x_l; when `prefetch` != 0 and l + 1 < layer_end, also route layer
  * l + 1 on x_l (the guess); read both id sets back to the host (this
  * synchronises `stream`); moe_cache_ensure(l, distinct ids of the T tokens);
- * moe_cache_prefetch(l + 1, distinct guessed ids) when the guess fits the pool;
+ * moe_cache_prefetch(l + 1, distinct guessed ids) when the guess fits the pool's
+ * dynamic slots (a guess that does not fit is not prefetched);
  * then the layer itself (as moe_stack_forward over [l, l + 1) with the routed
  * ids forced), so the guessed experts' copies run while layer l computes
  * ("An expert-offloading engine, from scratch", "What the numbers say").  The
@@ -317,6 +320,22 @@ moe_status moe_cache_prefetch(moe_ctx* ctx, int32_t layer, const int32_t* expert
 moe_status moe_stack_forward_pooled(moe_ctx* ctx, int32_t layer_begin, int32_t layer_end, float* h,
                                     int32_t T, int32_t prefetch, int32_t step, int32_t* ids_trace,
                                     int32_t* guess_trace, void* stream);
+
+/* Static / hybrid hot set ("An expert-offloading engine, from scratch", "What
+ * the numbers say": a hot set measured on one prompt did worse than LFU on
+ * another; "F51 Nitro / Nitro-MoE", "The simulator": static per-layer and
+ * global hot sets against dynamic LRU).  On a cold pool (no ensure, prefetch or
+ * pin on `layer` yet), the experts (host int32 [n], distinct) take slots
+ * 0 .. n-1 in ascending id, are copied from the pinned backing on the side
+ * stream and published in `stream` order; they are never evicted, and every
+ * later group must have at most C - n experts outside the hot set
+ * (MOE_E_CAPACITY from moe_cache_ensure otherwise).  The other slots stay
+ * dynamic under the configured policy.  Returns MOE_E_ARG for a bad or repeated
+ * id or a pool that is not cold, MOE_E_CAPACITY when n >= C, MOE_E_TRANSFER when
+ * a copy cannot be enqueued (nothing changes).  With MOE_RESIDENT_ALL it does
+ * nothing. */
+moe_status moe_cache_pin(moe_ctx* ctx, int32_t layer, const int32_t* experts, int32_t n, int32_t step,
+                         void* stream);
 
 /* The stack's normalisation on its own: x = fp16(h / sqrt(mean(h^2) + 1e-5)),
  * unit weight, per token.  h: dev FP32 [T,H]; x: dev FP16 [T,H] out;
@@ -356,6 +375,8 @@ void moe_policy_free(moe_policy_engine* p);
  * slots [n] out in the order of `experts`; events appended to the engine's log. */
 moe_status moe_policy_access(moe_policy_engine* p, const int32_t* experts, int32_t n,
                              int32_t step, int32_t* slots);
+/* The decision part of moe_cache_pin (MOE_E_ARG for a pool that is not cold). */
+moe_status moe_policy_pin(moe_policy_engine* p, const int32_t* experts, int32_t n, int32_t step);
 /* The decision part of moe_cache_prefetch (same rules and return codes). */
 moe_status moe_policy_prefetch(moe_policy_engine* p, const int32_t* experts, int32_t n,
                                int32_t step);
@@ -386,6 +407,14 @@ moe_status moe_trace_opt(const int32_t* ids, int32_t n_steps, int32_t width, int
  * one access per row (the same engine as moe_policy_access). */
 moe_status moe_trace_policy(int32_t policy, const int32_t* ids, int32_t n_steps, int32_t width,
                             int32_t n_experts, int32_t capacity, int64_t* hits, int64_t* misses);
+/* moe_trace_policy with the hot set `hot` (host int32 [n_hot], distinct) pinned
+ * first, as moe_cache_pin does: those experts are never evicted and count as
+ * hits whenever named; the other capacity - n_hot slots run the policy.
+ * MOE_E_CAPACITY when n_hot >= capacity or a row has more than
+ * capacity - n_hot experts outside the hot set. */
+moe_status moe_trace_policy_pinned(int32_t policy, const int32_t* ids, int32_t n_steps, int32_t width,
+                                   int32_t n_experts, int32_t capacity, const int32_t* hot, int32_t n_hot,
+                                   int64_t* hits, int64_t* misses);
 /* Share of all selections (selection = a row naming an expert) that fall on the
  * n_top most-selected experts, ties to the lower id: the hit rate of a static
  * pin of those experts.  0 for an empty trace. */

@@ -255,3 +255,48 @@ def test_pool_prefetch_argument_errors(moe, olmoe_layers):
         res.stack_forward_pooled(h=torch.zeros((1, fx.OLMOE.hidden), device="cuda"))
     assert e.value.status == capi.MOE_E_ARG
     res.close()
+
+
+# ---- static / hybrid hot sets -------------------------------------------------------
+
+def _hot_sets(n_hot):
+    """Per layer, the n_hot most-selected experts of a calibration trace with the
+    same popularity ranking as the test trace (other draws)."""
+    calib = fx.zipf_trace("pool-zipf-calib", 128, L, fx.OLMOE.n_experts, fx.OLMOE.top_k, s=1.1,
+                          perm_cfg="pool-zipf")
+    hot = []
+    for l in range(L):
+        cnt = np.bincount(calib[:, l, :].ravel(), minlength=fx.OLMOE.n_experts)
+        hot.append(sorted(sorted(range(fx.OLMOE.n_experts), key=lambda e: (-int(cnt[e]), e))[:n_hot]))
+    return hot
+
+
+@pytest.mark.parametrize("policy,C,n_hot", [("lfu", 24, 12), ("lru", 32, 20)])
+def test_pool_hot_set_bit_identical_and_decisions_match_oracle(moe, olmoe_layers, trace, h0s, resident_out,
+                                                              policy, C, n_hot):
+    say(f"test_pool_hot_set policy={policy} C={C} hot={n_hot}")
+    hot = _hot_sets(n_hot)
+    ctx = _ctx(moe, olmoe_layers, policy=policy, slots=C)
+    for l in range(L):
+        ctx.cache_pin(l, hot[l], step=0)
+    out = _run(ctx, trace, h0s, pooled=True)
+    assert torch.equal(out, resident_out), "hot set changed the output"
+    blob = fx.OLMOE.blob_bytes
+    rates = []
+    for l in range(L):
+        sim = ora.CacheSim(POLICY_ORACLE[policy], fx.OLMOE.n_experts, C, layer=l)
+        sim.pin(hot[l], 0)
+        for s in range(STEPS):
+            sim.ensure(trace[s, l].tolist(), s)
+        assert ctx.cache_events(l) == [e.as_tuple() for e in sim.events], f"layer {l}"
+        st = ctx.cache_stats(l)
+        assert st["pinned"] == n_hot and st["hits"] == sim.hits and st["misses"] == sim.misses
+        assert st["h2d_bytes"] == (sim.misses + n_hot) * blob
+        rates.append(st["hits"] / st["accesses"])
+    say(f"  mean hit rate {np.mean(rates):.3f}")
+    # a pin is for a cold pool only
+    from w4a16_routed_expert_router_amd import MoEError, capi
+    with pytest.raises(MoEError) as e:
+        ctx.cache_pin(0, [63])
+    assert e.value.status == capi.MOE_E_ARG
+    ctx.close()

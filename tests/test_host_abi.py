@@ -221,3 +221,64 @@ def test_policy_engine_prefetch_rejects_bad_guesses():
             eng.prefetch(bad)
         assert e.value.status == code
     assert eng.events() == []
+
+
+@pytest.mark.parametrize("policy", ["lru", "lfu", "lru_freq"])
+def test_policy_engine_pin_matches_oracle(policy):
+    from w4a16_routed_expert_router_amd import PolicyEngine
+    rng = np.random.default_rng(7)
+    tr = fx.zipf_trace("abi-pin", 100, 1, 64, 8)[:, 0, :]
+    hot = sorted(int(e) for e in rng.choice(64, size=10, replace=False))
+    eng = PolicyEngine(policy, 64, 20, layer=1)
+    sim = ora.CacheSim(policy, 64, 20, layer=1)
+    eng.pin(hot, step=0)
+    sim.pin(hot, step=0)
+    for t in range(len(tr)):
+        if t and rng.random() < 0.5:
+            guess = _noisy_guess(rng, tr[t], 64, 0.3)
+            try:
+                sim.prefetch(guess, step=t)
+                eng.prefetch(guess, step=t)
+            except ValueError:
+                pass                                  # a guess that does not fit is refused by both
+        eng.access(tr[t], step=t)
+        sim.ensure(tr[t], step=t)
+    assert eng.events() == [e.as_tuple() for e in sim.events]
+
+
+@pytest.mark.parametrize("C,n_hot", [(16, 8), (24, 12), (32, 24)])
+def test_trace_policy_pinned_matches_oracle(C, n_hot):
+    import w4a16_routed_expert_router_amd as moe
+    tr = fx.zipf_trace("abi-pin-trace", 96, 2, 64, 8)
+    calib = fx.zipf_trace("abi-pin-calib", 96, 2, 64, 8)
+    for layer in range(2):
+        rows = tr[:, layer, :]
+        groups = _oracle_groups(rows)
+        cnt = ora.selection_counts(_oracle_groups(calib[:, layer, :]), 64)
+        hot = sorted(sorted(range(64), key=lambda e: (-int(cnt[e]), e))[:n_hot])
+        for pol in ("lru", "lfu", "lru_freq"):
+            assert moe.trace_policy_pinned(pol, rows, 64, C, hot) == ora.policy_hits(pol, groups, 64, C, pinned=hot)
+
+
+def test_pin_rejections():
+    import w4a16_routed_expert_router_amd as moe
+    from w4a16_routed_expert_router_amd import MoEError, PolicyEngine, capi
+    eng = PolicyEngine("lru", 16, 4)
+    for bad, code in (([1, 1], capi.MOE_E_ARG), ([16], capi.MOE_E_ARG), ([0, 1, 2, 3], capi.MOE_E_CAPACITY)):
+        with pytest.raises(MoEError) as e:
+            eng.pin(bad)
+        assert e.value.status == code
+    eng.access([5])
+    with pytest.raises(MoEError) as e:
+        eng.pin([1])                                   # not a cold pool
+    assert e.value.status == capi.MOE_E_ARG
+    eng2 = PolicyEngine("lfu", 16, 4)
+    eng2.pin([0, 1])
+    with pytest.raises(MoEError) as e:
+        eng2.access([2, 3, 4])                         # three outside the hot set, two dynamic slots
+    assert e.value.status == capi.MOE_E_CAPACITY
+    eng2.access([0, 1, 2, 3])
+    rows = np.array([[0, 1, 2]], dtype=np.int32)
+    with pytest.raises(MoEError) as e:
+        moe.trace_policy_pinned("lru", rows, 8, 3, [5, 6])   # 2 dynamic slots, 3 outside
+    assert e.value.status == capi.MOE_E_CAPACITY

@@ -193,6 +193,11 @@ class MoEContext:
             _stream(stream, self.device)))
         return (ids, gs) if trace else None
 
+    def cache_pin(self, layer, experts, step=0, stream=None):
+        e = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+        self._check(_lib.moe_cache_pin(self._h, layer, e.ctypes.data, e.size, step,
+                                       _stream(stream, self.device)))
+
     def rmsnorm(self, h, out=None, stream=None):
         sh = self.shape
         T = h.shape[0]
@@ -265,6 +270,12 @@ class PolicyEngine:
             raise MoEError(st, "policy access rejected")
         return slots
 
+    def pin(self, experts, step=0):
+        e = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+        st = _lib.moe_policy_pin(self._h, e.ctypes.data, e.size, step)
+        if st != capi.MOE_OK:
+            raise MoEError(st, "policy pin rejected")
+
     def prefetch(self, experts, step=0):
         e = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
         st = _lib.moe_policy_prefetch(self._h, e.ctypes.data, e.size, step)
@@ -314,6 +325,19 @@ def trace_policy(policy, ids, n_experts, capacity):
                                C.byref(h), C.byref(m))
     if st != capi.MOE_OK:
         raise MoEError(st, "trace_policy rejected the trace")
+    return h.value, m.value
+
+
+def trace_policy_pinned(policy, ids, n_experts, capacity, hot):
+    """(hits, misses) of a policy over one layer's trace with the hot set pinned first."""
+    a = _trace(ids)
+    p = POLICIES[policy] if isinstance(policy, str) else int(policy)
+    hh = np.ascontiguousarray(np.asarray(hot, dtype=np.int32))
+    h, m = C.c_int64(), C.c_int64()
+    st = _lib.moe_trace_policy_pinned(p, a.ctypes.data, a.shape[0], a.shape[1], n_experts, capacity,
+                                      hh.ctypes.data, hh.size, C.byref(h), C.byref(m))
+    if st != capi.MOE_OK:
+        raise MoEError(st, "trace_policy_pinned rejected the trace")
     return h.value, m.value
 
 

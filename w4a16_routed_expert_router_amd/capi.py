@@ -37,7 +37,7 @@ class moe_cache_counters(C.Structure):
     _fields_ = [("accesses", C.c_uint64), ("hits", C.c_uint64), ("misses", C.c_uint64),
                 ("evictions", C.c_uint64), ("h2d_bytes", C.c_uint64), ("d2h_bytes", C.c_uint64),
                 ("failures", C.c_uint64), ("h2d_seconds", C.c_double),
-                ("prefetches", C.c_uint64), ("prefetch_used", C.c_uint64)]
+                ("prefetches", C.c_uint64), ("prefetch_used", C.c_uint64), ("pinned", C.c_uint64)]
 
 
 class moe_skew_report(C.Structure):
@@ -67,6 +67,7 @@ SIGNATURES = {
     "moe_check_device_errors": (_I, [_P, _P, C.POINTER(C.c_uint32)]),
     "moe_cache_ensure": (_I, [_P, _I, _P, _I, _P, _I, _P]),
     "moe_cache_prefetch": (_I, [_P, _I, _P, _I, _I, _P]),
+    "moe_cache_pin": (_I, [_P, _I, _P, _I, _I, _P]),
     "moe_rmsnorm": (_I, [_P, _P, _I, _P, _P]),
     "moe_stack_forward_pooled": (_I, [_P, _I, _I, _P, _I, _I, _I, _P, _P, _P]),
     "moe_cache_stats": (_I, [_P, _I, C.POINTER(moe_cache_counters)]),
@@ -79,6 +80,8 @@ SIGNATURES = {
     "moe_policy_free": (None, [_P]),
     "moe_policy_access": (_I, [_P, _P, _I, _I, _P]),
     "moe_policy_prefetch": (_I, [_P, _P, _I, _I]),
+    "moe_policy_pin": (_I, [_P, _P, _I, _I]),
+    "moe_trace_policy_pinned": (_I, [_I, _P, _I, _I, _I, _I, _P, _I, C.POINTER(C.c_int64), C.POINTER(C.c_int64)]),
     "moe_policy_event_count": (_I, [_P]),
     "moe_policy_events": (_I, [_P, C.POINTER(moe_cache_event), _I]),
     "moe_trace_opt": (_I, [_P, _I, _I, _I, _I, C.POINTER(C.c_int64), C.POINTER(C.c_int64)]),

@@ -824,6 +824,67 @@ moe_status moe_cache_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts,
   return MOE_OK;
 }
 
+moe_status moe_cache_pin(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int32_t step,
+                         void* stream) {
+  if (moe_status st = check_ctx(c)) return st;
+  if (moe_status st = check_layer(c, layer)) return st;
+  if (n < 0 || (n > 0 && !experts)) return fail(c, MOE_E_ARG, "bad experts");
+  const moe_config& g = c->cfg;
+  for (int i = 0; i < n; ++i)
+    if (experts[i] < 0 || experts[i] >= g.n_experts) return fail(c, MOE_E_ARG, "expert id out of range");
+  if (!pooled(c)) return MOE_OK;
+  LayerState& L = c->layers[layer];
+  hipStream_t s = (hipStream_t)stream;
+  const PolicyEngine saved = *L.policy;
+  std::vector<PolicyEngine::Decision> dec;
+  const int rc = L.policy->pin(experts, n, step, dec);
+  if (rc == 2) return fail(c, MOE_E_CAPACITY, "a hot set must leave at least one dynamic slot");
+  if (rc == 3) return fail(c, MOE_E_ARG, "a hot set is pinned on a cold pool only");
+  if (rc != 0) return fail(c, MOE_E_ARG, "repeated expert in hot set");
+  if (dec.empty()) return MOE_OK;
+  const int64_t blob = c->lay.total();
+  bool good = true;
+  hipEvent_t t0 = nullptr, t1 = nullptr;
+  good = good && hipEventCreate(&t0) == hipSuccess && hipEventCreate(&t1) == hipSuccess;
+  good = good && hipStreamWaitEvent(c->side, L.retired, 0) == hipSuccess;
+  good = good && hipEventRecord(t0, c->side) == hipSuccess;
+  for (const auto& d : dec) {
+    if (!good) break;
+    good = hipMemcpyAsync(L.store + (int64_t)d.slot * blob, L.backing + (int64_t)d.expert * blob,
+                          (size_t)blob, hipMemcpyHostToDevice, c->side) == hipSuccess;
+  }
+  good = good && hipEventRecord(t1, c->side) == hipSuccess;
+  good = good && hipEventRecord(L.ready, c->side) == hipSuccess;
+  good = good && hipStreamWaitEvent(s, L.ready, 0) == hipSuccess;
+  if (!good) {
+    (void)hipGetLastError();
+    if (t0) (void)hipEventDestroy(t0);
+    if (t1) (void)hipEventDestroy(t1);
+    *L.policy = saved;
+    L.stats.failures += 1;
+    return fail(c, MOE_E_TRANSFER, "hot-set transfer failed; nothing was published");
+  }
+  L.timing.emplace_back(t0, t1);
+  PublishArgs pa{};
+  pa.map = L.map;
+  for (const auto& d : dec) {
+    if (pa.n == kMaxPublish) {
+      launch_publish(pa, s);
+      pa.n = 0;
+    }
+    pa.u[pa.n++] = PublishUpdate{d.expert, d.slot};
+  }
+  if (pa.n) launch_publish(pa, s);
+  if (hipGetLastError() != hipSuccess) {
+    c->faulted = true;
+    L.stats.failures += 1;
+    return fail(c, MOE_E_FAULTED, "failure after a hot set was published: context faulted");
+  }
+  L.stats.pinned += dec.size();
+  L.stats.h2d_bytes += (uint64_t)dec.size() * blob;
+  return MOE_OK;
+}
+
 moe_status moe_stack_forward_pooled(moe_ctx* c, int32_t layer_begin, int32_t layer_end, float* h, int32_t T,
                                     int32_t prefetch, int32_t step, int32_t* ids_trace, int32_t* guess_trace,
                                     void* stream) {
@@ -868,10 +929,12 @@ moe_status moe_stack_forward_pooled(moe_ctx* c, int32_t layer_begin, int32_t lay
       return st;
     if (guess_next) {
       group_of(gids_h, guess);
-      // a guess larger than the pool is not prefetched
-      if ((int32_t)guess.size() <= g.slots_per_layer)
-        if (moe_status st = moe_cache_prefetch(c, l + 1, guess.data(), (int32_t)guess.size(), step, stream))
-          return st;
+      // a guess that does not fit the pool's dynamic slots is not prefetched
+      // (the engine is left unchanged by that refusal)
+      if ((int32_t)guess.size() <= g.slots_per_layer) {
+        const moe_status st = moe_cache_prefetch(c, l + 1, guess.data(), (int32_t)guess.size(), step, stream);
+        if (st != MOE_OK && st != MOE_E_CAPACITY) return st;
+      }
     }
     // the layer itself, routed by the ids just read (the same router, the same x)
     if (moe_status st = moe_stack_forward(c, l, l + 1, h, T, c->pool_ids, nullptr, nullptr, nullptr, stream))

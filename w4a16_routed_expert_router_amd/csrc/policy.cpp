@@ -28,6 +28,14 @@
 // resident is filled like a miss (last = the current clock, LFU count
 // unchanged, sfreq = 1), is not a miss for the LRU-FREQ decay, and stays
 // pending until an access names it, which counts a hit on the prefetched copy.
+//
+// Static / hybrid hot sets ("An expert-offloading engine, from scratch", "What
+// the numbers say": a hot set measured on one prompt did worse than LFU on
+// another; "F51 Nitro / Nitro-MoE", "The simulator": static per-layer and
+// global hot sets against dynamic LRU): pinned experts fill slots 0 .. n-1 of a
+// cold pool in ascending id and are never victims; the other slots stay
+// dynamic, and a group fits when its experts outside the hot set number at
+// most C - n.
 #include "policy.hpp"
 
 #include <algorithm>
@@ -36,7 +44,7 @@ namespace moe {
 
 PolicyEngine::PolicyEngine(int policy, int n_experts, int capacity, int layer)
     : policy_(policy), E_(n_experts), C_(capacity), layer_(layer),
-      pending_(n_experts, 0), slot_of_(n_experts, -1), expert_in_(capacity, -1), last_(n_experts, 0),
+      pending_(n_experts, 0), pinned_(n_experts, 0), slot_of_(n_experts, -1), expert_in_(capacity, -1), last_(n_experts, 0),
       count_(n_experts, 0), sfreq_(capacity, 0.0) {}
 
 #pragma clang fp contract(off)
@@ -74,6 +82,39 @@ int PolicyEngine::check_group(const int32_t* experts, int n, std::vector<int32_t
   std::sort(g.begin(), g.end());
   for (int i = 1; i < n; ++i)
     if (g[i] == g[i - 1]) return 1;
+  int outside = 0;
+  for (int e : g) outside += pinned_[e] ? 0 : 1;
+  if (outside > C_ - n_pinned_) return 2;
+  return 0;
+}
+
+int PolicyEngine::pin(const int32_t* experts, int n, int step, std::vector<Decision>& out) {
+  out.clear();
+  std::vector<int32_t> g;
+  if (n < 0) return 1;
+  g.assign(experts, experts + n);
+  for (int e : g)
+    if (e < 0 || e >= E_) return 1;
+  std::sort(g.begin(), g.end());
+  for (int i = 1; i < n; ++i)
+    if (g[i] == g[i - 1]) return 1;
+  if (n >= C_) return 2;
+  bool cold = clock_ == 0 && n_pinned_ == 0;
+  for (int s = 0; s < C_; ++s) cold = cold && expert_in_[s] < 0;
+  if (!cold) return 3;
+  for (int i = 0; i < n; ++i) {
+    const int e = g[i];
+    expert_in_[i] = e;
+    slot_of_[e] = i;
+    last_[e] = 0;
+    count_[e] = 0;
+    sfreq_[i] = 1.0;
+    pinned_[e] = 1;
+    out.push_back(Decision{e, i, -1, false, kPin});
+  }
+  n_pinned_ = n;
+  for (const Decision& d : out)
+    log_.push_back(moe_cache_event{step, layer_, d.expert, d.kind, d.slot, d.victim});
   return 0;
 }
 
@@ -83,7 +124,7 @@ int PolicyEngine::take_slot(const std::vector<char>& in_group, int& victim) {
     if (expert_in_[s] < 0) return s;
   for (int s = 0; s < C_; ++s) {
     const int x = expert_in_[s];
-    if (in_group[x]) continue;
+    if (in_group[x] || pinned_[x]) continue;
     if (victim < 0 || less_key(x, victim)) victim = x;
   }
   const int slot = slot_of_[victim];
@@ -196,6 +237,13 @@ moe_status moe_policy_prefetch(moe_policy_engine* p, const int32_t* experts, int
   if (rc == 1) return MOE_E_ARG;
   if (rc == 2) return MOE_E_CAPACITY;
   return MOE_OK;
+}
+moe_status moe_policy_pin(moe_policy_engine* p, const int32_t* experts, int32_t n, int32_t step) {
+  if (!p || (n > 0 && !experts)) return MOE_E_ARG;
+  std::vector<moe::PolicyEngine::Decision> d;
+  const int rc = p->eng.pin(experts, n, step, d);
+  if (rc == 2) return MOE_E_CAPACITY;
+  return rc == 0 ? MOE_OK : MOE_E_ARG;
 }
 int32_t moe_policy_event_count(const moe_policy_engine* p) {
   return p ? (int32_t)p->eng.log().size() : 0;

@@ -12,7 +12,7 @@ namespace moe {
 class PolicyEngine {
  public:
   // event kinds (the `hit` field of moe_cache_event)
-  enum Kind { kMiss = 0, kHit = 1, kPrefetch = 2, kPrefetchHit = 3 };
+  enum Kind { kMiss = 0, kHit = 1, kPrefetch = 2, kPrefetchHit = 3, kPin = 4 };
   struct Decision {
     int32_t expert;
     int32_t slot;
@@ -31,6 +31,12 @@ class PolicyEngine {
   // expert that is not resident is filled like a miss and stays pending until
   // an access names it.  Same return codes; `out` gets the fills.
   int prefetch(const int32_t* experts, int n, int step, std::vector<Decision>& out);
+  // Hot set on a cold pool: the experts (ascending id) take slots 0 .. n-1 and
+  // are never victims.  0 ok, 1 bad or repeated id, 2 n >= C (no dynamic slot
+  // left), 3 the pool is not cold.  `out` gets the fills.
+  int pin(const int32_t* experts, int n, int step, std::vector<Decision>& out);
+  int pinned_count() const { return n_pinned_; }
+  bool is_pinned(int e) const { return pinned_[e] != 0; }
 
   int32_t slot_of(int e) const { return slot_of_[e]; }
   const std::vector<moe_cache_event>& log() const { return log_; }
@@ -50,6 +56,8 @@ class PolicyEngine {
   int policy_, E_, C_, layer_;
   int64_t clock_ = 0, misses_ = 0, hits_ = 0, prefetches_ = 0, prefetch_used_ = 0;
   std::vector<char> pending_;       // expert -> prefetched, not yet named by an access
+  std::vector<char> pinned_;        // expert -> in the hot set (never a victim)
+  int n_pinned_ = 0;
   std::vector<int32_t> slot_of_;    // expert -> slot or -1
   std::vector<int32_t> expert_in_;  // slot -> expert or -1
   std::vector<int64_t> last_;       // expert -> clock of last use

@@ -153,6 +153,29 @@ moe_status moe_trace_policy(int32_t policy, const int32_t* ids, int32_t n_steps,
   return MOE_OK;
 }
 
+moe_status moe_trace_policy_pinned(int32_t policy, const int32_t* ids, int32_t n_steps, int32_t width,
+                                   int32_t n_experts, int32_t capacity, const int32_t* hot, int32_t n_hot,
+                                   int64_t* hits, int64_t* misses) {
+  if (policy < MOE_POLICY_LRU || policy > MOE_POLICY_LRU_FREQ) return MOE_E_ARG;
+  if (bad_trace_args(ids, n_steps, width, n_experts) || capacity < 1 || !hits || !misses) return MOE_E_ARG;
+  if (n_hot < 0 || (n_hot > 0 && !hot)) return MOE_E_ARG;
+  std::vector<std::vector<int32_t>> gs;
+  if (!trace_groups(ids, n_steps, width, n_experts, gs)) return MOE_E_ARG;
+  moe::PolicyEngine eng(policy, n_experts, capacity, 0);
+  std::vector<moe::PolicyEngine::Decision> d;
+  const int prc = eng.pin(hot, n_hot, 0, d);
+  if (prc == 2) return MOE_E_CAPACITY;
+  if (prc != 0) return MOE_E_ARG;
+  for (int32_t t = 0; t < n_steps; ++t) {
+    const int rc = eng.access(gs[t].data(), (int)gs[t].size(), t, d);
+    if (rc == 2) return MOE_E_CAPACITY;
+    if (rc != 0) return MOE_E_ARG;
+  }
+  *hits = eng.hits();
+  *misses = eng.misses();
+  return MOE_OK;
+}
+
 moe_status moe_trace_top_share(const int32_t* ids, int32_t n_steps, int32_t width, int32_t n_experts,
                                int32_t n_top, double* share) {
   if (bad_trace_args(ids, n_steps, width, n_experts) || n_top < 0 || !share) return MOE_E_ARG;
