@@ -225,9 +225,9 @@ def extra_pool(moe, fx, dev, stream, steps=256, layers=16):
     h0s = torch.stack([fx.activations(("bench-pool-h0", i), 1, shape.hidden, device="cuda").float()
                        for i in range(32)])
 
-    def run(policy, C):
+    def run(policy, C, **kw):
         ctx = moe.MoEContext(shape, n_layers=layers, max_tokens=1,
-                             policy=policy, slots=C)
+                             policy=policy, slots=C, **kw)
         for l, w in enumerate(lw):
             ctx.register_layer(l, w)
         outs = torch.empty((steps, 1, shape.hidden), dtype=torch.float32, device=dev)
@@ -249,13 +249,15 @@ def extra_pool(moe, fx, dev, stream, steps=256, layers=16):
 
     ref, dt_ref, _ = run("resident", 0)
     res = {"steps": steps, "layers": layers, "resident_tokens_per_s": round(steps / dt_ref, 1)}
-    for policy, C in (("lru", 16), ("lfu", 16), ("lru", 32), ("lfu", 32), ("lru", 48), ("lfu", 48)):
-        out, dt, st = run(policy, C)
+    staged = dict(flags=moe.capi.MOE_FLAG_STAGED_TRANSPORT, staging_blobs=4, spare_rows=8)
+    for policy, C, kw in (("lru", 16, {}), ("lfu", 16, {}), ("lru", 32, {}), ("lfu", 32, {}), ("lru", 48, {}),
+                          ("lfu", 48, {}), ("lfu", 32, staged)):
+        out, dt, st = run(policy, C, **kw)
         acc = sum(x["accesses"] for x in st)
         hits = sum(x["hits"] for x in st)
         h2d = sum(x["h2d_bytes"] for x in st)
         h2d_s = sum(x["h2d_seconds"] for x in st)
-        res[f"{policy}_C{C}"] = {
+        res[f"{policy}_C{C}" + ("_staged_transport" if kw else "")] = {
             "hit_rate": round(hits / max(acc, 1), 4),
             "h2d_gb": round(h2d / 1e9, 3),
             "h2d_gbps_copy": round(h2d / max(h2d_s, 1e-12) / 1e9, 2),

@@ -95,6 +95,23 @@ typedef enum moe_policy {
 #define MOE_FLAG_FORCE_MFMA 4u          /* take the MFMA path for every expert */
 #define MOE_FLAG_NO_FUSED 8u            /* stacks: never take the fused one-launch
                                            decode path (use per-layer kernels)  */
+#define MOE_FLAG_STAGED_TRANSPORT 16u   /* slot pools: the staged miss transport
+                                           ("Horizon RunMap", "Partial-residency
+                                           contract: immutable authority and miss
+                                           lifecycle"): the complete host source
+                                           is immutable pageable RAM, each miss
+                                           goes RAM -> one of `staging_blobs`
+                                           pinned staging buffers (reused once its
+                                           transfer has completed) -> an
+                                           unpublished spare GPU row, the routed
+                                           group is published after its transfers
+                                           complete, and a victim's row is reused
+                                           only after the consumers of the old
+                                           generation have retired (no wait for
+                                           them before a copy).  Needs
+                                           staging_blobs >= 1 and spare_rows >=
+                                           min(C, max_tokens*k), else moe_create
+                                           fails with MOE_E_CAPACITY             */
 
 typedef struct moe_config {
   int32_t hidden;          /* H, multiple of 256                                  */
@@ -111,6 +128,10 @@ typedef struct moe_config {
   int32_t policy;          /* moe_policy                                          */
   int32_t slots_per_layer; /* C, slot-pool capacity per layer (policy != 0)       */
   uint32_t flags;          /* MOE_FLAG_*                                          */
+  int32_t staging_blobs;   /* MOE_FLAG_STAGED_TRANSPORT: pinned staging buffers of
+                              one expert blob each (context-wide)                 */
+  int32_t spare_rows;      /* MOE_FLAG_STAGED_TRANSPORT: GPU rows per layer beyond
+                              the C slots, which misses land in unpublished       */
 } moe_config;
 
 typedef struct moe_cache_counters {

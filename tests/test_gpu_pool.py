@@ -300,3 +300,64 @@ def test_pool_hot_set_bit_identical_and_decisions_match_oracle(moe, olmoe_layers
         ctx.cache_pin(0, [63])
     assert e.value.status == capi.MOE_E_ARG
     ctx.close()
+
+
+# ---- staged transport: pageable source, pinned staging, spare rows, leases --------
+
+STAGED = dict(flags=16, staging_blobs=2, spare_rows=8)
+
+
+@pytest.mark.parametrize("policy,C", [("lfu", 16), ("lru_freq", 24)])
+def test_pool_staged_transport_bit_identical_and_decisions_match_oracle(moe, olmoe_layers, trace, h0s,
+                                                                       resident_out, policy, C):
+    say(f"test_pool_staged policy={policy} C={C}")
+    ctx = _ctx(moe, olmoe_layers, policy=policy, slots=C, **STAGED)
+    out = _run(ctx, trace, h0s, pooled=True)
+    assert torch.equal(out, resident_out), "staged transport changed the output"
+    blob = fx.OLMOE.blob_bytes
+    for l in range(L):
+        sim = ora.CacheSim(POLICY_ORACLE[policy], fx.OLMOE.n_experts, C, layer=l)
+        for s in range(STEPS):
+            sim.ensure(trace[s, l].tolist(), s)
+        assert ctx.cache_events(l) == [e.as_tuple() for e in sim.events], f"layer {l}"
+        st = ctx.cache_stats(l)
+        assert st["misses"] == sim.misses and st["h2d_bytes"] == sim.misses * blob and st["d2h_bytes"] == 0
+    ctx.close()
+
+
+def test_pool_staged_transport_natural_routing_prefetch_and_hot_set(moe, olmoe_layers, h0s):
+    # natural routing with prefetch and a pinned hot set: the staged transport
+    # gives the same bits and the same decisions as the pinned-backing one
+    say("test_pool_staged_natural")
+    hot = [sorted(range(4 * (l % 3), 4 * (l % 3) + 4)) for l in range(L)]
+    res = {}
+    for mode, kw in (("direct", {}), ("staged", STAGED)):
+        ctx = _ctx(moe, olmoe_layers, policy="lru", slots=16, **kw)
+        for l in range(L):
+            ctx.cache_pin(l, hot[l])
+        out, ids, gs = _run_natural(ctx, h0s, True)
+        res[mode] = (out, ids, [ctx.cache_events(l) for l in range(L)])
+        ctx.close()
+    assert torch.equal(res["staged"][0], res["direct"][0])
+    assert np.array_equal(res["staged"][1], res["direct"][1])
+    assert res["staged"][2] == res["direct"][2]
+
+
+def test_pool_staged_transfer_failure_before_publication_keeps_state(moe, olmoe_layers, trace, h0s):
+    say("test_pool_staged_transfer_failure")
+    ctx = _ctx(moe, olmoe_layers, policy="lfu", slots=16, **STAGED)
+    _run(ctx, trace, h0s, pooled=True, steps=10)
+    sim = ora.CacheSim(ora.LFU, fx.OLMOE.n_experts, 16, layer=5)
+    for s in range(10):
+        sim.ensure(trace[s, 5].tolist(), s)
+    miss_group = np.array([e for e in range(fx.OLMOE.n_experts) if e not in sim.slot_of][:8], dtype=np.int32)
+    before = ctx.cache_events(5)
+    ctx.inject_transfer_failure(5, 1)
+    with pytest.raises(moe.MoEError) as ei:
+        ctx.cache_ensure(5, miss_group, step=99)
+    assert ei.value.status == 7          # MOE_E_TRANSFER: the old generation stays authoritative
+    assert ctx.cache_events(5) == before
+    ctx.cache_ensure(5, miss_group, step=99)
+    sim.ensure(miss_group.tolist(), 99)
+    assert ctx.cache_events(5) == [e.as_tuple() for e in sim.events]
+    ctx.close()

@@ -45,7 +45,11 @@ def test_create_rejects_bad_configs_without_touching_a_gpu():
                 slots_per_layer=0, flags=0)
     bad = [dict(hidden=100), dict(inter=4096), dict(top_k=0), dict(top_k=65, n_experts=64),
            dict(group=64), dict(max_tokens=0), dict(policy=7),
-           dict(policy=1, slots_per_layer=4)]          # C < min(E, T*k) = 32
+           dict(policy=1, slots_per_layer=4),          # C < min(E, T*k) = 32
+           # staged transport without staging, or with fewer spare rows than
+           # the misses one call can have (min(C, T*k) = 32): startup fails
+           dict(policy=1, slots_per_layer=32, flags=16, staging_blobs=0, spare_rows=32),
+           dict(policy=1, slots_per_layer=32, flags=16, staging_blobs=2, spare_rows=31)]
     for b in bad:
         cfg = capi.moe_config(**{**good, **b})
         h = C.c_void_p()

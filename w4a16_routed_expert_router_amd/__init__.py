@@ -52,7 +52,7 @@ class MoEContext:
     """One library context: `n_layers` MoE layers of one shape on one device."""
 
     def __init__(self, shape, n_layers=1, max_tokens=64, device=0, policy="resident",
-                 slots=0, flags=0):
+                 slots=0, flags=0, staging_blobs=0, spare_rows=0):
         self.shape = shape
         self.n_layers = n_layers
         self.max_tokens = max_tokens
@@ -62,7 +62,8 @@ class MoEContext:
                               top_k=shape.top_k, renorm=int(shape.renorm), n_layers=n_layers,
                               shared_inter=shape.shared_inter, group=shape.group,
                               max_tokens=max_tokens, device=device, policy=self.policy,
-                              slots_per_layer=slots, flags=flags)
+                              slots_per_layer=slots, flags=flags, staging_blobs=staging_blobs,
+                              spare_rows=spare_rows)
         h = C.c_void_p()
         self._destroy = _lib.moe_destroy
         capi.check(_lib.moe_create(C.byref(cfg), C.byref(h)), None)

@@ -23,6 +23,7 @@ MOE_FLAG_ROUTER_EXACT_ALWAYS = 1
 MOE_FLAG_FORCE_GEMV = 2
 MOE_FLAG_FORCE_MFMA = 4
 MOE_FLAG_NO_FUSED = 8
+MOE_FLAG_STAGED_TRANSPORT = 16
 
 
 class moe_config(C.Structure):
@@ -30,7 +31,7 @@ class moe_config(C.Structure):
                 ("top_k", C.c_int32), ("renorm", C.c_int32), ("n_layers", C.c_int32),
                 ("shared_inter", C.c_int32), ("group", C.c_int32), ("max_tokens", C.c_int32),
                 ("device", C.c_int32), ("policy", C.c_int32), ("slots_per_layer", C.c_int32),
-                ("flags", C.c_uint32)]
+                ("flags", C.c_uint32), ("staging_blobs", C.c_int32), ("spare_rows", C.c_int32)]
 
 
 class moe_cache_counters(C.Structure):

@@ -39,7 +39,17 @@ struct LayerState {
   uint8_t* store = nullptr;    // dev: E blobs (resident) or C slot blobs (pool)
   uint8_t* shared = nullptr;   // dev: shared-expert blob
   int32_t* map = nullptr;      // dev [E]: expert -> slot, -1 = not resident
-  uint8_t* backing = nullptr;  // pinned host [E blobs] (pool only)
+  uint8_t* backing = nullptr;  // host [E blobs] (pool only): pinned, or pageable RAM (staged transport)
+  bool pageable = false;
+  // staged transport: logical slot -> GPU row (-1 empty), and the rows no
+  // generation reads, each with the event after which its last reader of an
+  // older generation has retired (null: never read)
+  std::vector<int32_t> phys;
+  struct FreeRow {
+    int32_t row;
+    std::shared_ptr<ihipEvent_t> lease;
+  };
+  std::vector<FreeRow> free_rows;
   std::unique_ptr<PolicyEngine> policy;
   hipEvent_t retired = nullptr;
   hipEvent_t ready = nullptr;
@@ -86,6 +96,12 @@ struct moe_ctx {
   int grid = 0;
   int ncu = 1;                 // compute units (grid of the streaming kernel)
   uint64_t* stamps = nullptr;  // caller-owned phase-timestamp buffer or null
+  // staged transport: pinned staging buffers (one blob each), reused after the
+  // transfer out of each has completed
+  std::vector<uint8_t*> stage;
+  std::vector<hipEvent_t> stage_ev;
+  std::vector<char> stage_used;
+  int stage_next = 0;
   // natural routing over slot pools (moe_stack_forward_pooled)
   uint16_t* pool_x = nullptr;   // dev FP16 [max_tokens, H]: x of the current layer
   int32_t* pool_ids = nullptr;  // dev [n_layers, T, k] (room for max_tokens): routed ids, forced ids of the layer calls
@@ -173,6 +189,88 @@ moe_status check_layer(moe_ctx* c, int layer) {
 }
 
 bool pooled(const moe_ctx* c) { return c->cfg.policy != MOE_RESIDENT_ALL; }
+
+// GPU row that holds logical slot `slot` of a pooled layer.
+int32_t row_of(const LayerState& L, int32_t slot) { return L.pageable ? L.phys[slot] : slot; }
+
+// Row state of the staged transport, saved before a transaction so that a
+// failure before publication leaves the old generation as it was.
+struct RowState {
+  std::vector<int32_t> phys;
+  std::vector<LayerState::FreeRow> free_rows;
+};
+RowState save_rows(const LayerState& L) { return RowState{L.phys, L.free_rows}; }
+void restore_rows(LayerState& L, RowState&& r) {
+  L.phys = std::move(r.phys);
+  L.free_rows = std::move(r.free_rows);
+}
+
+// Enqueues the transfers of `fills` (decisions that load an expert into a
+// logical slot) on the side stream, between the timing events t0 and t1, and
+// records `done` after them.  Returns false if one could not be enqueued; the
+// caller then restores the policy and row state it saved.
+//   pinned backing: the side stream first waits for the layer's last reader
+//     (`retired`), then copies each blob straight into its slot;
+//   staged transport: each fill takes the lowest free GPU row (after that
+//     row's lease), and goes from the pageable source into the next pinned
+//     staging buffer (a host wait until that buffer's previous transfer has
+//     completed) and from there into the row.  The rows the victims leave are
+//     freed after this call with a lease recorded now on `s`: every reader of
+//     the old generation is enqueued before it, so no transfer waits for the
+//     current readers and none overwrites a row they still read.
+bool enqueue_fills(moe_ctx* c, LayerState& L, const std::vector<PolicyEngine::Decision>& fills, hipStream_t s,
+                   hipEvent_t t0, hipEvent_t t1, hipEvent_t done) {
+  const int64_t blob = c->lay.total();
+  bool good = true;
+  if (!L.pageable) {
+    good = hipStreamWaitEvent(c->side, L.retired, 0) == hipSuccess;
+    good = good && hipEventRecord(t0, c->side) == hipSuccess;
+    for (const auto& d : fills) {
+      if (!good) break;
+      good = hipMemcpyAsync(L.store + (int64_t)d.slot * blob, L.backing + (int64_t)d.expert * blob,
+                            (size_t)blob, hipMemcpyHostToDevice, c->side) == hipSuccess;
+    }
+  } else {
+    std::shared_ptr<ihipEvent_t> lease;
+    bool vacates = false;
+    for (const auto& d : fills) vacates = vacates || L.phys[d.slot] >= 0;
+    if (vacates) {
+      hipEvent_t ev = nullptr;
+      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return false;
+      lease.reset(ev, [](hipEvent_t e) { (void)hipEventDestroy(e); });
+      good = hipEventRecord(ev, s) == hipSuccess;
+    }
+    good = good && hipEventRecord(t0, c->side) == hipSuccess;
+    std::vector<LayerState::FreeRow> released;
+    for (const auto& d : fills) {
+      if (!good || L.free_rows.empty()) {
+        good = false;  // (spare_rows >= the fills of one call: a free row exists)
+        break;
+      }
+      size_t bi = 0;
+      for (size_t i = 1; i < L.free_rows.size(); ++i)
+        if (L.free_rows[i].row < L.free_rows[bi].row) bi = i;
+      const LayerState::FreeRow fr = L.free_rows[bi];
+      L.free_rows.erase(L.free_rows.begin() + bi);
+      if (fr.lease) good = hipStreamWaitEvent(c->side, fr.lease.get(), 0) == hipSuccess;
+      const int si = c->stage_next;
+      c->stage_next = (c->stage_next + 1) % (int)c->stage.size();
+      if (good && c->stage_used[si]) good = hipEventSynchronize(c->stage_ev[si]) == hipSuccess;
+      if (!good) break;
+      memcpy(c->stage[si], L.backing + (int64_t)d.expert * blob, (size_t)blob);
+      good = hipMemcpyAsync(L.store + (int64_t)fr.row * blob, c->stage[si], (size_t)blob, hipMemcpyHostToDevice,
+                            c->side) == hipSuccess;
+      good = good && hipEventRecord(c->stage_ev[si], c->side) == hipSuccess;
+      c->stage_used[si] = 1;
+      if (L.phys[d.slot] >= 0) released.push_back({L.phys[d.slot], lease});
+      L.phys[d.slot] = fr.row;
+    }
+    for (auto& r : released) L.free_rows.push_back(std::move(r));
+  }
+  good = good && hipEventRecord(t1, c->side) == hipSuccess;
+  good = good && hipEventRecord(done, c->side) == hipSuccess;
+  return good;
+}
 
 enum KernelKind {
   kKindLogits = 0, kKindTopk, kKindGroup, kKindGateUp, kKindDown, kKindCombine, kKindNorm, kKindFused,
@@ -358,6 +456,13 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       return fail(nullptr, MOE_E_CAPACITY,
                   "slots_per_layer must be >= min(E, max_tokens*k) and <= E");
   }
+  const bool staged = g.policy != MOE_RESIDENT_ALL && (g.flags & MOE_FLAG_STAGED_TRANSPORT);
+  if (staged) {
+    const int64_t need = std::min<int64_t>(g.slots_per_layer, (int64_t)g.max_tokens * g.top_k);
+    if (g.staging_blobs < 1 || g.spare_rows < need)
+      return fail(nullptr, MOE_E_CAPACITY,
+                  "staged transport needs staging_blobs >= 1 and spare_rows >= min(C, max_tokens*k)");
+  }
   std::unique_ptr<moe_ctx> c(new moe_ctx());
   c->cfg = g;
   const int64_t cb = (int64_t)g.inter * g.hidden / 2, sc = (int64_t)g.inter * g.hidden / 128;
@@ -376,7 +481,8 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   };
   c->layers.resize(g.n_layers);
   const int64_t blob = c->lay.total();
-  const int nslots = g.policy == MOE_RESIDENT_ALL ? g.n_experts : g.slots_per_layer;
+  const int nslots = g.policy == MOE_RESIDENT_ALL ? g.n_experts
+                                                  : g.slots_per_layer + (staged ? g.spare_rows : 0);
   bool ok = true;
   for (int l = 0; l < g.n_layers && ok; ++l) {
     LayerState& L = c->layers[l];
@@ -384,7 +490,13 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     ok = ok && dalloc((void**)&L.store, (size_t)nslots * blob);
     ok = ok && dalloc((void**)&L.map, (size_t)g.n_experts * 4);
     if (g.shared_inter) ok = ok && dalloc((void**)&L.shared, (size_t)c->shared_lay.total());
-    if (ok && g.policy != MOE_RESIDENT_ALL) {
+    if (ok && staged) {
+      // the complete host source in pageable RAM, touched page by page when the
+      // layer is registered, immutable afterwards
+      L.backing = new (std::nothrow) uint8_t[(size_t)g.n_experts * blob];
+      L.pageable = true;
+      ok = L.backing != nullptr;
+    } else if (ok && g.policy != MOE_RESIDENT_ALL) {
       if (hipHostMalloc((void**)&L.backing, (size_t)g.n_experts * blob, hipHostMallocDefault) != hipSuccess) {
         (void)hipGetLastError();
         L.backing = nullptr;
@@ -452,6 +564,25 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       ok = false;
     }
   }
+  if (ok && staged) {
+    for (int i = 0; i < g.staging_blobs && ok; ++i) {
+      uint8_t* p = nullptr;
+      hipEvent_t ev = nullptr;
+      if (hipHostMalloc((void**)&p, (size_t)blob, hipHostMallocDefault) != hipSuccess) {
+        (void)hipGetLastError();
+        ok = false;
+        break;
+      }
+      c->stage.push_back(p);
+      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+        (void)hipGetLastError();
+        ok = false;
+        break;
+      }
+      c->stage_ev.push_back(ev);
+      c->stage_used.push_back(0);
+    }
+  }
   if (ok && hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess) ok = false;
   if (ok) {
     const uint32_t zero = 0;
@@ -474,7 +605,9 @@ void moe_destroy(moe_ctx* c) {
     (void)hipFree(L.store);
     (void)hipFree(L.map);
     (void)hipFree(L.shared);
-    if (L.backing) (void)hipHostFree(L.backing);
+    if (L.backing && L.pageable) delete[] L.backing;
+    else if (L.backing) (void)hipHostFree(L.backing);
+    L.free_rows.clear();  // releases the lease events
     if (L.retired) (void)hipEventDestroy(L.retired);
     if (L.ready) (void)hipEventDestroy(L.ready);
     if (L.pf_ready) (void)hipEventDestroy(L.pf_ready);
@@ -489,6 +622,8 @@ void moe_destroy(moe_ctx* c) {
                   c->pool_x, c->pool_ids, c->pool_w, c->pool_gids};
   for (void* p : bufs) (void)hipFree(p);
   if (c->pool_ids_h) (void)hipHostFree(c->pool_ids_h);
+  for (uint8_t* p : c->stage) (void)hipHostFree(p);
+  for (hipEvent_t e : c->stage_ev) (void)hipEventDestroy(e);
   if (c->side) (void)hipStreamDestroy(c->side);
   for (auto& p : c->timer_events) {
     (void)hipEventDestroy(p.first);
@@ -516,6 +651,11 @@ moe_status moe_register_layer(moe_ctx* c, int32_t layer, const uint16_t* router,
     for (int e = 0; e < g.n_experts; ++e) map[e] = -1;
     L.policy.reset(new PolicyEngine(g.policy, g.n_experts, g.slots_per_layer, layer));
     L.stats = moe_cache_counters{};
+    if (L.pageable) {
+      L.phys.assign(g.slots_per_layer, -1);
+      L.free_rows.clear();
+      for (int r = 0; r < g.slots_per_layer + g.spare_rows; ++r) L.free_rows.push_back({r, nullptr});
+    }
   } else {
     // stage in chunks of experts through pinned memory
     const int chunk = 16;
@@ -695,24 +835,21 @@ moe_status moe_cache_ensure(moe_ctx* c, int32_t layer, const int32_t* experts, i
     return fail(c, MOE_E_TRANSFER, "could not order the first use of a prefetched copy");
   }
   if (nmiss > 0) {
-    // transport: side stream waits for the last reader of this layer's slots
+    // transport of the misses, then `stream` waits for all of them
     bool good = L.inject != 1;
     hipEvent_t t0 = nullptr, t1 = nullptr;
     good = good && hipEventCreate(&t0) == hipSuccess && hipEventCreate(&t1) == hipSuccess;
-    good = good && hipStreamWaitEvent(c->side, L.retired, 0) == hipSuccess;
-    good = good && hipEventRecord(t0, c->side) == hipSuccess;
-    for (const auto& d : dec) {
-      if (d.hit || !good) continue;
-      good = hipMemcpyAsync(L.store + (int64_t)d.slot * blob, L.backing + (int64_t)d.expert * blob,
-                            (size_t)blob, hipMemcpyHostToDevice, c->side) == hipSuccess;
-    }
-    good = good && hipEventRecord(t1, c->side) == hipSuccess;
-    good = good && hipEventRecord(L.ready, c->side) == hipSuccess;
+    RowState rows = save_rows(L);
+    std::vector<PolicyEngine::Decision> fills;
+    for (const auto& d : dec)
+      if (!d.hit) fills.push_back(d);
+    good = good && enqueue_fills(c, L, fills, s, t0, t1, L.ready);
     good = good && hipStreamWaitEvent(s, L.ready, 0) == hipSuccess;
     if (!good) {
       (void)hipGetLastError();
       if (t0) (void)hipEventDestroy(t0);
       if (t1) (void)hipEventDestroy(t1);
+      restore_rows(L, std::move(rows));
       *L.policy = saved;  // the old generation stays authoritative
       L.inject = 0;
       L.stats.failures += 1;
@@ -732,10 +869,10 @@ moe_status moe_cache_ensure(moe_ctx* c, int32_t layer, const int32_t* experts, i
       pa.u[pa.n++] = PublishUpdate{e, slot};
     };
     for (const auto& d : dec) {
-      if (d.kind == PolicyEngine::kPrefetchHit) push(d.expert, d.slot);
+      if (d.kind == PolicyEngine::kPrefetchHit) push(d.expert, row_of(L, d.slot));
       if (d.hit) continue;
       if (d.victim >= 0) push(d.victim, -1);
-      push(d.expert, d.slot);
+      push(d.expert, row_of(L, d.slot));
     }
     if (pa.n) launch_publish(pa, s);
     if (hipGetLastError() != hipSuccess || (nmiss > 0 && L.inject == 2)) {
@@ -778,19 +915,13 @@ moe_status moe_cache_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts,
   bool good = L.inject != 1;
   hipEvent_t t0 = nullptr, t1 = nullptr;
   good = good && hipEventCreate(&t0) == hipSuccess && hipEventCreate(&t1) == hipSuccess;
-  good = good && hipStreamWaitEvent(c->side, L.retired, 0) == hipSuccess;
-  good = good && hipEventRecord(t0, c->side) == hipSuccess;
-  for (const auto& d : dec) {
-    if (!good) break;
-    good = hipMemcpyAsync(L.store + (int64_t)d.slot * blob, L.backing + (int64_t)d.expert * blob,
-                          (size_t)blob, hipMemcpyHostToDevice, c->side) == hipSuccess;
-  }
-  good = good && hipEventRecord(t1, c->side) == hipSuccess;
-  good = good && hipEventRecord(L.pf_ready, c->side) == hipSuccess;
+  RowState rows = save_rows(L);
+  good = good && enqueue_fills(c, L, dec, s, t0, t1, L.pf_ready);
   if (!good) {
     (void)hipGetLastError();
     if (t0) (void)hipEventDestroy(t0);
     if (t1) (void)hipEventDestroy(t1);
+    restore_rows(L, std::move(rows));
     *L.policy = saved;
     L.inject = 0;
     L.stats.failures += 1;
@@ -846,20 +977,14 @@ moe_status moe_cache_pin(moe_ctx* c, int32_t layer, const int32_t* experts, int3
   bool good = true;
   hipEvent_t t0 = nullptr, t1 = nullptr;
   good = good && hipEventCreate(&t0) == hipSuccess && hipEventCreate(&t1) == hipSuccess;
-  good = good && hipStreamWaitEvent(c->side, L.retired, 0) == hipSuccess;
-  good = good && hipEventRecord(t0, c->side) == hipSuccess;
-  for (const auto& d : dec) {
-    if (!good) break;
-    good = hipMemcpyAsync(L.store + (int64_t)d.slot * blob, L.backing + (int64_t)d.expert * blob,
-                          (size_t)blob, hipMemcpyHostToDevice, c->side) == hipSuccess;
-  }
-  good = good && hipEventRecord(t1, c->side) == hipSuccess;
-  good = good && hipEventRecord(L.ready, c->side) == hipSuccess;
+  RowState rows = save_rows(L);
+  good = good && enqueue_fills(c, L, dec, s, t0, t1, L.ready);
   good = good && hipStreamWaitEvent(s, L.ready, 0) == hipSuccess;
   if (!good) {
     (void)hipGetLastError();
     if (t0) (void)hipEventDestroy(t0);
     if (t1) (void)hipEventDestroy(t1);
+    restore_rows(L, std::move(rows));
     *L.policy = saved;
     L.stats.failures += 1;
     return fail(c, MOE_E_TRANSFER, "hot-set transfer failed; nothing was published");
@@ -872,7 +997,7 @@ moe_status moe_cache_pin(moe_ctx* c, int32_t layer, const int32_t* experts, int3
       launch_publish(pa, s);
       pa.n = 0;
     }
-    pa.u[pa.n++] = PublishUpdate{d.expert, d.slot};
+    pa.u[pa.n++] = PublishUpdate{d.expert, row_of(L, d.slot)};
   }
   if (pa.n) launch_publish(pa, s);
   if (hipGetLastError() != hipSuccess) {
