@@ -390,7 +390,7 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   }
   if (any_mfma) {
     ScopedTimer tm(c, kKindMfmaGateUp, s);
-    launch_mfma_gateup(ma, mfma_max_tiles(T, g.top_k, g.n_experts, g.inter, 0), s);
+    launch_mfma_gateup(ma, mfma_max_tiles(T, g.top_k, g.n_experts, g.inter, 0, mfma_min), s);
   }
   if (!all_mfma) {
     ScopedTimer tm(c, kKindDown, s);
@@ -399,7 +399,7 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   }
   if (any_mfma) {
     ScopedTimer tm(c, kKindMfmaDown, s);
-    launch_mfma_down(ma, mfma_max_tiles(T, g.top_k, g.n_experts, g.hidden, 1), s);
+    launch_mfma_down(ma, mfma_max_tiles(T, g.top_k, g.n_experts, g.hidden, 1, mfma_min), s);
   }
   if (g.shared_inter && !shared_in_stream) {
     ExpertArgs sa = ea;

@@ -477,9 +477,11 @@ static int rows_per_block(int mode, int nb) {
   return nb == 4 ? block_rows<1, 4>() : block_rows<1, 2>();
 }
 
-int mfma_max_tiles(int T, int k, int E, int rows, int mode) {
+int mfma_max_tiles(int T, int k, int E, int rows, int mode, int mfma_min) {
   const int pairs = T * k;
-  const int max_mtiles = (pairs + kMT - 1) / kMT + std::min(E, pairs);
+  // sum over those experts of ceil(n_e / kMT) <= ceil(pairs / kMT) + their
+  // number, which is at most min(E, pairs / mfma_min)
+  const int max_mtiles = (pairs + kMT - 1) / kMT + std::min(E, pairs / std::max(mfma_min, 1));
   const int ntn = rows / rows_per_block(mode, mfma_nb(mode, rows));
   // the block mapping covers token tiles in multiples of the XCD count
   return ((max_mtiles + kXcd - 1) / kXcd) * kXcd * ntn;

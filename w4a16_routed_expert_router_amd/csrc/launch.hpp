@@ -59,7 +59,9 @@ struct MfmaArgs {
   uint16_t* hbuf;             // [positions, I] fp16
   float* ybuf;                // [positions, H] fp32
 };
-int mfma_max_tiles(int T, int k, int E, int rows, int mode);
+// Blocks of a grouped-GEMM launch: enough token tiles for any routing of the
+// call in which only experts with at least mfma_min tokens take the grouped GEMM.
+int mfma_max_tiles(int T, int k, int E, int rows, int mode, int mfma_min);
 void launch_mfma_gateup(const MfmaArgs& a, int max_tiles, hipStream_t stream);
 void launch_mfma_down(const MfmaArgs& a, int max_tiles, hipStream_t stream);
 
