@@ -18,7 +18,9 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <condition_variable>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -32,6 +34,79 @@ using namespace moe;
 namespace {
 
 thread_local std::string g_create_error;
+
+// Host copy into pinned staging, split over a few persistent threads (the
+// caller takes one part): one thread cannot fill a staging buffer as fast as
+// the link drains it.
+class CopyPool {
+ public:
+  explicit CopyPool(int workers) {
+    for (int i = 0; i < workers; ++i) th_.emplace_back([this, i] { run(i); });
+  }
+  ~CopyPool() {
+    {
+      std::lock_guard<std::mutex> lk(m_);
+      stop_ = true;
+    }
+    cv_.notify_all();
+    for (auto& t : th_) t.join();
+  }
+  void copy(uint8_t* dst, const uint8_t* src, size_t bytes) {
+    const size_t parts = th_.size() + 1;
+    const size_t part = ((bytes + parts - 1) / parts + 63) & ~(size_t)63;
+    {
+      std::lock_guard<std::mutex> lk(m_);
+      dst_ = dst;
+      src_ = src;
+      bytes_ = bytes;
+      part_ = part;
+      pending_ = (int)th_.size();
+      ++gen_;
+    }
+    cv_.notify_all();
+    piece(th_.size(), dst, src, bytes, part);  // the caller's part
+    std::unique_lock<std::mutex> lk(m_);
+    done_.wait(lk, [this] { return pending_ == 0; });
+  }
+
+ private:
+  static void piece(size_t i, uint8_t* dst, const uint8_t* src, size_t bytes, size_t part) {
+    const size_t b = i * part;
+    if (b < bytes) memcpy(dst + b, src + b, std::min(part, bytes - b));
+  }
+  void run(int i) {
+    uint64_t seen = 0;
+    for (;;) {
+      uint8_t* dst;
+      const uint8_t* src;
+      size_t bytes, part;
+      {
+        std::unique_lock<std::mutex> lk(m_);
+        cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+        if (stop_) return;
+        seen = gen_;
+        dst = dst_;
+        src = src_;
+        bytes = bytes_;
+        part = part_;
+      }
+      piece((size_t)i, dst, src, bytes, part);
+      {
+        std::lock_guard<std::mutex> lk(m_);
+        if (--pending_ == 0) done_.notify_one();
+      }
+    }
+  }
+  std::mutex m_;
+  std::condition_variable cv_, done_;
+  std::vector<std::thread> th_;
+  uint8_t* dst_ = nullptr;
+  const uint8_t* src_ = nullptr;
+  size_t bytes_ = 0, part_ = 0;
+  uint64_t gen_ = 0;
+  int pending_ = 0;
+  bool stop_ = false;
+};
 
 struct LayerState {
   bool registered = false;
@@ -102,6 +177,7 @@ struct moe_ctx {
   std::vector<hipEvent_t> stage_ev;
   std::vector<char> stage_used;
   int stage_next = 0;
+  std::unique_ptr<CopyPool> copier;
   // natural routing over slot pools (moe_stack_forward_pooled)
   uint16_t* pool_x = nullptr;   // dev FP16 [max_tokens, H]: x of the current layer
   int32_t* pool_ids = nullptr;  // dev [n_layers, T, k] (room for max_tokens): routed ids, forced ids of the layer calls
@@ -257,7 +333,7 @@ bool enqueue_fills(moe_ctx* c, LayerState& L, const std::vector<PolicyEngine::De
       c->stage_next = (c->stage_next + 1) % (int)c->stage.size();
       if (good && c->stage_used[si]) good = hipEventSynchronize(c->stage_ev[si]) == hipSuccess;
       if (!good) break;
-      memcpy(c->stage[si], L.backing + (int64_t)d.expert * blob, (size_t)blob);
+      c->copier->copy(c->stage[si], L.backing + (int64_t)d.expert * blob, (size_t)blob);
       good = hipMemcpyAsync(L.store + (int64_t)fr.row * blob, c->stage[si], (size_t)blob, hipMemcpyHostToDevice,
                             c->side) == hipSuccess;
       good = good && hipEventRecord(c->stage_ev[si], c->side) == hipSuccess;
@@ -582,6 +658,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
       c->stage_ev.push_back(ev);
       c->stage_used.push_back(0);
     }
+    if (ok) c->copier.reset(new CopyPool(3));
   }
   if (ok && hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess) ok = false;
   if (ok) {
@@ -622,6 +699,7 @@ void moe_destroy(moe_ctx* c) {
                   c->pool_x, c->pool_ids, c->pool_w, c->pool_gids};
   for (void* p : bufs) (void)hipFree(p);
   if (c->pool_ids_h) (void)hipHostFree(c->pool_ids_h);
+  c->copier.reset();
   for (uint8_t* p : c->stage) (void)hipHostFree(p);
   for (hipEvent_t e : c->stage_ev) (void)hipEventDestroy(e);
   if (c->side) (void)hipStreamDestroy(c->side);
