@@ -251,13 +251,13 @@ def extra_pool(moe, fx, dev, stream, steps=256, layers=16):
     res = {"steps": steps, "layers": layers, "resident_tokens_per_s": round(steps / dt_ref, 1)}
     staged = dict(flags=moe.capi.MOE_FLAG_STAGED_TRANSPORT, staging_blobs=4, spare_rows=8)
     for policy, C, kw in (("lru", 16, {}), ("lfu", 16, {}), ("lru", 32, {}), ("lfu", 32, {}), ("lru", 48, {}),
-                          ("lfu", 48, {}), ("lfu", 32, staged)):
+                          ("lfu", 48, {}), ("lfu", 32, staged), ("lfu", 32, dict(spare_rows=8))):
         out, dt, st = run(policy, C, **kw)
         acc = sum(x["accesses"] for x in st)
         hits = sum(x["hits"] for x in st)
         h2d = sum(x["h2d_bytes"] for x in st)
         h2d_s = sum(x["h2d_seconds"] for x in st)
-        res[f"{policy}_C{C}" + ("_staged_transport" if kw else "")] = {
+        res[f"{policy}_C{C}" + ("" if not kw else "_staged_transport" if "flags" in kw else "_spare_rows")] = {
             "hit_rate": round(hits / max(acc, 1), 4),
             "h2d_gb": round(h2d / 1e9, 3),
             "h2d_gbps_copy": round(h2d / max(h2d_s, 1e-12) / 1e9, 2),

@@ -130,8 +130,15 @@ typedef struct moe_config {
   uint32_t flags;          /* MOE_FLAG_*                                          */
   int32_t staging_blobs;   /* MOE_FLAG_STAGED_TRANSPORT: pinned staging buffers of
                               one expert blob each (context-wide)                 */
-  int32_t spare_rows;      /* MOE_FLAG_STAGED_TRANSPORT: GPU rows per layer beyond
-                              the C slots, which misses land in unpublished       */
+  int32_t spare_rows;      /* slot pools: GPU rows per layer beyond the C slots.
+                              0 (and no staged transport): a miss is copied into
+                              its victim's slot after the layer's last reader has
+                              retired.  > 0: misses land in unpublished rows that
+                              no generation reads, so no copy waits for the
+                              current readers; a victim's row is reused only
+                              after the readers of its generation retire.  Needs
+                              spare_rows >= min(C, max_tokens*k) (MOE_E_CAPACITY
+                              from moe_create otherwise)                          */
 } moe_config;
 
 typedef struct moe_cache_counters {

@@ -305,13 +305,14 @@ def test_pool_hot_set_bit_identical_and_decisions_match_oracle(moe, olmoe_layers
 # ---- staged transport: pageable source, pinned staging, spare rows, leases --------
 
 STAGED = dict(flags=16, staging_blobs=2, spare_rows=8)
+SPARE = dict(spare_rows=8)          # spare rows straight from the pinned backing
 
 
-@pytest.mark.parametrize("policy,C", [("lfu", 16), ("lru_freq", 24)])
+@pytest.mark.parametrize("policy,C,mode", [("lfu", 16, "staged"), ("lru_freq", 24, "staged"), ("lru", 16, "spare")])
 def test_pool_staged_transport_bit_identical_and_decisions_match_oracle(moe, olmoe_layers, trace, h0s,
-                                                                       resident_out, policy, C):
-    say(f"test_pool_staged policy={policy} C={C}")
-    ctx = _ctx(moe, olmoe_layers, policy=policy, slots=C, **STAGED)
+                                                                       resident_out, policy, C, mode):
+    say(f"test_pool_staged policy={policy} C={C} mode={mode}")
+    ctx = _ctx(moe, olmoe_layers, policy=policy, slots=C, **(STAGED if mode == "staged" else SPARE))
     out = _run(ctx, trace, h0s, pooled=True)
     assert torch.equal(out, resident_out), "staged transport changed the output"
     blob = fx.OLMOE.blob_bytes
@@ -331,16 +332,17 @@ def test_pool_staged_transport_natural_routing_prefetch_and_hot_set(moe, olmoe_l
     say("test_pool_staged_natural")
     hot = [sorted(range(4 * (l % 3), 4 * (l % 3) + 4)) for l in range(L)]
     res = {}
-    for mode, kw in (("direct", {}), ("staged", STAGED)):
+    for mode, kw in (("direct", {}), ("staged", STAGED), ("spare", SPARE)):
         ctx = _ctx(moe, olmoe_layers, policy="lru", slots=16, **kw)
         for l in range(L):
             ctx.cache_pin(l, hot[l])
         out, ids, gs = _run_natural(ctx, h0s, True)
         res[mode] = (out, ids, [ctx.cache_events(l) for l in range(L)])
         ctx.close()
-    assert torch.equal(res["staged"][0], res["direct"][0])
-    assert np.array_equal(res["staged"][1], res["direct"][1])
-    assert res["staged"][2] == res["direct"][2]
+    for mode in ("staged", "spare"):
+        assert torch.equal(res[mode][0], res["direct"][0])
+        assert np.array_equal(res[mode][1], res["direct"][1])
+        assert res[mode][2] == res["direct"][2]
 
 
 def test_pool_staged_transfer_failure_before_publication_keeps_state(moe, olmoe_layers, trace, h0s):

@@ -49,7 +49,9 @@ def test_create_rejects_bad_configs_without_touching_a_gpu():
            # staged transport without staging, or with fewer spare rows than
            # the misses one call can have (min(C, T*k) = 32): startup fails
            dict(policy=1, slots_per_layer=32, flags=16, staging_blobs=0, spare_rows=32),
-           dict(policy=1, slots_per_layer=32, flags=16, staging_blobs=2, spare_rows=31)]
+           dict(policy=1, slots_per_layer=32, flags=16, staging_blobs=2, spare_rows=31),
+           dict(policy=1, slots_per_layer=32, spare_rows=8),       # spare rows below 32
+           dict(policy=1, slots_per_layer=32, spare_rows=-1)]
     for b in bad:
         cfg = capi.moe_config(**{**good, **b})
         h = C.c_void_p()

@@ -116,7 +116,8 @@ struct LayerState {
   int32_t* map = nullptr;      // dev [E]: expert -> slot, -1 = not resident
   uint8_t* backing = nullptr;  // host [E blobs] (pool only): pinned, or pageable RAM (staged transport)
   bool pageable = false;
-  // staged transport: logical slot -> GPU row (-1 empty), and the rows no
+  bool spare = false;  // spare rows: misses land in rows no generation reads
+  // with spare rows: logical slot -> GPU row (-1 empty), and the rows no
   // generation reads, each with the event after which its last reader of an
   // older generation has retired (null: never read)
   std::vector<int32_t> phys;
@@ -267,9 +268,9 @@ moe_status check_layer(moe_ctx* c, int layer) {
 bool pooled(const moe_ctx* c) { return c->cfg.policy != MOE_RESIDENT_ALL; }
 
 // GPU row that holds logical slot `slot` of a pooled layer.
-int32_t row_of(const LayerState& L, int32_t slot) { return L.pageable ? L.phys[slot] : slot; }
+int32_t row_of(const LayerState& L, int32_t slot) { return L.spare ? L.phys[slot] : slot; }
 
-// Row state of the staged transport, saved before a transaction so that a
+// Row state of a pool with spare rows, saved before a transaction so that a
 // failure before publication leaves the old generation as it was.
 struct RowState {
   std::vector<int32_t> phys;
@@ -285,20 +286,21 @@ void restore_rows(LayerState& L, RowState&& r) {
 // logical slot) on the side stream, between the timing events t0 and t1, and
 // records `done` after them.  Returns false if one could not be enqueued; the
 // caller then restores the policy and row state it saved.
-//   pinned backing: the side stream first waits for the layer's last reader
-//     (`retired`), then copies each blob straight into its slot;
-//   staged transport: each fill takes the lowest free GPU row (after that
-//     row's lease), and goes from the pageable source into the next pinned
-//     staging buffer (a host wait until that buffer's previous transfer has
-//     completed) and from there into the row.  The rows the victims leave are
-//     freed after this call with a lease recorded now on `s`: every reader of
-//     the old generation is enqueued before it, so no transfer waits for the
-//     current readers and none overwrites a row they still read.
+//   in-place slots (no spare rows): the side stream first waits for the
+//     layer's last reader (`retired`), then copies each blob into its slot;
+//   spare rows: each fill takes the lowest free GPU row (after that row's
+//     lease).  The rows the victims leave are freed after this call with a
+//     lease recorded now on `s`: every reader of the old generation is
+//     enqueued before it, so no transfer waits for the current readers and
+//     none overwrites a row they still read.
+// A blob comes straight from the pinned backing, or (staged transport) from
+// the pageable source through the next pinned staging buffer, after a host
+// wait until that buffer's previous transfer has completed.
 bool enqueue_fills(moe_ctx* c, LayerState& L, const std::vector<PolicyEngine::Decision>& fills, hipStream_t s,
                    hipEvent_t t0, hipEvent_t t1, hipEvent_t done) {
   const int64_t blob = c->lay.total();
   bool good = true;
-  if (!L.pageable) {
+  if (!L.spare) {
     good = hipStreamWaitEvent(c->side, L.retired, 0) == hipSuccess;
     good = good && hipEventRecord(t0, c->side) == hipSuccess;
     for (const auto& d : fills) {
@@ -329,15 +331,21 @@ bool enqueue_fills(moe_ctx* c, LayerState& L, const std::vector<PolicyEngine::De
       const LayerState::FreeRow fr = L.free_rows[bi];
       L.free_rows.erase(L.free_rows.begin() + bi);
       if (fr.lease) good = hipStreamWaitEvent(c->side, fr.lease.get(), 0) == hipSuccess;
-      const int si = c->stage_next;
-      c->stage_next = (c->stage_next + 1) % (int)c->stage.size();
-      if (good && c->stage_used[si]) good = hipEventSynchronize(c->stage_ev[si]) == hipSuccess;
       if (!good) break;
-      c->copier->copy(c->stage[si], L.backing + (int64_t)d.expert * blob, (size_t)blob);
-      good = hipMemcpyAsync(L.store + (int64_t)fr.row * blob, c->stage[si], (size_t)blob, hipMemcpyHostToDevice,
-                            c->side) == hipSuccess;
-      good = good && hipEventRecord(c->stage_ev[si], c->side) == hipSuccess;
-      c->stage_used[si] = 1;
+      if (L.pageable) {
+        const int si = c->stage_next;
+        c->stage_next = (c->stage_next + 1) % (int)c->stage.size();
+        if (c->stage_used[si]) good = hipEventSynchronize(c->stage_ev[si]) == hipSuccess;
+        if (!good) break;
+        c->copier->copy(c->stage[si], L.backing + (int64_t)d.expert * blob, (size_t)blob);
+        good = hipMemcpyAsync(L.store + (int64_t)fr.row * blob, c->stage[si], (size_t)blob,
+                              hipMemcpyHostToDevice, c->side) == hipSuccess;
+        good = good && hipEventRecord(c->stage_ev[si], c->side) == hipSuccess;
+        c->stage_used[si] = 1;
+      } else {
+        good = hipMemcpyAsync(L.store + (int64_t)fr.row * blob, L.backing + (int64_t)d.expert * blob,
+                              (size_t)blob, hipMemcpyHostToDevice, c->side) == hipSuccess;
+      }
       if (L.phys[d.slot] >= 0) released.push_back({L.phys[d.slot], lease});
       L.phys[d.slot] = fr.row;
     }
@@ -533,11 +541,14 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
                   "slots_per_layer must be >= min(E, max_tokens*k) and <= E");
   }
   const bool staged = g.policy != MOE_RESIDENT_ALL && (g.flags & MOE_FLAG_STAGED_TRANSPORT);
-  if (staged) {
+  const bool spare = g.policy != MOE_RESIDENT_ALL && (staged || g.spare_rows > 0);
+  if (g.spare_rows < 0) return fail(nullptr, MOE_E_ARG, "spare_rows must be >= 0");
+  if (spare) {
     const int64_t need = std::min<int64_t>(g.slots_per_layer, (int64_t)g.max_tokens * g.top_k);
-    if (g.staging_blobs < 1 || g.spare_rows < need)
+    if ((staged && g.staging_blobs < 1) || g.spare_rows < need)
       return fail(nullptr, MOE_E_CAPACITY,
-                  "staged transport needs staging_blobs >= 1 and spare_rows >= min(C, max_tokens*k)");
+                  "spare rows need spare_rows >= min(C, max_tokens*k), and the staged transport "
+                  "staging_blobs >= 1");
   }
   std::unique_ptr<moe_ctx> c(new moe_ctx());
   c->cfg = g;
@@ -558,10 +569,11 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   c->layers.resize(g.n_layers);
   const int64_t blob = c->lay.total();
   const int nslots = g.policy == MOE_RESIDENT_ALL ? g.n_experts
-                                                  : g.slots_per_layer + (staged ? g.spare_rows : 0);
+                                                  : g.slots_per_layer + (spare ? g.spare_rows : 0);
   bool ok = true;
   for (int l = 0; l < g.n_layers && ok; ++l) {
     LayerState& L = c->layers[l];
+    L.spare = spare;
     ok = ok && dalloc((void**)&L.router, (size_t)g.n_experts * g.hidden * 2);
     ok = ok && dalloc((void**)&L.store, (size_t)nslots * blob);
     ok = ok && dalloc((void**)&L.map, (size_t)g.n_experts * 4);
@@ -729,7 +741,7 @@ moe_status moe_register_layer(moe_ctx* c, int32_t layer, const uint16_t* router,
     for (int e = 0; e < g.n_experts; ++e) map[e] = -1;
     L.policy.reset(new PolicyEngine(g.policy, g.n_experts, g.slots_per_layer, layer));
     L.stats = moe_cache_counters{};
-    if (L.pageable) {
+    if (L.spare) {
       L.phys.assign(g.slots_per_layer, -1);
       L.free_rows.clear();
       for (int r = 0; r < g.slots_per_layer + g.spare_rows; ++r) L.free_rows.push_back({r, nullptr});
