@@ -339,7 +339,11 @@ moe_status moe_cache_prefetch(moe_ctx* ctx, int32_t layer, const int32_t* expert
  * ("An expert-offloading engine, from scratch", "What the numbers say").  The
  * result equals moe_stack_forward's with natural routing and full residency,
  * whatever is prefetched.  h: dev FP32 [T,H], updated in place; step: the
- * label of the event-log entries.  ids_trace (dev int32 [L,T,k]) receives each
+ * label of the event-log entries.  When a pinned hot set leaves fewer slots
+ * than the experts of the batch's routed group outside it, the layer runs over
+ * contiguous token chunks instead -- each the longest run from its first token
+ * whose group fits -- ensured and computed one after another (MOE_E_CAPACITY if
+ * one token's experts do not fit).  ids_trace (dev int32 [L,T,k]) receives each
  * layer's routed ids and guess_trace (dev int32 [L,T,k]) at row l + 1 the ids
  * guessed for layer l + 1, when non-NULL (indexed by absolute layer; rows not
  * written are left as they are).  Needs a slot pool (MOE_E_ARG otherwise) and

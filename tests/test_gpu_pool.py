@@ -363,3 +363,68 @@ def test_pool_staged_transfer_failure_before_publication_keeps_state(moe, olmoe_
     sim.ensure(miss_group.tolist(), 99)
     assert ctx.cache_events(5) == [e.as_tuple() for e in sim.events]
     ctx.close()
+
+
+def _chunks(ids_l, hot, dyn):
+    """Greedy contiguous token chunks whose groups keep at most `dyn` experts
+    outside the hot set (ids_l: [T, k] of one layer)."""
+    out, t0, T = [], 0, ids_l.shape[0]
+    grp = lambda a, b: sorted(set(int(e) for e in ids_l[a:b].ravel()))
+    outside = lambda g: sum(1 for e in g if e not in hot)
+    while t0 < T:
+        t1 = t0 + 1
+        while t1 < T and outside(grp(t0, t1 + 1)) <= dyn:
+            t1 += 1
+        out.append(grp(t0, t1))
+        t0 = t1
+    return out
+
+
+def test_pool_batch_group_larger_than_dynamic_slots_runs_in_chunks(moe, olmoe_layers):
+    # 4 tokens, C = 32 with 24 pinned: 8 dynamic slots, fewer than a 4-token
+    # group usually needs, so layers run over token chunks; results equal the
+    # all-resident stack's and decisions equal the oracle's over the same chunks
+    say("test_pool_batch_group_chunks")
+    from gpu_util import rel_l2
+    T, C, n_hot, steps = 4, 32, 24, 6
+    hot = _hot_sets(n_hot)
+    ctx = moe.MoEContext(fx.OLMOE, n_layers=L, max_tokens=T, policy="lru", slots=C)
+    for l, w in enumerate(olmoe_layers):
+        ctx.register_layer(l, w)
+        ctx.cache_pin(l, hot[l])
+    res = moe.MoEContext(fx.OLMOE, n_layers=L, max_tokens=T)
+    for l, w in enumerate(olmoe_layers):
+        res.register_layer(l, w)
+    sims = [ora.CacheSim(ora.LRU, fx.OLMOE.n_experts, C, layer=l) for l in range(L)]
+    for l in range(L):
+        sims[l].pin(hot[l], 0)
+    n_chunked = 0
+    for s in range(steps):
+        h0 = fx.activations(("pool-chunks", s), T, fx.OLMOE.hidden, device="cuda").float()
+        h = h0.clone()
+        ids, gs = ctx.stack_forward_pooled(h, step=s, prefetch=True, trace=True)
+        ids, gs = ids.cpu().numpy(), gs.cpu().numpy()
+        hr = h0.clone()
+        _, rids, _ = res.stack_forward(hr, trace=True)
+        assert np.array_equal(rids.cpu().numpy(), ids)
+        assert rel_l2(h.cpu().numpy(), hr.cpu().numpy()) <= 2e-3
+        for l in range(L):
+            if l > 0:
+                guess = sorted(set(int(e) for e in gs[l].ravel()))
+                try:
+                    if len(guess) <= C:
+                        sims[l].prefetch(guess, s)
+                except ValueError:
+                    pass                      # does not fit the dynamic slots: not prefetched
+            chunks = _chunks(ids[l], set(hot[l]), C - n_hot)
+            n_chunked += len(chunks) > 1
+            for g in chunks:
+                sims[l].ensure(g, s)
+    torch.cuda.synchronize()
+    assert ctx.check_device_errors() == 0
+    assert n_chunked > 0
+    for l in range(L):
+        assert ctx.cache_events(l) == [e.as_tuple() for e in sims[l].events], f"layer {l}"
+    say(f"  chunked layer calls: {n_chunked} of {steps * L}")
+    ctx.close()
+    res.close()

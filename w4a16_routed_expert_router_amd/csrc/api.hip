@@ -184,6 +184,7 @@ struct moe_ctx {
   int32_t* pool_ids = nullptr;  // dev [n_layers, T, k] (room for max_tokens): routed ids, forced ids of the layer calls
   float* pool_w = nullptr;      // dev [max_tokens, k]
   int32_t* pool_gids = nullptr; // dev [max_tokens, k]: next layer's guessed ids
+  int32_t* pool_cids = nullptr; // dev [n_layers, max_tokens, k]: forced ids of a token chunk
   int32_t* pool_ids_h = nullptr;   // pinned host [2, max_tokens, k]: routed + guessed ids
   // kernel timer
   int timer_kind = -1;
@@ -266,6 +267,27 @@ moe_status check_layer(moe_ctx* c, int layer) {
 }
 
 bool pooled(const moe_ctx* c) { return c->cfg.policy != MOE_RESIDENT_ALL; }
+
+// Keeps the timing events of a layer's transfers bounded: once many are held,
+// the pairs whose transfers have completed are folded into h2d_seconds (the
+// rest are kept for moe_cache_stats, which waits for them).
+void note_transfer(LayerState& L, hipEvent_t t0, hipEvent_t t1) {
+  L.timing.emplace_back(t0, t1);
+  if (L.timing.size() < 256) return;
+  size_t keep = 0;
+  for (auto& p : L.timing) {
+    float ms = 0.0f;
+    if (hipEventQuery(p.second) == hipSuccess && hipEventElapsedTime(&ms, p.first, p.second) == hipSuccess) {
+      L.stats.h2d_seconds += ms * 1e-3;
+      (void)hipEventDestroy(p.first);
+      (void)hipEventDestroy(p.second);
+    } else {
+      (void)hipGetLastError();  // not complete yet (hipErrorNotReady)
+      L.timing[keep++] = p;
+    }
+  }
+  L.timing.resize(keep);
+}
 
 // GPU row that holds logical slot `slot` of a pooled layer.
 int32_t row_of(const LayerState& L, int32_t slot) { return L.spare ? L.phys[slot] : slot; }
@@ -646,6 +668,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
     ok = ok && dalloc((void**)&c->pool_ids, (size_t)g.n_layers * P * 4);
     ok = ok && dalloc((void**)&c->pool_w, (size_t)P * 4);
     ok = ok && dalloc((void**)&c->pool_gids, (size_t)P * 4);
+    ok = ok && dalloc((void**)&c->pool_cids, (size_t)g.n_layers * P * 4);
     if (ok && hipHostMalloc((void**)&c->pool_ids_h, (size_t)2 * P * 4, hipHostMallocDefault) != hipSuccess) {
       (void)hipGetLastError();
       c->pool_ids_h = nullptr;
@@ -708,7 +731,7 @@ void moe_destroy(moe_ctx* c) {
   void* bufs[] = {c->logits, c->rscratch, c->ids,  c->w,    c->ids_s,   c->active,  c->n_active, c->perm_tok,
                   c->pos_of, c->hbuf, c->ybuf, c->xbuf,    c->err,     c->hshared,  c->yshared,
                   c->dlayers, c->mtile_off, c->xh, c->xlg, c->xhb, c->xgate, c->epoch,
-                  c->pool_x, c->pool_ids, c->pool_w, c->pool_gids};
+                  c->pool_x, c->pool_ids, c->pool_w, c->pool_gids, c->pool_cids};
   for (void* p : bufs) (void)hipFree(p);
   if (c->pool_ids_h) (void)hipHostFree(c->pool_ids_h);
   c->copier.reset();
@@ -945,7 +968,7 @@ moe_status moe_cache_ensure(moe_ctx* c, int32_t layer, const int32_t* experts, i
       L.stats.failures += 1;
       return fail(c, MOE_E_TRANSFER, "miss transfer failed before publication");
     }
-    L.timing.emplace_back(t0, t1);
+    note_transfer(L, t0, t1);
   }
   if (nmiss > 0 || nfirst > 0) {
     // publication in stream order, after the copies
@@ -1018,7 +1041,7 @@ moe_status moe_cache_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts,
     return fail(c, MOE_E_TRANSFER, "prefetch transfer failed; nothing was published");
   }
   L.pf_recorded = true;
-  L.timing.emplace_back(t0, t1);
+  note_transfer(L, t0, t1);
   // the victims' old copies are being overwritten: their map entries go to -1
   // in `stream` order, so no later kernel can read a victim through a stale map
   PublishArgs pa{};
@@ -1079,7 +1102,7 @@ moe_status moe_cache_pin(moe_ctx* c, int32_t layer, const int32_t* experts, int3
     L.stats.failures += 1;
     return fail(c, MOE_E_TRANSFER, "hot-set transfer failed; nothing was published");
   }
-  L.timing.emplace_back(t0, t1);
+  note_transfer(L, t0, t1);
   PublishArgs pa{};
   pa.map = L.map;
   for (const auto& d : dec) {
@@ -1115,13 +1138,13 @@ moe_status moe_stack_forward_pooled(moe_ctx* c, int32_t layer_begin, int32_t lay
   const int k = g.top_k, P = T * k;
   int32_t* ids_h = c->pool_ids_h;
   int32_t* gids_h = c->pool_ids_h + (int64_t)g.max_tokens * k;
-  // distinct ids of T tokens, ascending
-  auto group_of = [&](const int32_t* v, std::vector<int32_t>& grp) {
-    grp.assign(v, v + P);
+  // distinct ids of tokens [t0, t1), ascending
+  auto group_of = [&](const int32_t* v, int t0, int t1, std::vector<int32_t>& grp) {
+    grp.assign(v + (int64_t)t0 * k, v + (int64_t)t1 * k);
     std::sort(grp.begin(), grp.end());
     grp.erase(std::unique(grp.begin(), grp.end()), grp.end());
   };
-  std::vector<int32_t> grp, guess, slots;
+  std::vector<int32_t> grp, next, guess, slots;
   for (int l = layer_begin; l < layer_end; ++l) {
     int32_t* ids_l = c->pool_ids + (int64_t)l * P;  // forced ids of the layer call: [L, T, k]
     const bool guess_next = prefetch && l + 1 < layer_end;
@@ -1138,22 +1161,61 @@ moe_status moe_stack_forward_pooled(moe_ctx* c, int32_t layer_begin, int32_t lay
     HIPCHK(c, hipMemcpyAsync(ids_h, ids_l, (size_t)P * 4, hipMemcpyDeviceToHost, s));
     if (guess_next) HIPCHK(c, hipMemcpyAsync(gids_h, c->pool_gids, (size_t)P * 4, hipMemcpyDeviceToHost, s));
     HIPCHK(c, hipStreamSynchronize(s));
-    group_of(ids_h, grp);
-    slots.resize(grp.size());
-    if (moe_status st = moe_cache_ensure(c, l, grp.data(), (int32_t)grp.size(), slots.data(), step, stream))
-      return st;
-    if (guess_next) {
-      group_of(gids_h, guess);
+    const PolicyEngine& eng = *c->layers[l].policy;
+    const int dyn = g.slots_per_layer - eng.pinned_count();  // slots outside the hot set
+    auto outside = [&](const std::vector<int32_t>& v) {
+      int n = 0;
+      for (int e : v) n += eng.is_pinned(e) ? 0 : 1;
+      return n;
+    };
+    auto do_prefetch = [&]() -> moe_status {
+      if (!guess_next) return MOE_OK;
+      group_of(gids_h, 0, T, guess);
       // a guess that does not fit the pool's dynamic slots is not prefetched
       // (the engine is left unchanged by that refusal)
-      if ((int32_t)guess.size() <= g.slots_per_layer) {
-        const moe_status st = moe_cache_prefetch(c, l + 1, guess.data(), (int32_t)guess.size(), step, stream);
-        if (st != MOE_OK && st != MOE_E_CAPACITY) return st;
-      }
+      if ((int32_t)guess.size() > g.slots_per_layer) return MOE_OK;
+      const moe_status st = moe_cache_prefetch(c, l + 1, guess.data(), (int32_t)guess.size(), step, stream);
+      return st == MOE_E_CAPACITY ? MOE_OK : st;
+    };
+    group_of(ids_h, 0, T, grp);
+    if (outside(grp) <= dyn) {
+      slots.resize(grp.size());
+      if (moe_status st = moe_cache_ensure(c, l, grp.data(), (int32_t)grp.size(), slots.data(), step, stream))
+        return st;
+      if (moe_status st = do_prefetch()) return st;
+      // the layer itself, routed by the ids just read (the same router, the same x)
+      if (moe_status st = moe_stack_forward(c, l, l + 1, h, T, c->pool_ids, nullptr, nullptr, nullptr, stream))
+        return st;
+      continue;
     }
-    // the layer itself, routed by the ids just read (the same router, the same x)
-    if (moe_status st = moe_stack_forward(c, l, l + 1, h, T, c->pool_ids, nullptr, nullptr, nullptr, stream))
-      return st;
+    // The batch's routed group does not fit the slots outside the hot set: the
+    // layer runs over contiguous token chunks, each the longest run from its
+    // first token whose group fits, one after another (each chunk's group is
+    // ensured, then computed, so a later chunk may evict an expert only after
+    // the earlier chunk that read it has retired).
+    if (moe_status st = do_prefetch()) return st;
+    for (int t0 = 0; t0 < T;) {
+      int t1 = t0 + 1;
+      group_of(ids_h, t0, t1, grp);
+      if (outside(grp) > dyn)
+        return fail(c, MOE_E_CAPACITY, "one token's experts exceed the pool's slots outside the hot set");
+      while (t1 < T) {
+        group_of(ids_h, t0, t1 + 1, next);
+        if (outside(next) > dyn) break;
+        grp.swap(next);
+        ++t1;
+      }
+      slots.resize(grp.size());
+      if (moe_status st = moe_cache_ensure(c, l, grp.data(), (int32_t)grp.size(), slots.data(), step, stream))
+        return st;
+      const int Tc = t1 - t0;
+      int32_t* cids = c->pool_cids + (int64_t)l * Tc * k;  // forced ids of the chunk call: [L, Tc, k]
+      HIPCHK(c, hipMemcpyAsync(cids, ids_l + (int64_t)t0 * k, (size_t)Tc * k * 4, hipMemcpyDeviceToDevice, s));
+      if (moe_status st = moe_stack_forward(c, l, l + 1, h + (int64_t)t0 * g.hidden, Tc, c->pool_cids, nullptr,
+                                            nullptr, nullptr, stream))
+        return st;
+      t0 = t1;
+    }
   }
   return MOE_OK;
 }
