@@ -31,9 +31,9 @@ N_INPUTS = 32
 # the kernel sources they were taken on (sha256 prefixes below); a changed
 # kernel reports traffic = null until the counters are taken again.
 COUNTED_TRAFFIC = {
-    "bytes": 460_667_500,
+    "bytes": 460_669_500,
     "sources": {"decode_fused.hip": "797a12d1a7250f4c", "common.hpp": "37382b37738b7af7",
-                "launch.hpp": "cde11929a039a6ba"},
+                "launch.hpp": "b7745b977f9c10ce"},
 }
 
 
@@ -281,10 +281,10 @@ def extra_prefetch(moe, fx, dev, stream, steps=64, layers=16):
     h0s = torch.stack([fx.activations(("bench-prefetch-h0", i), 1, shape.hidden, device="cuda").float()
                        for i in range(32)])
     res = {"steps": steps, "layers": layers, "routing": "natural (router of each layer)"}
-    for policy, C in (("lru", 16), ("lfu", 32), ("lfu", 48)):
+    for policy, C, spare in (("lru", 16, 0), ("lfu", 32, 0), ("lfu", 48, 0), ("lfu", 32, 8)):
         outs = {}
         for pf in (False, True):
-            ctx = moe.MoEContext(shape, n_layers=layers, max_tokens=1, policy=policy, slots=C)
+            ctx = moe.MoEContext(shape, n_layers=layers, max_tokens=1, policy=policy, slots=C, spare_rows=spare)
             for l, w in enumerate(lw):
                 ctx.register_layer(l, w)
             out = torch.empty((steps, 1, shape.hidden), dtype=torch.float32, device=dev)
@@ -309,8 +309,9 @@ def extra_prefetch(moe, fx, dev, stream, steps=64, layers=16):
                 row["prefetches_per_token"] = round(pfs / steps, 2)
                 row["prefetch_used_frac"] = round(sum(x["prefetch_used"] for x in st) / max(pfs, 1), 4)
             outs[pf] = out
-            res[f"{policy}_C{C}_{'prefetch' if pf else 'no_prefetch'}"] = row
-        res[f"{policy}_C{C}_bit_identical"] = bool(torch.equal(outs[True], outs[False]))
+            tag = f"{policy}_C{C}" + (f"_spare{spare}" if spare else "")
+            res[f"{tag}_{'prefetch' if pf else 'no_prefetch'}"] = row
+        res[f"{tag}_bit_identical"] = bool(torch.equal(outs[True], outs[False]))
     return res
 
 
