@@ -428,3 +428,43 @@ def test_pool_batch_group_larger_than_dynamic_slots_runs_in_chunks(moe, olmoe_la
     say(f"  chunked layer calls: {n_chunked} of {steps * L}")
     ctx.close()
     res.close()
+
+
+def test_pool_qwen_like_natural_routing_prefetch(moe):
+    # the Qwen3-Next-like shape (512 experts, top-10 renormalised, always-on
+    # shared expert outside the pool): natural routing over 64-slot pools with
+    # prefetch gives the all-resident stack's ids and outputs, and the oracle's
+    # decisions
+    say("test_pool_qwen_like_natural_routing_prefetch")
+    from gpu_util import rel_l2
+    shape, nl, C, steps = fx.QWEN_NEXT, 4, 64, 6
+    layers = [{k: v.cpu().numpy() for k, v in
+               fx.layer_weights(shape, "pool-qwen", l, device="cuda", batched=True).items()}
+              for l in range(nl)]
+    pool = moe.MoEContext(shape, n_layers=nl, max_tokens=1, policy="lfu", slots=C, spare_rows=10)
+    res = moe.MoEContext(shape, n_layers=nl, max_tokens=1)
+    for l, w in enumerate(layers):
+        pool.register_layer(l, w)
+        res.register_layer(l, w)
+    sims = [ora.CacheSim(ora.LFU, shape.n_experts, C, layer=l) for l in range(nl)]
+    for s in range(steps):
+        h0 = fx.activations(("pool-qwen-h0", s), 1, shape.hidden, device="cuda").float()
+        h = h0.clone()
+        ids, gs = pool.stack_forward_pooled(h, step=s, prefetch=True, trace=True)
+        ids, gs = ids.cpu().numpy(), gs.cpu().numpy()
+        hr = h0.clone()
+        _, rids, _ = res.stack_forward(hr, trace=True)
+        assert np.array_equal(rids.cpu().numpy(), ids)
+        assert rel_l2(h.cpu().numpy(), hr.cpu().numpy()) <= 2e-3
+        for l in range(nl):
+            if l > 0:
+                sims[l].prefetch(sorted(set(int(e) for e in gs[l].ravel())), s)
+            sims[l].ensure(sorted(set(int(e) for e in ids[l].ravel())), s)
+    torch.cuda.synchronize()
+    assert pool.check_device_errors() == 0
+    for l in range(nl):
+        assert pool.cache_events(l) == [e.as_tuple() for e in sims[l].events], f"layer {l}"
+        st = pool.cache_stats(l)
+        assert st["prefetch_used"] == sims[l].prefetch_used
+    pool.close()
+    res.close()
