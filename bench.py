@@ -385,8 +385,8 @@ def extra_trace_analysis(moe, fx, steps=256):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                          "(the multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1 "
+                          "(expert-parallel sharding over several GPUs is not built)"}))
         sys.exit(2)
     import numpy as np
     import torch
