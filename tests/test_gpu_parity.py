@@ -311,3 +311,34 @@ def test_layer_shared_expert_two_subtiles(moe, T):
     say(f"test_layer_shared_expert_two_subtiles T={T}")
     shape = fx.MoEShape(hidden=2048, n_experts=16, inter=512, top_k=2, renorm=True, shared_inter=512)
     _layer_case(moe, shape, "gpu-shared-2sub", T)
+
+
+def test_boundary_rejects_empty_and_oversized_batches(moe):
+    # T = 0 and T > max_tokens are refused before anything is enqueued, at every
+    # entry point that takes a batch; the context keeps working afterwards
+    import ctypes as C
+    from w4a16_routed_expert_router_amd import capi
+    say("test_boundary_rejects_empty_and_oversized_batches")
+    wts = gpu_layer(SMALL, "gpu-boundary", 0)
+    ctx = _ctx(moe, SMALL, max_tokens=8)
+    ctx.register_layer(0, wts)
+    lib, h = capi.load(), ctx._h
+    H, k = SMALL.hidden, SMALL.top_k
+    x = torch.zeros((16, H), dtype=torch.float16, device="cuda")
+    hh = torch.zeros((16, H), dtype=torch.float32, device="cuda")
+    ids = torch.zeros((16, k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((16, k), dtype=torch.float32, device="cuda")
+    out = torch.zeros((16, H), dtype=torch.float16, device="cuda")
+    p = lambda t: C.c_void_p(t.data_ptr())
+    for T in (0, 9, -1):
+        assert lib.moe_route(h, 0, p(x), T, None, p(ids), p(w), None, None) == capi.MOE_E_ARG
+        assert lib.moe_expert_forward(h, 0, p(x), T, p(ids), p(w), p(out), None) == capi.MOE_E_ARG
+        assert lib.moe_stack_forward(h, 0, 1, p(hh), T, None, None, None, None, None) == capi.MOE_E_ARG
+        assert lib.moe_rmsnorm(h, p(hh), T, p(out), None) == capi.MOE_E_ARG
+        assert lib.moe_last_error(h)
+    # an unregistered layer and a layer out of range are refused too
+    assert lib.moe_route(h, 1, p(x), 1, None, p(ids), p(w), None, None) != capi.MOE_OK
+    xs = fx.activations(("gpu-boundary-x",), 8, H).numpy()
+    _check_route(ctx, wts, SMALL, xs)
+    assert ctx.check_device_errors() == 0
+    ctx.close()
