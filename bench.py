@@ -25,6 +25,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 N_INPUTS = 32
+N_CHECK = 4          # inputs whose final residual is checked against the oracle
+REL_L2_TOL = 2e-3    # layer-output tolerance, applied to the final residual
 
 # HBM bytes per launch of the fused decode kernel from the FETCH_SIZE /
 # WRITE_SIZE counter passes (scaled by a 1 GiB reference copy), valid only for
@@ -79,25 +81,55 @@ def gateup_bytes_per_launch(shape, n_active):
     return n_active * 2 * (shape.code_bytes + 2 * shape.scale_count)
 
 
-def cpu_baseline(shape, layers_np, h0_np, budget_s):
-    import numpy as np
-    from oracle import moe_oracle as ora
+def host_cpu():
+    """CPU model (/proc/cpuinfo), the cores this process may run on, and the
+    BLAS library numpy calls."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0))
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        libs = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
     except Exception:
-        threads = 1
+        pass
+    return model, cores, blas
+
+
+def cpu_baseline(shape, layers_np, h0_np, budget_s, min_inputs):
+    """The oracle on the host cores: as many whole 16-layer inputs as fit in
+    `budget_s` (at least `min_inputs`), BLAS threads = the cores of the
+    process's affinity mask."""
+    from oracle import moe_oracle as ora
+    model, cores, blas = host_cpu()
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+    except Exception:
+        limiter = None
     t0 = time.perf_counter()
     outs = []
     while len(outs) < len(h0_np):
         outs.append(ora.stack_forward(h0_np[len(outs)], layers_np, shape)["h"])
-        if time.perf_counter() - t0 > budget_s:
+        if len(outs) >= min_inputs and time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister()
     n = len(outs)
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{n} of the {len(h0_np)} batch-1 inputs through all {len(layers_np)} layers "
-                      f"(float64 numpy oracle, exact router), {dt:.1f} s"}, outs
+                      f"(float64 numpy oracle, exact router), {dt:.1f} s",
+            "cpu": model, "blas": blas, "blas_threads": int(cores)}, outs
 
 
 MFMA_FP16_PEAK_TFLOPS = 2500.0
@@ -396,6 +428,10 @@ def main():
 
     shape, L, T = fx.OLMOE, 16, 1
     dev = torch.device("cuda", 0)
+    # one stream for everything: inputs, library calls, copies and checks are
+    # all ordered on it (graph capture needs a stream other than the default)
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.set_stream(stream)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 18          # float32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -422,7 +458,6 @@ def main():
     t_gen = time.perf_counter() - t_gen
     print(f"[bench] weights generated and registered in {t_gen:.1f} s", file=sys.stderr, flush=True)
 
-    stream = torch.cuda.Stream(device=dev)
     h = torch.empty((T, shape.hidden), dtype=torch.float32, device=dev)
 
     def step(i):
@@ -483,13 +518,20 @@ def main():
         kname, per_launch = "gateup_gemv_kernel<64>", gateup_bytes_per_launch(shape, shape.top_k * T)
     achieved = per_launch / (avg_ms * 1e-3) / 1e9
 
-    # final residual of the first inputs (compared with the oracle below)
-    finals = []
-    for i in range(4):
-        hb = h0[i].clone()
-        ctx.stack_forward(hb, stream=stream)
-        finals.append(hb)
+    # final residuals of the first inputs, compared with the oracle below: the
+    # graph replays the timed loop ran, and direct launches.  Every copy is
+    # enqueued on `stream`, the stream the kernel runs on, so nothing reads
+    # an input before it has landed.
+    finals_graph, finals_direct = [], []
+    with torch.cuda.stream(stream):
+        for i in range(N_CHECK):
+            run(i)
+            finals_graph.append(h.clone())
+            hb = h0[i].clone()
+            ctx.stack_forward(hb, stream=stream)
+            finals_direct.append(hb)
     stream.synchronize()
+    graph_eq_direct = all(torch.equal(a, b) for a, b in zip(finals_graph, finals_direct))
     assert ctx.check_device_errors(stream) == 0
 
     bytes_tok = algorithmic_bytes_per_token(shape, L)
@@ -535,19 +577,33 @@ def main():
         extra["policy_sweep_zipf"] = extra_trace_analysis(moe, fx)
         print(f"[bench] policy sweep done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
         out["extra"] = extra
+    # the oracle: the CPU baseline (timed) and the reference of the check;
+    # with --no-cpu-baseline only the checked inputs are computed, untimed
+    h0_np = [h0[i].cpu().numpy().astype(np.float16) for i in range(N_INPUTS)]
     if not args.no_cpu_baseline:
-        h0_np = [h0[i].cpu().numpy().astype(np.float16) for i in range(N_INPUTS)]
-        cb, refs = cpu_baseline(shape, layers_np, h0_np, args.cpu_seconds)
-        cb["cpu"] = platform.processor() or platform.machine()
+        cb, refs = cpu_baseline(shape, layers_np, h0_np, args.cpu_seconds, N_CHECK)
         out["cpu_baseline"] = cb
-        errs = []
-        for i, ref in enumerate(refs[:len(finals)]):
-            got = finals[i].cpu().numpy().astype(np.float64).reshape(ref.shape)
+    else:
+        from oracle import moe_oracle as ora
+        refs = [ora.stack_forward(h0_np[i], layers_np, shape)["h"] for i in range(N_CHECK)]
+    errs = []
+    for i in range(N_CHECK):
+        ref = refs[i]
+        for got_t in (finals_graph[i], finals_direct[i]):
+            got = got_t.cpu().numpy().astype(np.float64).reshape(ref.shape)
             errs.append(float(np.linalg.norm(got - ref) / np.linalg.norm(ref)))
-        out["oracle_check"] = {"inputs": len(errs), "max_rel_l2": max(errs) if errs else None,
-                               "tolerance": 2e-3}
+    ok = graph_eq_direct and max(errs) <= REL_L2_TOL
+    out["oracle_check"] = {"inputs": N_CHECK, "checked": "graph replays of the timed loop and direct launches",
+                           "max_rel_l2": max(errs), "tolerance": REL_L2_TOL,
+                           "graph_equals_direct": graph_eq_direct, "pass": ok}
+    if not ok:
+        out["valid"] = False
     print(json.dumps(out), flush=True)
     ctx.close()
+    if not out["oracle_check"]["pass"]:
+        print("[bench] oracle check FAILED: the timed path's outputs disagree with the oracle",
+              file=sys.stderr, flush=True)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -311,6 +311,115 @@ def test_rmsnorm_constant_vector_closed_form():
     assert np.all(x == np.float16(3.0 / math.sqrt(9.0 + 1e-5)))
 
 
+def _fp16_of_exact(num: Fraction, den_sq: Fraction) -> np.float16:
+    """FP16 nearest to num / sqrt(den_sq), from 60-digit decimal arithmetic;
+    the value is checked to lie far from an FP16 rounding midpoint, so the
+    rounding through float64 cannot differ from rounding the exact value."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    v = Decimal(num.numerator) / Decimal(num.denominator) / (
+        Decimal(den_sq.numerator) / Decimal(den_sq.denominator)).sqrt()
+    r = np.float16(float(v))
+    lo, hi = np.nextafter(r, np.float16(-np.inf)), np.nextafter(r, np.float16(np.inf))
+    for nb in (lo, hi):
+        mid = (Decimal(float(r)) + Decimal(float(nb))) / 2
+        assert abs(v - mid) > abs(Decimal(float(nb)) - Decimal(float(r))) / 64
+    return r
+
+
+def test_rmsnorm_alternating_vector_exact():
+    """h = [3, 4, 3, 4, ...]: mean(h^2) = 12.5 (mean(h)^2 would be 12.25, and
+    a sum instead of a mean 3200), so x = h / sqrt(12.5 + 1e-5) in exact
+    arithmetic, rounded once to FP16."""
+    H = 256
+    h = np.tile(np.array([3.0, 4.0]), H // 2)[None, :]
+    x = ora.rmsnorm_fp16(h)
+    ms = Fraction(25, 2) + Fraction(1, 100000)
+    want3, want4 = _fp16_of_exact(Fraction(3), ms), _fp16_of_exact(Fraction(4), ms)
+    assert np.all(x[0, 0::2] == want3) and np.all(x[0, 1::2] == want4)
+    # the readings this pin rejects give other FP16 values
+    assert want3 != np.float16(3.0 / 3.5) and want4 != np.float16(4.0 / 3.5)
+
+
+def test_rmsnorm_small_norm_pins_eps():
+    """|h_i| = 2^-10 for every i: mean(h^2) = 2^-20 ~ 9.5e-7, the same order as
+    eps, so eps = 1e-5 decides the result: x = 2^-10 / sqrt(2^-20 + 1e-5)
+    (~0.3028), where eps = 0 gives 1, eps = 1e-6 gives ~0.70 and eps = 1e-4
+    gives ~0.0976."""
+    H = 512
+    sgn = np.where(np.arange(H) % 3 == 0, -1.0, 1.0)
+    h = (sgn * 2.0 ** -10)[None, :]
+    x = ora.rmsnorm_fp16(h)
+    ms = Fraction(1, 2 ** 20) + Fraction(1, 100000)
+    want = _fp16_of_exact(Fraction(1, 2 ** 10), ms)
+    assert np.all(x[0] == (sgn * float(want)).astype(np.float16))
+    for eps in (0.0, 1e-6, 1e-4):
+        other = _fp16_of_exact(Fraction(1, 2 ** 10), Fraction(1, 2 ** 20) + Fraction(eps))
+        assert other != want
+
+
+def test_rmsnorm_rows_are_independent():
+    """Each token (row) is normalised by its own mean square."""
+    h = np.stack([np.full(256, 3.0), np.tile([3.0, 4.0], 128)])
+    x = ora.rmsnorm_fp16(h)
+    assert np.all(x[0] == np.float16(3.0 / math.sqrt(9.0 + 1e-5)))
+    assert np.array_equal(x[1], ora.rmsnorm_fp16(h[1:2])[0])
+
+
+def _py_rmsnorm_fp16(hrow):
+    ms = sum(v * v for v in hrow) / len(hrow)
+    r = 1.0 / math.sqrt(ms + 1e-5)
+    return [float(np.float16(v * r)) for v in hrow]
+
+
+def _py_layer(xrow, wts, shape):
+    """One token through one layer with scalar Python: Fraction-exact logits,
+    (logit desc, id asc) order, softmax probabilities, rank-ordered sum."""
+    H, I, k = shape.hidden, shape.inter, shape.top_k
+    logits = [_fraction_dot(np.asarray(xrow, dtype=np.float16), wts["router"][e])
+              for e in range(shape.n_experts)]
+    order = sorted(range(shape.n_experts), key=lambda e: (-logits[e], e))[:k]
+    m = max(float(v) for v in logits)
+    p = [math.exp(float(v) - m) for v in logits]
+    tot = sum(p)
+    out = [0.0] * H
+    for e in order:
+        mats = [_py_matrix(wts["q"][e][m_], wts["s"][e][m_], *nk, 128)
+                for m_, nk in ((0, (I, H)), (1, (I, H)), (2, (H, I)))]
+        y = _py_ffn(xrow, *mats)
+        out = [o + p[e] / tot * yy for o, yy in zip(out, y)]
+    return out, order
+
+
+def test_stack_two_layer_recurrence_python_loops():
+    """Two layers, one token: h1 = h0 + L0(n(h0)), h2 = h1 + L1(n(h1)), with
+    n, the routing and the FFN written as scalar Python loops.  Normalising h0
+    at both layers, skipping the residual, or reusing layer 0's weights would
+    each give another h2 (checked below, so the pin keeps its power)."""
+    sh = SMALL
+    l0, l1 = _small_layer(layer=0), _small_layer(layer=1)
+    h0 = fx.activations(("pin-stack-2",), 1, sh.hidden).numpy()
+    res = ora.stack_forward(h0, [l0, l1], sh)
+    h = [float(v) for v in h0[0]]
+    x0 = _py_rmsnorm_fp16(h)
+    o0, ids0 = _py_layer(x0, l0, sh)
+    h1 = [a + b for a, b in zip(h, o0)]
+    x1 = _py_rmsnorm_fp16(h1)
+    o1, ids1 = _py_layer(x1, l1, sh)
+    h2 = [a + b for a, b in zip(h1, o1)]
+    assert res["ids"][0][0].tolist() == ids0 and res["ids"][1][0].tolist() == ids1
+    assert np.array_equal(res["x"][1][0].astype(np.float64), np.array(x1))
+    np.testing.assert_allclose(res["h"][0], h2, rtol=1e-9, atol=1e-9)
+    # slips this pin must catch
+    stale, _ = _py_layer(x0, l1, sh)
+    wrong_norm = [a + b for a, b in zip(h1, stale)]
+    same_w, _ = _py_layer(x1, l0, sh)
+    wrong_layer = [a + b for a, b in zip(h1, same_w)]
+    no_resid = o1
+    for bad in (wrong_norm, wrong_layer, no_resid):   # each far outside the 1e-9 tolerance above
+        assert np.max(np.abs(np.array(bad) - np.array(h2))) > 1e-6
+
+
 def test_stack_zero_weights_is_identity_and_one_layer_is_layer():
     wts = _small_layer()
     zero = dict(wts)

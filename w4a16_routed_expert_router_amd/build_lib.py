@@ -35,21 +35,39 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    missing = [s for s in srcs if not os.path.exists(s)]
-    if missing:
-        raise RuntimeError(f"missing sources: {missing}")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-o", tmp,
-           "-I", os.path.join(ROOT, "include"), *srcs, "-lpthread"]
-    # policy.cpp and trace_analysis.cpp have no device code; hipcc compiles them as host C++.
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libmoe_w4a16.so")
+    return res.returncode
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source to an object in parallel (in-tree, under
+    _build/), then links libmoe_w4a16.so.  Always recompiles."""
+    from concurrent.futures import ThreadPoolExecutor
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    missing = [s for s in srcs if not os.path.exists(s)]
+    if missing:
+        raise RuntimeError(f"missing sources: {missing}")
+    obj_dir = os.path.join(ROOT, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
+    # policy.cpp and trace_analysis.cpp have no device code; hipcc compiles them as host C++.
+    jobs = []
+    for src in srcs:
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        jobs.append((obj, [hipcc(), *HIP_FLAGS, *inc, "-c", src, "-o", obj]))
+    workers = max(1, min(len(jobs), len(os.sched_getaffinity(0)), 16))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        rcs = list(ex.map(lambda j: _run(j[1], verbose), jobs))
+    if any(rcs):
+        raise RuntimeError("hipcc failed compiling the library sources")
+    tmp = LIB + ".tmp"
+    if _run([hipcc(), *HIP_FLAGS, "-shared", "-o", tmp, *[j[0] for j in jobs], "-lpthread"], verbose):
+        raise RuntimeError("hipcc failed linking libmoe_w4a16.so")
     os.replace(tmp, LIB)
     return LIB
 
