@@ -171,7 +171,12 @@ typedef struct moe_cache_event {
 
 /* ---- lifetime -------------------------------------------------------------- */
 
-/* Validates `cfg`, selects cfg->device, allocates per-layer HBM expert storage
+/* Context creation ("Horizon RunMap - Architecture, Results and Public
+ * Evaluation", "Partial-residency contract: immutable authority and miss
+ * lifecycle": capacity is fixed before admission and a pool too small for the
+ * routed group fails at startup; "The complete execution path": full or
+ * partial residency of the routed experts).
+ * Validates `cfg`, selects cfg->device, allocates per-layer HBM expert storage
  * (E experts, or C slots with policy != MOE_RESIDENT_ALL, plus pinned host
  * backing for all E experts), scratch sized by max_tokens, a side stream and
  * events.  Capacity is fixed here: with a slot pool, C < min(E, max_tokens*k)
@@ -203,7 +208,12 @@ moe_status moe_register_layer(moe_ctx* ctx, int32_t layer, const uint16_t* route
 
 /* ---- hot path ---------------------------------------------------------------- */
 
-/* Router of `layer` for T tokens (1 <= T <= max_tokens).
+/* Router of `layer` for T tokens (1 <= T <= max_tokens) ("Horizon RunMap -
+ * Architecture, Results and Public Evaluation", "The complete execution path":
+ * the router picks each token's experts before the routed group is acquired;
+ * "An expert-offloading engine, from scratch", "Terms used here": 8 of 64
+ * experts per token; "F51 Nitro / Nitro-MoE", "The thesis": 10 of 512 plus a
+ * shared expert).
  *   logit[t,e] = the FP32 value nearest (ties to even) to the exact sum
  *                sum_i x[t,i] * router[e,i];
  *   ids[t,:]   = the k experts with the largest logits, ordered by (logit
@@ -219,7 +229,13 @@ moe_status moe_route(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
                      const int32_t* forced_ids, int32_t* ids, float* w, float* logits,
                      void* stream);
 
-/* Routed experts of `layer` for T tokens, given their ids and weights:
+/* Routed experts of `layer` for T tokens, given their ids and weights
+ * ("Horizon RunMap - Architecture, Results and Public Evaluation",
+ * "Architecture invariants" and "What is implemented": the routed experts run
+ * from compact INT4 data with FP16 scales and FP16 activations, never
+ * expanded; "The complete execution path": custom W4A16 kernels over the
+ * routed group; "An expert-offloading engine, from scratch", "Correct first":
+ * caching never changes the result, hence the fixed summation order):
  *   out[t] = fp16( sum_{j=0}^{k-1} w[t,j] * FFN_{ids[t,j]}(x[t])
  *                  + FFN_shared(x[t]) )       (shared term iff shared_inter)
  *   FFN_e(x) = (silu(x Wg_e^T) * (x Wu_e^T)) Wd_e^T, silu(z) = z / (1 + e^-z),
@@ -288,7 +304,14 @@ moe_status moe_fused_phase_stamps(moe_ctx* ctx, uint64_t* dev_buf, int64_t count
 
 /* ---- expert-slot pool (partial residency) ------------------------------------ */
 
-/* ensure() of the slot pool of `layer` for one routed group.
+/* ensure() of the slot pool of `layer` for one routed group ("F51 Nitro /
+ * Nitro-MoE", "Layer 1 - expert persistence cache": lookup, evict, copy host
+ * to device, return the slot; "Horizon RunMap - Architecture, Results and
+ * Public Evaluation", "Partial-residency contract: immutable authority and
+ * miss lifecycle": an all-hit group reads the existing copies, a miss is
+ * transported H2D from the immutable host source and published only after
+ * the transfer completes, eviction discards the GPU copy, a failure before
+ * publication leaves the old generation authoritative).
  * experts: host int32 [n], distinct, 0 <= e < E, n <= C.  slots: host int32
  * [n] out: the slot each expert occupies.  step: a label copied into the event
  * log.  Hits refresh the policy state.  Each miss evicts a victim (chosen by
