@@ -248,6 +248,30 @@ moe_status moe_route(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
 moe_status moe_expert_forward(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
                               const int32_t* ids, const float* w, void* out, void* stream);
 
+/* Allocation-free variant of moe_expert_forward, for callers that cannot
+ * allocate device memory while they run it: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results and errors as moe_expert_forward (the same kernels, bit-identical
+ * outputs); the call makes no allocation of any kind (no hipMalloc, no
+ * hipFree, no event or library allocation).
+ * Its scratch (grouping lists, intermediates, expert outputs) lives in a
+ * static array of MOE_NOALLOC_SCRATCH_BYTES in each GPU's memory, held until
+ * the process ends.  A call needs about
+ *   T*k*(4*H + 2*max(I, Is) + 12) + 2*T*max(I, Is) + 36*E
+ *   (+ T*(2*Is + 4*H) with a shared expert)
+ * bytes (each part rounded up to 256); a T that needs more returns MOE_E_ARG
+ * (with the sizes in moe_last_error) and enqueues nothing.  The OLMoE-like
+ * shape (H 2048, I 1024, k 8, E 64) fits up to T = 99 tokens, the
+ * Qwen3-Next-like one (H 2048, I = Is = 512, k 10, E 512) up to T = 81.
+ * Every call on one GPU, from any context, uses the same array: two calls
+ * whose work overlaps on the GPU (different streams not ordered by events,
+ * or different threads) race and give undefined results.  Nothing in the
+ * array has to start at zero: every word a call reads is written earlier in
+ * that call. */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+moe_status moe_expert_forward_noalloc(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
+                                      const int32_t* ids, const float* w, void* out, void* stream);
+
 /* Residual stack over layers [layer_begin, layer_end):
  *   for l: x_l = fp16(RMSNorm(h)), RMSNorm(h) = h / sqrt(mean(h^2) + 1e-5);
  *          route x_l (forced_ids + l*T*k when forced_ids != NULL);

@@ -131,6 +131,19 @@ class MoEContext:
                                             _stream(stream, self.device)))
         return out
 
+    def expert_forward_noalloc(self, layer, x, ids, w, out, stream=None):
+        """moe_expert_forward_noalloc: the library's static scratch, no allocation
+        in the call; `out` (FP16 [T,H]) must be given."""
+        sh = self.shape
+        T = x.shape[0]
+        xp = _dev(x, torch.float16, (T, sh.hidden), self.device, "x")
+        ip = _dev(ids, torch.int32, (T, sh.top_k), self.device, "ids")
+        wp = _dev(w, torch.float32, (T, sh.top_k), self.device, "w")
+        op = _dev(out, torch.float16, (T, sh.hidden), self.device, "out")
+        self._check(_lib.moe_expert_forward_noalloc(self._h, layer, xp, T, ip, wp, op,
+                                                    _stream(stream, self.device)))
+        return out
+
     def stack_forward(self, h, layer_begin=0, layer_end=None, forced_ids=None, trace=False,
                       stream=None):
         """h: FP32 [T,H] CUDA tensor, updated in place.  forced_ids: int32 [L,T,k].

@@ -64,6 +64,7 @@ SIGNATURES = {
     "moe_register_layer": (_I, [_P, _I, _P, _P, _P, _P, _P]),
     "moe_route": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _P]),
     "moe_expert_forward": (_I, [_P, _I, _P, _I, _P, _P, _P, _P]),
+    "moe_expert_forward_noalloc": (_I, [_P, _I, _P, _I, _P, _P, _P, _P]),
     "moe_stack_forward": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
     "moe_check_device_errors": (_I, [_P, _P, C.POINTER(C.c_uint32)]),
     "moe_cache_ensure": (_I, [_P, _I, _P, _I, _P, _I, _P]),

@@ -31,9 +31,36 @@
 
 using namespace moe;
 
+// Scratch of moe_expert_forward_noalloc: a fixed array in every GPU's memory,
+// held until the process ends and shared by every call on that GPU.  Host
+// code never passes this name to a kernel (on the host it is only a stand-in
+// for the symbol): it uses the device address that hipGetSymbolAddress
+// returned for the current device, kept in g_scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_create_error;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on `device`, which must be the current device;
+// looked up once per device.  Returns null when the lookup fails.
+void* scratch_on_device(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[device] = p;
+  }
+  return g_scratch_ptr[device];
+}
 
 // Host copy into pinned staging, split over a few persistent threads (the
 // caller takes one part): one thread cannot fill a staging buffer as fast as
@@ -400,8 +427,10 @@ struct ScopedTimer {
   moe_ctx* c;
   hipStream_t s;
   hipEvent_t stop = nullptr;
-  ScopedTimer(moe_ctx* ctx, int kind, hipStream_t stream) : c(ctx), s(stream) {
-    if (c->timer_kind != kind) return;
+  ScopedTimer(moe_ctx* ctx, int kind, hipStream_t stream) : ScopedTimer(ctx, true, kind, stream) {}
+  // enabled = false: never times (and never creates events)
+  ScopedTimer(moe_ctx* ctx, bool enabled, int kind, hipStream_t stream) : c(ctx), s(stream) {
+    if (!enabled || c->timer_kind != kind) return;
     if (c->timer_used == c->timer_events.size()) {
       hipEvent_t a = nullptr, b = nullptr;
       if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
@@ -431,11 +460,64 @@ void run_router(moe_ctx* c, const RouterArgs& ra, hipStream_t s) {
   launch_router_topk(ra, s);
 }
 
+// Device scratch of the expert path of one call: the grouping's outputs, the
+// FP16 intermediates and the FP32 expert outputs.  Every word the kernels read
+// is written earlier in the same call, so nothing has to start at zero.
+struct ExpertScratch {
+  int32_t* ids_s;          // [P]
+  ActiveExpert* active;    // [2E]: active list, then the few-token kernel's list
+  int32_t* n_active;       // [2]
+  int32_t* perm_tok;       // [P]
+  int32_t* pos_of;         // [P]
+  int32_t* mtile_off;      // [E+1]
+  uint16_t* hbuf;          // [P + T, max(I, Is)] fp16
+  float* ybuf;             // [P, H]
+  uint16_t* hshared;       // [T, Is] fp16 (shared expert only)
+  float* yshared;          // [T, H]   (shared expert only)
+};
+
+ExpertScratch ctx_scratch(moe_ctx* c) {
+  return ExpertScratch{c->ids_s, c->active, c->n_active, c->perm_tok, c->pos_of,
+                       c->mtile_off, c->hbuf, c->ybuf, c->hshared, c->yshared};
+}
+
+// Carves the scratch of a T-token call out of `base` (256-byte aligned parts);
+// returns the bytes used, whether or not base is null.
+size_t carve_scratch(const moe_config& g, int T, uint8_t* base, ExpertScratch* out) {
+  const size_t P = (size_t)T * g.top_k;
+  const size_t Imax = (size_t)std::max(g.inter, g.shared_inter);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> uint8_t* {
+    uint8_t* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  ExpertScratch x{};
+  x.ids_s = (int32_t*)take(P * 4);
+  x.active = (ActiveExpert*)take((size_t)2 * g.n_experts * sizeof(ActiveExpert));
+  x.n_active = (int32_t*)take(2 * 4);
+  x.perm_tok = (int32_t*)take(P * 4);
+  x.pos_of = (int32_t*)take(P * 4);
+  x.mtile_off = (int32_t*)take((size_t)(g.n_experts + 1) * 4);
+  x.hbuf = (uint16_t*)take((P + T) * Imax * 2);
+  x.ybuf = (float*)take(P * g.hidden * 4);
+  if (g.shared_inter) {
+    x.hshared = (uint16_t*)take((size_t)T * g.shared_inter * 2);
+    x.yshared = (float*)take((size_t)T * g.hidden * 4);
+  }
+  if (out) *out = x;
+  return off;
+}
+
 // group -> gate/up -> down (routed and shared) -> combine into out or resid.
+// `timed`: launches may be bracketed by the kernel timer's events (which it
+// creates on first use); the allocation-free entry point passes false.
 moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const int32_t* ids,
-                       const float* w, uint16_t* out, float* resid, hipStream_t s) {
+                       const float* w, uint16_t* out, float* resid, hipStream_t s,
+                       const ExpertScratch& sc, bool timed = true) {
   LayerState& L = c->layers[layer];
   const moe_config& g = c->cfg;
+
   // experts with at least mfma_min tokens run on the MFMA grouped GEMM; the
   // choice depends only on the token counts
   // experts with few tokens take the persistent streaming kernel where the
@@ -452,32 +534,32 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   const int mfma_min = force_gemv ? INT32_MAX
                        : all_mfma ? 1
                        : (stream_gu ? kStreamTokens + 1 : kMfmaMinTokens);
-  GroupArgs ga{ids, T, g.top_k, g.n_experts, L.map, c->ids_s, c->active, c->n_active,
-               c->perm_tok, c->pos_of, c->err, mfma_min, c->mtile_off,
-               c->active + g.n_experts, c->n_active + 1};
+  GroupArgs ga{ids, T, g.top_k, g.n_experts, L.map, sc.ids_s, sc.active, sc.n_active,
+               sc.perm_tok, sc.pos_of, c->err, mfma_min, sc.mtile_off,
+               sc.active + g.n_experts, sc.n_active + 1};
   {
-    ScopedTimer tm(c, kKindGroup, s);
+    ScopedTimer tm(c, timed, kKindGroup, s);
     launch_group(ga, s);
   }
   const bool any_mfma = T >= mfma_min;
-  MfmaArgs ma{L.store, c->lay.total(), c->lay, c->active, c->n_active, c->mtile_off,
-              g.hidden, g.inter, x, c->perm_tok, c->hbuf, c->ybuf};
+  MfmaArgs ma{L.store, c->lay.total(), c->lay, sc.active, sc.n_active, sc.mtile_off,
+              g.hidden, g.inter, x, sc.perm_tok, sc.hbuf, sc.ybuf};
   ExpertArgs ea{};
   ea.mfma_min = mfma_min;
   ea.blobs = L.store;
   ea.blob_stride = c->lay.total();
   ea.lay = c->lay;
-  ea.active = c->active;
-  ea.n_active = c->n_active;
-  ea.small = c->active + g.n_experts;
-  ea.n_small = c->n_active + 1;
+  ea.active = sc.active;
+  ea.n_active = sc.n_active;
+  ea.small = sc.active + g.n_experts;
+  ea.n_small = sc.n_active + 1;
   ea.max_active = max_active(c, T);
   ea.H = g.hidden;
   ea.I = g.inter;
   ea.x = x;
-  ea.perm_tok = c->perm_tok;
-  ea.hbuf = c->hbuf;
-  ea.ybuf = c->ybuf;
+  ea.perm_tok = sc.perm_tok;
+  ea.hbuf = sc.hbuf;
+  ea.ybuf = sc.ybuf;
   // a shared expert of the routed experts' shape rides along in the streaming
   // launches as one more list entry (one weight stream over the whole chip
   // instead of two launches of its own)
@@ -486,25 +568,25 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   if (shared_in_stream) {
     ea.shared_blob = L.shared;
     ea.shared_count = T;
-    ea.shared_h = c->hshared;
-    ea.shared_y = c->yshared;
+    ea.shared_h = sc.hshared;
+    ea.shared_y = sc.yshared;
   }
   if (!all_mfma) {
-    ScopedTimer tm(c, kKindGateUp, s);
+    ScopedTimer tm(c, timed, kKindGateUp, s);
     if (stream_gu) launch_stream_expert(ea, 0, c->ncu, s);
     else launch_gateup_gemv(ea, s);
   }
   if (any_mfma) {
-    ScopedTimer tm(c, kKindMfmaGateUp, s);
+    ScopedTimer tm(c, timed, kKindMfmaGateUp, s);
     launch_mfma_gateup(ma, mfma_max_tiles(T, g.top_k, g.n_experts, g.inter, 0, mfma_min), s);
   }
   if (!all_mfma) {
-    ScopedTimer tm(c, kKindDown, s);
+    ScopedTimer tm(c, timed, kKindDown, s);
     if (stream_dn && stream_gu) launch_stream_expert(ea, 1, c->ncu, s);
     else launch_down_gemv(ea, s);
   }
   if (any_mfma) {
-    ScopedTimer tm(c, kKindMfmaDown, s);
+    ScopedTimer tm(c, timed, kKindMfmaDown, s);
     launch_mfma_down(ma, mfma_max_tiles(T, g.top_k, g.n_experts, g.hidden, 1, mfma_min), s);
   }
   if (g.shared_inter && !shared_in_stream) {
@@ -515,8 +597,8 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
     sa.fixed_count = T;
     sa.fixed_offset = 0;
     sa.I = g.shared_inter;
-    sa.hbuf = c->hshared;
-    sa.ybuf = c->yshared;
+    sa.hbuf = sc.hshared;
+    sa.ybuf = sc.yshared;
     const bool st_gu = !force_gemv && T <= kStreamTokens && stream_supported(0, g.hidden, g.shared_inter);
     const bool st_dn = st_gu && stream_supported(1, g.shared_inter, g.hidden);
     if (st_gu) launch_stream_expert(sa, 0, c->ncu, s);
@@ -524,10 +606,10 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
     if (st_dn) launch_stream_expert(sa, 1, c->ncu, s);
     else launch_down_gemv(sa, s);
   }
-  CombineArgs ca{c->ybuf, g.shared_inter ? c->yshared : nullptr, c->pos_of, w, T, g.top_k,
+  CombineArgs ca{sc.ybuf, g.shared_inter ? sc.yshared : nullptr, sc.pos_of, w, T, g.top_k,
                  g.hidden, out, resid};
   {
-    ScopedTimer tm(c, kKindCombine, s);
+    ScopedTimer tm(c, timed, kKindCombine, s);
     launch_combine(ca, s);
   }
   if (pooled(c)) HIPCHK(c, hipEventRecord(L.retired, s));
@@ -580,6 +662,10 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   c->shared_lay = BlobLayout{scb, ssc * 2};
   hipError_t e = hipSetDevice(g.device);
   if (e != hipSuccess) return fail(nullptr, MOE_E_HIP, std::string("hipSetDevice: ") + hipGetErrorString(e));
+  // the allocation-free entry point's scratch on this device (its address is
+  // looked up here, with the device current, once per device)
+  if (!scratch_on_device(g.device))
+    return fail(nullptr, MOE_E_HIP, "hipGetSymbolAddress of the static scratch failed");
 
   auto dalloc = [&](void** p, size_t bytes) -> bool {
     if (hipMalloc(p, bytes < 256 ? 256 : bytes) != hipSuccess) {
@@ -821,7 +907,26 @@ moe_status moe_expert_forward(moe_ctx* c, int32_t layer, const void* x, int32_t 
   if (x == out) return fail(c, MOE_E_ARG, "out must not alias x");
   if (T < 1 || T > c->cfg.max_tokens) return fail(c, MOE_E_ARG, "T out of range [1, max_tokens]");
   return run_experts(c, layer, (const uint16_t*)x, T, ids, w, (uint16_t*)out, nullptr,
-                     (hipStream_t)stream);
+                     (hipStream_t)stream, ctx_scratch(c));
+}
+
+moe_status moe_expert_forward_noalloc(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* ids,
+                                      const float* w, void* out, void* stream) {
+  if (moe_status st = check_ctx(c)) return st;
+  if (moe_status st = check_layer(c, layer)) return st;
+  if (!x || !ids || !w || !out) return fail(c, MOE_E_ARG, "x, ids, w and out are required");
+  if (x == out) return fail(c, MOE_E_ARG, "out must not alias x");
+  if (T < 1 || T > c->cfg.max_tokens) return fail(c, MOE_E_ARG, "T out of range [1, max_tokens]");
+  const size_t need = carve_scratch(c->cfg, T, nullptr, nullptr);
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(c, MOE_E_ARG, "T needs " + std::to_string(need) + " bytes of scratch, more than the " +
+                                  std::to_string((size_t)MOE_NOALLOC_SCRATCH_BYTES) + " of the static scratch");
+  uint8_t* base = (uint8_t*)g_scratch_ptr[c->cfg.device];  // looked up by moe_create on this device
+  if (!base) return fail(c, MOE_E_HIP, "static scratch address unknown on this device");
+  ExpertScratch sc{};
+  carve_scratch(c->cfg, T, base, &sc);
+  return run_experts(c, layer, (const uint16_t*)x, T, ids, w, (uint16_t*)out, nullptr, (hipStream_t)stream, sc,
+                     false);
 }
 
 moe_status moe_stack_forward(moe_ctx* c, int32_t layer_begin, int32_t layer_end, float* h, int32_t T,
@@ -893,7 +998,7 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t layer_begin, int32_t layer_end,
                   forced_ids ? forced_ids + l * tk : nullptr, ids, w, c->err,
                   (int)(g.flags & MOE_FLAG_ROUTER_EXACT_ALWAYS)};
     run_router(c, ra, s);
-    if (moe_status st = run_experts(c, l, x, T, ids, w, nullptr, h, s)) return st;
+    if (moe_status st = run_experts(c, l, x, T, ids, w, nullptr, h, s, ctx_scratch(c))) return st;
   }
   return MOE_OK;
 }
