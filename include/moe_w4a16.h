@@ -113,6 +113,26 @@ typedef enum moe_policy {
                                            min(C, max_tokens*k), else moe_create
                                            fails with MOE_E_CAPACITY             */
 
+#define MOE_FLAG_GUESS_AHEAD 32u        /* stacks at batch 1 (opt-in): a kernel
+                                           that loads each layer's weights during
+                                           the previous layer, for the experts
+                                           that layer's router picks on the
+                                           previous layer's input.  The result
+                                           is that of the default path within
+                                           the stated tolerance.  Measured slower
+                                           on MI355X than the default one-launch
+                                           kernel (the weight stream slows the
+                                           exchange reads of the same CUs)      */
+/* Test hooks of the guess-ahead kernel, for tests of its reload path: the
+ * guess of the next layer's experts is replaced by the k experts with the
+ * lowest guess logits (nearly every unit's weights are loaded after the
+ * selection), by the guess ranks k/2 .. k/2 + k - 1 (about half are), or by
+ * no guess at all (every unit's weights are loaded after the selection).
+ * The bits of the result do not depend on the guess. */
+#define MOE_FLAG_TEST_GUESS_LOWEST 64u
+#define MOE_FLAG_TEST_GUESS_SHIFTED 128u
+#define MOE_FLAG_TEST_GUESS_NONE 256u
+
 typedef struct moe_config {
   int32_t hidden;          /* H, multiple of 256                                  */
   int32_t n_experts;       /* E routed experts per layer, 1..1024                 */
@@ -281,10 +301,18 @@ moe_status moe_expert_forward_noalloc(moe_ctx* ctx, int32_t layer, const void* x
  * (dev int32 [L,T,k]) and w_trace (dev FP32 [L,T,k]) receive each layer's
  * x, ids and w when non-NULL (indexed by absolute layer).  With a slot pool
  * forced_ids is required and each layer's group must have been ensured.
- * Small batches (T <= 8, T*k <= 64, T*E <= 4096, H = 2048, I in {512, 1024},
+ * Small batches (T <= 4, T*k <= 64, T*E <= 4096, H = 2048, I in {512, 1024},
  * shared_inter in {0, I}) run as one persistent kernel per call; others run
  * the per-layer kernels.  Both give results within the stated tolerance and
- * each is deterministic. */
+ * each is deterministic.  With MOE_FLAG_GUESS_AHEAD, at T = 1 over resident
+ * layers without forced_ids (and k + shared <= 12, 64 | E, E <= 512), another
+ * persistent kernel loads each layer's weights during the previous layer,
+ * for the experts that layer's router picks on the previous layer's input
+ * ("An expert-offloading engine, from scratch", "Terms used here", "What the
+ * numbers say": the next layer's experts guessed from the current state); the
+ * guess changes only when weights move, never the result.  That kernel and
+ * the default one may differ in the last bits of a layer's output (FP32
+ * rounding of the same sums). */
 moe_status moe_stack_forward(moe_ctx* ctx, int32_t layer_begin, int32_t layer_end, float* h,
                              int32_t T, const int32_t* forced_ids, void* x_trace,
                              int32_t* ids_trace, float* w_trace, void* stream);

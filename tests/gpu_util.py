@@ -8,6 +8,7 @@ import numpy as np
 import torch
 
 from fixtures import moe_inputs as fx
+from oracle import moe_oracle as ora
 
 # Output tolerance of the layer (FP16 outputs vs the float64 oracle).
 REL_L2_TOL = 2e-3
@@ -45,3 +46,18 @@ def gpu_layer(shape, cfg, layer):
 def to_gpu(a, dtype=None):
     t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
     return t if dtype is None else t.to(dtype)
+
+
+def flip_is_explained(x_gpu, x_ora, router, ids_gpu, ids_ora):
+    """True when every expert that differs between the two selections is
+    within the logit change that the difference of the two inputs can cause:
+    for a chosen by the oracle only and b by the GPU only,
+    logit_ora(a) - logit_ora(b) <= B_a + B_b with B_e = sum_i |dx_i| |Wr_ei|
+    (logits on the oracle's input, exact)."""
+    dx = np.abs(x_gpu.astype(np.float64) - x_ora.astype(np.float64))
+    B = np.abs(router.astype(np.float64)) @ dx
+    lg = ora.router_logits(x_ora[None, :], router)[0].astype(np.float64)
+    only_o = sorted(set(ids_ora.tolist()) - set(ids_gpu.tolist()))
+    only_g = sorted(set(ids_gpu.tolist()) - set(ids_ora.tolist()))
+    worst = max((lg[a] - lg[b]) - (B[a] + B[b]) for a in only_o for b in only_g) if only_o else -1.0
+    return worst <= 0.0, worst

@@ -12,7 +12,7 @@ import torch
 from fixtures import moe_inputs as fx
 from oracle import moe_oracle as ora
 
-from gpu_util import assert_close, rel_l2, say
+from gpu_util import assert_close, flip_is_explained, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -159,21 +159,6 @@ def test_olmoe_stack_graph_replay_equals_direct_launch(moe):
     ctx.close()
 
 
-def _flip_is_explained(x_gpu, x_ora, router, ids_gpu, ids_ora):
-    """True when every expert that differs between the two selections is
-    within the logit change that the difference of the two inputs can cause:
-    for a chosen by the oracle only and b by the GPU only,
-    logit_ora(a) - logit_ora(b) <= B_a + B_b with B_e = sum_i |dx_i| |Wr_ei|
-    (logits on the oracle's input, exact)."""
-    dx = np.abs(x_gpu.astype(np.float64) - x_ora.astype(np.float64))
-    B = np.abs(router.astype(np.float64)) @ dx
-    lg = ora.router_logits(x_ora[None, :], router)[0].astype(np.float64)
-    only_o = sorted(set(ids_ora.tolist()) - set(ids_gpu.tolist()))
-    only_g = sorted(set(ids_gpu.tolist()) - set(ids_ora.tolist()))
-    worst = max((lg[a] - lg[b]) - (B[a] + B[b]) for a in only_o for b in only_g) if only_o else -1.0
-    return worst <= 0.0, worst
-
-
 @pytest.mark.parametrize("T", [1, 3])
 def test_olmoe_stack_free_running_vs_oracle(moe, T):
     """Whole stacks, free-running, against the oracle's free-running stack.
@@ -200,7 +185,7 @@ def test_olmoe_stack_free_running_vs_oracle(moe, T):
             np.testing.assert_array_equal(ids_l, own, err_msg=f"layer {l}: ids != oracle routing of the GPU's x")
             for t in range(T):
                 if not np.array_equal(np.sort(ids_l[t]), np.sort(ref["ids"][l][t])):
-                    ok, worst = _flip_is_explained(x_l[t], ref["x"][l][t], layers[l]["router"],
+                    ok, worst = flip_is_explained(x_l[t], ref["x"][l][t], layers[l]["router"],
                                                    ids_l[t], ref["ids"][l][t])
                     say(f"  fused={fused}: layer {l} token {t} routing differs; margin {worst:.3e}")
                     assert ok, (l, t, worst)

@@ -14,7 +14,7 @@ import torch
 
 from . import capi
 from .capi import (MOE_FLAG_FORCE_GEMV, MOE_FLAG_FORCE_MFMA,  # noqa: F401
-                   MOE_FLAG_NO_FUSED, MOE_FLAG_ROUTER_EXACT_ALWAYS, MOE_POLICY_LFU, MOE_POLICY_LRU,
+                   MOE_FLAG_NO_FUSED, MOE_FLAG_GUESS_AHEAD, MOE_FLAG_ROUTER_EXACT_ALWAYS, MOE_POLICY_LFU, MOE_POLICY_LRU,
                    MOE_POLICY_LRU_FREQ, MOE_RESIDENT_ALL, MoEError)
 
 _lib = capi.load()

@@ -24,6 +24,10 @@ MOE_FLAG_FORCE_GEMV = 2
 MOE_FLAG_FORCE_MFMA = 4
 MOE_FLAG_NO_FUSED = 8
 MOE_FLAG_STAGED_TRANSPORT = 16
+MOE_FLAG_GUESS_AHEAD = 32
+MOE_FLAG_TEST_GUESS_LOWEST = 64
+MOE_FLAG_TEST_GUESS_SHIFTED = 128
+MOE_FLAG_TEST_GUESS_NONE = 256
 
 
 class moe_config(C.Structure):

@@ -977,9 +977,29 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t layer_begin, int32_t layer_end,
     fa.w_trace = w_trace;
     fa.err = c->err;
     fa.stamps = c->stamps;
+    // one token over resident layers, routed by the router: the next layer's
+    // guessed experts are loaded during the current layer
+    const bool spec = (g.flags & MOE_FLAG_GUESS_AHEAD) && T == 1 && !forced_ids && !pooled(c) &&
+                      spec_supported(g.hidden, g.inter, g.n_experts, g.top_k, g.shared_inter);
+    if (spec) {
+      fa.guess_mode = (g.flags & MOE_FLAG_TEST_GUESS_NONE)      ? 3
+                      : (g.flags & MOE_FLAG_TEST_GUESS_LOWEST)  ? 1
+                      : (g.flags & MOE_FLAG_TEST_GUESS_SHIFTED) ? 2
+                                                                : 0;
+      // one logit item (an exact logit, or a guess logit of the next layer)
+      // per polling wave, 4 per block: one replica per XCD while each XCD
+      // has a wave per item
+      constexpr int kPollWaves = 4;
+      const int items = fa.guess_mode == 3 ? g.n_experts : 2 * g.n_experts;
+      fa.lg_reps = items <= (kFGrid / kFLogitReps) * kPollWaves ? kFLogitReps : 1;
+      fa.lg_sub = 1;
+    }
     {
       ScopedTimer tm(c, kKindFused, s);
-      launch_fused_decode(fa, s);
+      if (spec)
+        launch_spec_decode(fa, s);
+      else
+        launch_fused_decode(fa, s);
     }
     HIPCHK(c, hipGetLastError());
     if (pooled(c))

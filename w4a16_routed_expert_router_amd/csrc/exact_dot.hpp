@@ -92,6 +92,40 @@ __device__ inline float exact_dot_wave(const uint16_t* a, const uint16_t* b, int
 
 
 
+// exact_dot_wave with one chunk of each row in flight and no unrolling: the
+// same exact sum (so the same result) for a caller with little register room,
+// where the exact tier is a rare fallback.
+__device__ inline float exact_dot_wave_lean(const uint16_t* a, const uint16_t* b, int H, int lane) {
+  __int128 acc = 0;
+#pragma unroll 1
+  for (int k0 = lane * 8; k0 < H; k0 += kWave * 8) {
+    const uint4 av = *reinterpret_cast<const uint4*>(a + k0);
+    const uint4 bv = ldg_u4(b + k0);
+    const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
+    const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll 1
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t ah = (uint16_t)(aw[i >> 1] >> (16 * (i & 1)));
+      const uint16_t bh = (uint16_t)(bw[i >> 1] >> (16 * (i & 1)));
+      int32_t ma, sa, mb, sb;
+      f16_fixed(ah, ma, sa);
+      f16_fixed(bh, mb, sb);
+      acc += ((__int128)(ma * mb)) << (sa + sb);
+    }
+  }
+  uint64_t lo = (uint64_t)acc;
+  int64_t hi = (int64_t)(acc >> 64);
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const uint64_t lo2 = __shfl_xor(lo, o, kWave);
+    const int64_t hi2 = __shfl_xor(hi, o, kWave);
+    const uint64_t nlo = lo + lo2;
+    hi = hi + hi2 + (nlo < lo ? 1 : 0);
+    lo = nlo;
+  }
+  const __int128 S = (((__int128)hi) << 64) | (__int128)lo;
+  return round_i128_to_f32(S, -48);
+}
+
 // Compensated tier between the FP64 sum and the exact one.  Each product is
 // exact in FP64; they are added with TwoSum (Knuth), which returns the rounded
 // sum and its exact rounding error, the errors being summed separately, first

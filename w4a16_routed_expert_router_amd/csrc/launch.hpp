@@ -152,9 +152,17 @@ struct FusedArgs {
   float* w_trace;
   uint32_t* err;
   uint64_t* stamps;           // [grid][kStampStride] phase timestamps or null
+  int guess_mode;             // batch-1 path: 0 the router's guess; test hooks 1 the
+                              // k lowest guess logits, 2 guess ranks k/2 .. k/2+k-1;
+                              // 3 no guess (weights loaded after each selection)
 };
 bool fused_supported(int H, int I);
 void launch_fused_decode(const FusedArgs& a, hipStream_t stream);
+// Batch-1 fused decode with the next layer's weights loaded during the
+// current layer (decode_spec.hip); resident layers, no forced ids.  Uses
+// xlg[rep * kFMaxTE + E ..] for the guess logits.
+bool spec_supported(int H, int I, int E, int k, int shared_inter);
+void launch_spec_decode(const FusedArgs& a, hipStream_t stream);
 // words of each exchange buffer
 constexpr int64_t kFXhWords = 2ll * kFMaxT * 2048;
 constexpr int64_t kFXlgWords = (int64_t)kFLogitReps * kFMaxTE;
