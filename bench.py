@@ -49,6 +49,22 @@ def counted_traffic():
     return COUNTED_TRAFFIC["bytes"]
 
 
+# the other configurations and measurements, in the order they run
+EXTRAS = {
+    "olmoe_layer_t4": "extra_single_layer",
+    "olmoe_layer_batched": "extra_batched",
+    "qwen_next_like_stack": "extra_qwen",
+    "partial_residency_olmoe16": "extra_pool",
+    "prefetch_natural_routing_olmoe16": "extra_prefetch",
+    "policy_sweep_zipf": "extra_trace_analysis",
+}
+
+
+def run_extra(name, moe, fx, dev, stream):
+    fn = globals()[EXTRAS[name]]
+    return fn(moe, fx) if name == "policy_sweep_zipf" else fn(moe, fx, dev, stream)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -63,6 +79,8 @@ def parse():
     p.add_argument("--extras", type=int, default=1,
                    help="1: also measure the batched (prefill / batch-64), Qwen-like and "
                         "partial-residency workloads, reported under \"extra\"")
+    p.add_argument("--only", choices=sorted(EXTRAS), default=None,
+                   help="run only this measurement (no headline line): prints its JSON and exits")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="run one device-to-device copy of this many MiB first (a reference "
                         "kernel of known traffic for hardware byte counters)")
@@ -136,6 +154,22 @@ MFMA_FP16_PEAK_TFLOPS = 2500.0
 N_REPLICAS = 4   # weight replicas rotated through so that 207.6 MB layers do not sit in the 256 MB MALL
 
 
+def _rep_times_ms(fn, n, stream):
+    """Per-call times (ms) of n calls, each between its own pair of events on
+    `stream`; returns (median, p10, p90)."""
+    import numpy as np
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for i in range(n):
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+    ev[-1][1].synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+
 def _event_time_ms(fn, n, stream):
     import torch
     a = torch.cuda.Event(enable_timing=True)
@@ -147,6 +181,54 @@ def _event_time_ms(fn, n, stream):
         b.record(stream)
     b.synchronize()
     return a.elapsed_time(b) / n
+
+
+def extra_single_layer(moe, fx, dev, stream, reps=100):
+    """One OLMoE-shaped layer at 4 tokens, all 64 experts resident; weights rotate
+    over 4 replicas (830 MB > MALL).  Two entry points: the layer calls
+    (moe_route + moe_expert_forward: FP16 x in, FP16 out) and a one-layer
+    moe_stack_forward (the one-launch kernel: RMSNorm, the layer and the FP32
+    residual update).  Per-call median and p10/p90 of `reps` calls each."""
+    import numpy as np
+    import torch
+    shape, T = fx.OLMOE, 4
+    ctx = moe.MoEContext(shape, n_layers=N_REPLICAS, max_tokens=T)
+    for r in range(N_REPLICAS):
+        w = fx.layer_weights(shape, "bench-layer-t4", r, device="cuda", batched=True)
+        ctx.register_layer(r, {k: v.cpu().numpy() for k, v in w.items()})
+        del w
+    x = fx.activations(("bench-layer-t4-x",), T, shape.hidden, device="cuda")
+    out = torch.empty_like(x)
+    h0 = x.float()
+    h = torch.empty_like(h0)
+    ids_all = [ctx.route(r, x, stream=stream)[0] for r in range(N_REPLICAS)]
+    stream.synchronize()
+    used = float(np.mean([len(np.unique(i.cpu().numpy())) for i in ids_all]))
+    nbytes = used * shape.blob_bytes + shape.n_experts * shape.hidden * 2 + 2 * T * shape.hidden * 2
+    flops = 2.0 * T * shape.top_k * 3 * shape.hidden * shape.inter + 2.0 * T * shape.n_experts * shape.hidden
+
+    def layer_api(i):
+        r = i % N_REPLICAS
+        ids, w = ctx.route(r, x, stream=stream)
+        ctx.expert_forward(r, x, ids, w, out=out, stream=stream)
+
+    def fused(i):
+        r = i % N_REPLICAS
+        h.copy_(h0)
+        ctx.stack_forward(h, layer_begin=r, layer_end=r + 1, stream=stream)
+
+    res = {"tokens": T, "experts_touched_mean": used, "bytes_per_call": int(nbytes), "flops_per_call": flops}
+    for name, fn in (("layer_calls", layer_api), ("one_launch", fused)):
+        for i in range(10):
+            fn(i)
+        med, p10, p90 = _rep_times_ms(fn, reps, stream)
+        res[name] = {"us_median": round(med * 1e3, 2), "us_p10": round(p10 * 1e3, 2),
+                     "us_p90": round(p90 * 1e3, 2), "tokens_per_s": round(T / (med * 1e-3), 1),
+                     "hbm_gbps": round(nbytes / (med * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    assert ctx.check_device_errors(stream) == 0
+    ctx.close()
+    return res
 
 
 def extra_batched(moe, fx, dev, stream):
@@ -203,21 +285,36 @@ def extra_batched(moe, fx, dev, stream):
     return res
 
 
-def extra_qwen(moe, fx, dev, stream, n_layers=8, full_layers=48):
-    """Qwen3-Next-like layers (512 experts, top-10 renormalised, shared expert, I=512),
-    decode at batch 1 and 16: `n_layers` distinct layers are timed; the 48-layer
-    rate is the measured per-layer time times 48 (every layer has the same shape)."""
+def extra_qwen(moe, fx, dev, stream, n_sets=8, n_layers=48, reps=50):
+    """Qwen3-Next-like stack at its full 48 layers (512 experts, top-10
+    renormalised, shared expert, I=512), decode at batch 1 and 16.  Layer l holds
+    seeded weight set l % n_sets, each layer in storage of its own (39.9 GB of
+    expert blobs stream every step).  Per-step median and p10/p90 of `reps`
+    steps; bytes from the distinct experts each layer actually routes to."""
+    import numpy as np
     import torch
     shape = fx.QWEN_NEXT
     res = {}
     ctx = moe.MoEContext(shape, n_layers=n_layers, max_tokens=16)
-    for l in range(n_layers):
-        w = fx.layer_weights(shape, "bench-qwen", l, device="cuda", batched=True)
-        ctx.register_layer(l, {k: v.cpu().numpy() for k, v in w.items()})
+    sets = []
+    for j in range(n_sets):
+        w = fx.layer_weights(shape, "bench-qwen", j, device="cuda", batched=True)
+        sets.append({k: v.cpu().numpy() for k, v in w.items()})
         del w
+    for l in range(n_layers):
+        ctx.register_layer(l, sets[l % n_sets])
+    del sets
+    blob_shared = shape.blob_bytes  # the shared expert has the routed shape
+    router_b = shape.n_experts * shape.hidden * 2
     for T in (1, 16):
         h0 = fx.activations(("bench-qwen-h0", T), T, shape.hidden, device="cuda").float()
         h = torch.empty_like(h0)
+        h.copy_(h0)
+        _, ids, _ = ctx.stack_forward(h, trace=True, stream=stream)
+        stream.synchronize()
+        ids = ids.cpu().numpy()
+        distinct = [len(np.unique(ids[l])) for l in range(n_layers)]
+        nbytes = sum(u * shape.blob_bytes + blob_shared + router_b + 2 * T * shape.hidden * 4 for u in distinct)
 
         def step(i):
             h.copy_(h0)
@@ -225,20 +322,34 @@ def extra_qwen(moe, fx, dev, stream, n_layers=8, full_layers=48):
 
         for i in range(5):
             step(i)
-        ms = _event_time_ms(step, 30, stream)
-        per_layer_us = ms * 1e3 / n_layers
-        tok_s = T / (per_layer_us * full_layers * 1e-6)
-        entry = {"tokens": T, "layers_timed": n_layers, "per_layer_us": round(per_layer_us, 2),
-                 "tokens_per_s_48_layers": round(tok_s, 1),
-                 "path": "fused" if T <= 4 else "per-layer kernels"}
-        if T == 1:
-            bpt = full_layers * ((shape.top_k + 1) * shape.blob_bytes + shape.n_experts * shape.hidden * 2)
-            entry["bytes_per_token_48_layers"] = bpt
-            entry["hbm_frac"] = round(bpt * tok_s / 1e9 / HBM_PEAK_GBPS, 4)
-        res[f"batch_{T}"] = entry
+        med, p10, p90 = _rep_times_ms(step, reps, stream)
+        res[f"batch_{T}"] = {
+            "tokens": T, "layers": n_layers, "step_us_median": round(med * 1e3, 1),
+            "step_us_p10": round(p10 * 1e3, 1), "step_us_p90": round(p90 * 1e3, 1),
+            "per_layer_us": round(med * 1e3 / n_layers, 2),
+            "tokens_per_s": round(T / (med * 1e-3), 1),
+            "distinct_experts_per_layer_mean": round(float(np.mean(distinct)), 2),
+            "bytes_per_step": int(nbytes),
+            "hbm_gbps": round(nbytes / (med * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "path": "fused" if T <= 4 else "per-layer kernels"}
     assert ctx.check_device_errors(stream) == 0
     ctx.close()
     return res
+
+
+def pinned_h2d_peak(stream, nbytes, n=64):
+    """Host -> device rate of n copies of `nbytes` from pinned memory on `stream`
+    (the copy size of one OLMoE expert blob)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    src.fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    with torch.cuda.stream(stream):
+        for _ in range(4):
+            dst.copy_(src, non_blocking=True)
+    ms = _event_time_ms(lambda i: dst.copy_(src, non_blocking=True), n, stream)
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def extra_pool(moe, fx, dev, stream, steps=256, layers=16):
@@ -280,7 +391,9 @@ def extra_pool(moe, fx, dev, stream, steps=256, layers=16):
         return outs, dt, stats
 
     ref, dt_ref, _ = run("resident", 0)
-    res = {"steps": steps, "layers": layers, "resident_tokens_per_s": round(steps / dt_ref, 1)}
+    peak = pinned_h2d_peak(stream, shape.blob_bytes)
+    res = {"steps": steps, "layers": layers, "resident_tokens_per_s": round(steps / dt_ref, 1),
+           "pinned_h2d_peak_gbps": round(peak, 2)}
     staged = dict(flags=moe.capi.MOE_FLAG_STAGED_TRANSPORT, staging_blobs=4, spare_rows=8)
     for policy, C, kw in (("lru", 16, {}), ("lfu", 16, {}), ("lru", 32, {}), ("lfu", 32, {}), ("lru", 48, {}),
                           ("lfu", 48, {}), ("lfu", 32, staged), ("lfu", 32, dict(spare_rows=8))):
@@ -293,6 +406,7 @@ def extra_pool(moe, fx, dev, stream, steps=256, layers=16):
             "hit_rate": round(hits / max(acc, 1), 4),
             "h2d_gb": round(h2d / 1e9, 3),
             "h2d_gbps_copy": round(h2d / max(h2d_s, 1e-12) / 1e9, 2),
+            "h2d_copy_frac_of_pinned_peak": round(h2d / max(h2d_s, 1e-12) / 1e9 / peak, 3),
             "h2d_gbps_wall": round(h2d / dt / 1e9, 2),
             "tokens_per_s": round(steps / dt, 1),
             "bit_identical_to_resident": bool(torch.equal(out, ref)),
@@ -442,6 +556,10 @@ def main():
         print(f"[bench] calibration copy: {args.copy_calibration_mib} MiB read + "
               f"{args.copy_calibration_mib} MiB written", file=sys.stderr, flush=True)
         del src, dst
+    if args.only:
+        res = run_extra(args.only, moe, fx, dev, stream)
+        print(json.dumps({"workload": args.only, "result": res}))
+        return
     t_gen = time.perf_counter()
     ctx = moe.MoEContext(shape, n_layers=L, max_tokens=T,
                          flags=0 if args.fused else moe.MOE_FLAG_NO_FUSED)
@@ -566,16 +684,9 @@ def main():
         stream.synchronize()
         extra = {}
         t_x = time.perf_counter()
-        extra["olmoe_layer_batched"] = extra_batched(moe, fx, dev, stream)
-        print(f"[bench] batched extras done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
-        extra["qwen_next_like_stack"] = extra_qwen(moe, fx, dev, stream)
-        print(f"[bench] qwen extras done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
-        extra["partial_residency_olmoe16"] = extra_pool(moe, fx, dev, stream)
-        print(f"[bench] pool extras done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
-        extra["prefetch_natural_routing_olmoe16"] = extra_prefetch(moe, fx, dev, stream)
-        print(f"[bench] prefetch extras done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
-        extra["policy_sweep_zipf"] = extra_trace_analysis(moe, fx)
-        print(f"[bench] policy sweep done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
+        for name in EXTRAS:
+            extra[name] = run_extra(name, moe, fx, dev, stream)
+            print(f"[bench] {name} done ({time.perf_counter() - t_x:.1f} s)", file=sys.stderr, flush=True)
         out["extra"] = extra
     # the oracle: the CPU baseline (timed) and the reference of the check;
     # with --no-cpu-baseline only the checked inputs are computed, untimed
