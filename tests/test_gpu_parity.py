@@ -284,12 +284,13 @@ def test_layer_crowded_experts_mfma(moe, olmoe_layer, shape_name):
 
 
 def test_layer_crowded_experts_stream(moe, olmoe_layer):
-    """Batched decode with skewed routing: experts with 40 (grouped GEMM), 32,
-    31 and 17 tokens (two 16-token sub-tiles in the streaming kernel) and 16,
-    15, 2 and 1 (one sub-tile) next to evenly spread ones."""
+    """Batched decode with skewed routing, all of it in the streaming kernel:
+    experts with 64, 40 and 33 tokens (list entries of at most 32 tokens each:
+    two, two and two), 32, 31 and 17 tokens (two 16-token sub-tiles) and 2 and
+    1 (one sub-tile) next to evenly spread ones."""
     say("test_layer_crowded_experts_stream")
     shape, T = fx.OLMOE, 64
-    heads = [40, 32, 31, 17, 16, 15, 2, 1]
+    heads = [64, 40, 33, 32, 31, 17, 2, 1]
     forced = _skewed_ids(T, shape.n_experts, shape.top_k, heads, 11)
     ctx = moe.MoEContext(shape, n_layers=1, max_tokens=T)
     ctx.register_layer(0, olmoe_layer)

@@ -463,9 +463,16 @@ void run_router(moe_ctx* c, const RouterArgs& ra, hipStream_t s) {
 // Device scratch of the expert path of one call: the grouping's outputs, the
 // FP16 intermediates and the FP32 expert outputs.  Every word the kernels read
 // is written earlier in the same call, so nothing has to start at zero.
+// Entries of the active-expert lists of a T-token call: the active list (E),
+// then the few-token kernel's list (E, or with chunks of kStreamTokens tokens
+// E + ceil(T*k / kStreamTokens)).
+size_t active_list_entries(const moe_config& g, int T) {
+  return (size_t)2 * g.n_experts + ((size_t)T * g.top_k + kStreamTokens - 1) / kStreamTokens;
+}
+
 struct ExpertScratch {
   int32_t* ids_s;          // [P]
-  ActiveExpert* active;    // [2E]: active list, then the few-token kernel's list
+  ActiveExpert* active;    // [active_list_entries]: active list, then the few-token kernel's list
   int32_t* n_active;       // [2]
   int32_t* perm_tok;       // [P]
   int32_t* pos_of;         // [P]
@@ -494,7 +501,7 @@ size_t carve_scratch(const moe_config& g, int T, uint8_t* base, ExpertScratch* o
   };
   ExpertScratch x{};
   x.ids_s = (int32_t*)take(P * 4);
-  x.active = (ActiveExpert*)take((size_t)2 * g.n_experts * sizeof(ActiveExpert));
+  x.active = (ActiveExpert*)take(active_list_entries(g, T) * sizeof(ActiveExpert));
   x.n_active = (int32_t*)take(2 * 4);
   x.perm_tok = (int32_t*)take(P * 4);
   x.pos_of = (int32_t*)take(P * 4);
@@ -531,12 +538,18 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
                                         (int64_t)T * g.top_k >= (int64_t)kPrefillPairsPerExpert * g.n_experts);
   const bool stream_gu = !force_gemv && stream_supported(0, g.hidden, g.inter);
   const bool stream_dn = !force_gemv && stream_supported(1, g.inter, g.hidden);
+  // below the prefill threshold with both streaming kernels available, they
+  // take every expert (one with more than kStreamTokens tokens as several
+  // list entries, each streaming the weights again): no grouped-GEMM launch,
+  // which costs several microseconds even when it finds no tile
+  const bool chunk_all = !force_gemv && !all_mfma && stream_gu && stream_dn;
   const int mfma_min = force_gemv ? INT32_MAX
                        : all_mfma ? 1
+                       : chunk_all ? INT32_MAX
                        : (stream_gu ? kStreamTokens + 1 : kMfmaMinTokens);
   GroupArgs ga{ids, T, g.top_k, g.n_experts, L.map, sc.ids_s, sc.active, sc.n_active,
                sc.perm_tok, sc.pos_of, c->err, mfma_min, sc.mtile_off,
-               sc.active + g.n_experts, sc.n_active + 1};
+               sc.active + g.n_experts, sc.n_active + 1, chunk_all ? 1 : 0};
   {
     ScopedTimer tm(c, timed, kKindGroup, s);
     launch_group(ga, s);
@@ -715,7 +728,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   ok = ok && dalloc((void**)&c->w, (size_t)P * 4);
   ok = ok && dalloc((void**)&c->ids_s, (size_t)P * 4);
   // active list, then the list of the experts the few-token kernel takes
-  ok = ok && dalloc((void**)&c->active, (size_t)2 * g.n_experts * sizeof(ActiveExpert));
+  ok = ok && dalloc((void**)&c->active, active_list_entries(g, g.max_tokens) * sizeof(ActiveExpert));
   ok = ok && dalloc((void**)&c->n_active, 2 * 4);
   ok = ok && dalloc((void**)&c->perm_tok, (size_t)P * 4);
   ok = ok && dalloc((void**)&c->pos_of, (size_t)P * 4);

@@ -117,8 +117,12 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
   // offsets and the active list (ascending expert id); E <= 1024 = one per thread
   const int c = (tid < E) ? cnt[tid] : 0;
   const int mtiles = c >= a.mfma_min ? (c + kMfmaTileTokens - 1) / kMfmaTileTokens : 0;
-  const bool small = c > 0 && c <= kStreamTokens && c < a.mfma_min;
-  const int sv[4] = {c, mtiles, c > 0 ? 1 : 0, small ? 1 : 0};
+  // entries of the few-token kernel's list: one for an expert with at most
+  // kStreamTokens tokens below the MFMA threshold, or (chunk_all) one per
+  // chunk of kStreamTokens tokens of every active expert
+  const int nchunk = a.chunk_all ? (c + kStreamTokens - 1) / kStreamTokens
+                                 : (c > 0 && c <= kStreamTokens && c < a.mfma_min ? 1 : 0);
+  const int sv[4] = {c, mtiles, c > 0 ? 1 : 0, nchunk};
   int sx[4], st[4];
   block_exclusive_scan<4>(sv, sx, st, sh_warp, sh_tot);
   const int off = sx[0], moff = sx[1], mtotal = st[1], act = sx[2], nact = st[2];
@@ -189,7 +193,8 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
     a.mtile_off[act] = moff;
     a.active[act] = ActiveExpert{tid, slot, c, off};
   }
-  if (small) a.small[sidx] = ActiveExpert{tid, slot, c, off};
+  for (int i = 0; i < nchunk; ++i)
+    a.small[sidx + i] = ActiveExpert{tid, slot, min(kStreamTokens, c - i * kStreamTokens), off + i * kStreamTokens};
   if (tid == 0) {
     a.mtile_off[nact] = mtotal;
     *a.n_active = nact;

@@ -39,8 +39,11 @@ struct GroupArgs {
   uint32_t* err;
   int mfma_min;             // experts with at least this many tokens take the MFMA path
   int32_t* mtile_off;       // [E+1] MFMA token-tile offsets over the active list
-  ActiveExpert* small;      // [E] active experts with at most kStreamTokens tokens (below mfma_min)
+  ActiveExpert* small;      // [E + ceil(T*k / kStreamTokens)] the few-token kernel's list: active
+                            // experts with at most kStreamTokens tokens (below mfma_min), or with
+                            // chunk_all every active expert as chunks of at most kStreamTokens
   int32_t* n_small;         // [1]
+  int chunk_all;            // 1: every active expert goes to the few-token list, in chunks
 };
 void launch_group(const GroupArgs& a, hipStream_t stream);
 
@@ -81,7 +84,7 @@ struct ExpertArgs {
   uint16_t* hbuf;             // [positions, I] fp16
   float* ybuf;                // [positions, H] fp32
   int mfma_min;               // routed experts with count >= this are skipped (MFMA path)
-  const ActiveExpert* small;  // routed experts with at most kStreamTokens tokens, below mfma_min
+  const ActiveExpert* small;  // routed experts (or chunks of them) with at most kStreamTokens tokens
   const int32_t* n_small;
   // streaming kernel, routed mode: the shared expert taken as one more list
   // entry after the small experts (null: none); its tokens are 0..T-1 and its
