@@ -464,6 +464,27 @@ moe_status moe_cache_event_log(const moe_ctx* ctx, int32_t layer, moe_cache_even
  * publication (the context is faulted, MOE_E_FAULTED).  mode 0 disarms. */
 moe_status moe_debug_inject_transfer_failure(moe_ctx* ctx, int32_t layer, int32_t mode);
 
+/* Test hook for the ordering of slot publication, for callers that test it
+ * (the pages record output corrupted by an event-ordering mistake in a slot
+ * cache: "F51 Nitro / Nitro-MoE", "When forced on, the cache was slower - and
+ * once corrupt"): from now on every host-to-device blob copy of the context
+ * is preceded on the side stream by a wait of `microseconds` (a bounded
+ * kernel: it ends by the clock or, failing that, by an iteration count), so
+ * a reader that does not wait for a copy's completion reads the old row.
+ * Results must not change.  0 turns it off; values above
+ * MOE_MAX_COPY_DELAY_US give MOE_E_ARG. */
+#define MOE_MAX_COPY_DELAY_US 100000
+moe_status moe_debug_delay_copies(moe_ctx* ctx, int32_t microseconds);
+
+/* Debug mode, chosen by the environment when a context is created:
+ * MOE_SYNC_EACH_CALL=1 makes every call that enqueues GPU work (moe_route,
+ * moe_expert_forward and its allocation-free variant, moe_stack_forward,
+ * moe_stack_forward_pooled, moe_cache_ensure, moe_cache_prefetch,
+ * moe_cache_pin, moe_rmsnorm) wait for its stream and the context's side
+ * stream before it returns and read the device error word: a non-zero word
+ * gives MOE_E_DEVICE from that call (the word is left set; moe_check_device_errors
+ * reads and clears it).  Not for use under stream capture. */
+
 /* ---- host-only policy engine (no device needed) --------------------------------
  * The decision procedure moe_cache_ensure uses, exposed on its own so it can be
  * exercised without a GPU.  Per call: the clock ticks; the group (processed in

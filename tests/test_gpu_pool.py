@@ -468,3 +468,93 @@ def test_pool_qwen_like_natural_routing_prefetch(moe):
         assert st["prefetch_used"] == sims[l].prefetch_used
     pool.close()
     res.close()
+
+
+# ---- publication ordering under delayed copies ----------------------------------
+# Every host-to-device blob copy waits on the side stream before it starts, so a
+# layer that read a slot without waiting for that slot's copy would read the row's
+# previous occupant ("F51 Nitro / Nitro-MoE", "When forced on, the cache was slower
+# - and once corrupt": a cache there corrupted outputs through an event-ordering
+# mistake).  The wait is a bounded kernel; results must not change.
+DELAY_US = 300
+DELAY_STEPS = 48
+
+
+@pytest.mark.parametrize("mode", ["in_place", "spare", "staged"])
+def test_pool_delayed_copies_bit_identical(moe, olmoe_layers, trace, h0s, resident_out, mode):
+    say(f"test_pool_delayed_copies mode={mode}")
+    kw = {"in_place": {}, "spare": SPARE, "staged": STAGED}[mode]
+    ctx = _ctx(moe, olmoe_layers, policy="lru", slots=16, **kw)
+    ctx.delay_copies(DELAY_US)
+    out = _run(ctx, trace, h0s, pooled=True, steps=DELAY_STEPS)
+    assert torch.equal(out, resident_out[:DELAY_STEPS]), f"delayed copies changed the output ({mode})"
+    for l in range(L):
+        sim = ora.CacheSim(ora.LRU, fx.OLMOE.n_experts, 16, layer=l)
+        for s in range(DELAY_STEPS):
+            sim.ensure(trace[s, l].tolist(), s)
+        assert ctx.cache_events(l) == [e.as_tuple() for e in sim.events], f"layer {l}"
+        st = ctx.cache_stats(l)
+        assert st["misses"] == sim.misses
+        # the waits really ran: the side stream's busy time covers one per copy
+        assert st["h2d_seconds"] >= 0.9 * sim.misses * DELAY_US * 1e-6, (l, st["h2d_seconds"], sim.misses)
+    ctx.close()
+
+
+def test_pool_delayed_copies_natural_routing_prefetch(moe, olmoe_layers, h0s):
+    # next-layer prefetch and demand misses both delayed, with in-place slots and
+    # spare rows: the same bits, ids and decisions as without the delay
+    say("test_pool_delayed_copies_natural")
+    for kw in ({}, SPARE):
+        res = []
+        for delay in (0, DELAY_US):
+            ctx = _ctx(moe, olmoe_layers, policy="lfu", slots=16, **kw)
+            ctx.delay_copies(delay)
+            out, ids, _ = _run_natural(ctx, h0s, True, steps=24)
+            res.append((out, ids, [ctx.cache_events(l) for l in range(L)]))
+            ctx.close()
+        assert torch.equal(res[0][0], res[1][0]), f"delayed copies changed the output {kw}"
+        assert np.array_equal(res[0][1], res[1][1])
+        assert res[0][2] == res[1][2]
+
+
+def test_debug_delay_copies_argument_range(moe, olmoe_layers):
+    from w4a16_routed_expert_router_amd import MoEError, capi
+    ctx = _ctx(moe, olmoe_layers[:L], policy="lru", slots=8)
+    for bad in (-1, capi.MOE_MAX_COPY_DELAY_US + 1):
+        with pytest.raises(MoEError):
+            ctx.delay_copies(bad)
+    ctx.delay_copies(capi.MOE_MAX_COPY_DELAY_US)
+    ctx.delay_copies(0)
+    ctx.close()
+
+
+def test_sync_each_call_reports_device_errors_at_the_call(moe, olmoe_layers, monkeypatch):
+    # MOE_SYNC_EACH_CALL=1 (read when the context is created): the call that set
+    # the device error word fails with MOE_E_DEVICE itself; without it the call
+    # returns and the error shows at moe_check_device_errors.  Results are the
+    # same either way.
+    from w4a16_routed_expert_router_amd import MoEError, capi
+    say("test_sync_each_call")
+    shape = fx.OLMOE
+    x = fx.activations(("sync-each",), 3, shape.hidden).cuda()
+    bad = torch.tensor([[0, 1, 2, 3, 4, 5, 6, 7], [5, 5, 6, 7, 8, 9, 10, 11], [1, 2, 3, -4, 5, 6, 7, 8]],
+                       dtype=torch.int32, device="cuda")
+    w = torch.full((3, shape.top_k), 0.125, dtype=torch.float32, device="cuda")
+    outs = {}
+    for mode in ("0", "1"):
+        monkeypatch.setenv("MOE_SYNC_EACH_CALL", mode)
+        ctx = moe.MoEContext(shape, n_layers=1, max_tokens=4)
+        ctx.register_layer(0, olmoe_layers[0])
+        ids, ww = ctx.route(0, x[:1])
+        outs[mode] = ctx.expert_forward(0, x[:1], ids, ww).clone()
+        if mode == "1":
+            with pytest.raises(MoEError) as ei:
+                ctx.expert_forward(0, x, bad, w)
+            assert ei.value.status == capi.MOE_E_DEVICE
+        else:
+            ctx.expert_forward(0, x, bad, w)
+        assert ctx.check_device_errors() & 3 == 3
+        assert ctx.check_device_errors() == 0
+        ctx.close()
+    monkeypatch.delenv("MOE_SYNC_EACH_CALL")
+    assert torch.equal(outs["0"], outs["1"])

@@ -265,6 +265,11 @@ class MoEContext:
     def inject_transfer_failure(self, layer, mode):
         self._check(_lib.moe_debug_inject_transfer_failure(self._h, layer, mode))
 
+    def delay_copies(self, microseconds):
+        """Test hook: a bounded wait of `microseconds` on the side stream before
+        every host-to-device blob copy (0 turns it off)."""
+        self._check(_lib.moe_debug_delay_copies(self._h, microseconds))
+
 
 class PolicyEngine:
     """Host-only slot-pool decision engine of the library (no GPU needed)."""

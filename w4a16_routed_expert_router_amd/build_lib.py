@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_w4a16.so")
 
 SOURCES = ["api.hip", "router.hip", "group.hip", "expert_gemv.hip", "expert_mfma.hip", "expert_stream.hip",
-           "decode_fused.hip", "decode_spec.hip", "policy.cpp", "trace_analysis.cpp"]
+           "decode_fused.hip", "decode_spec.hip", "debug.hip", "policy.cpp", "trace_analysis.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

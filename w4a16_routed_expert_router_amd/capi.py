@@ -28,6 +28,7 @@ MOE_FLAG_GUESS_AHEAD = 32
 MOE_FLAG_TEST_GUESS_LOWEST = 64
 MOE_FLAG_TEST_GUESS_SHIFTED = 128
 MOE_FLAG_TEST_GUESS_NONE = 256
+MOE_MAX_COPY_DELAY_US = 100000
 
 
 class moe_config(C.Structure):
@@ -79,6 +80,7 @@ SIGNATURES = {
     "moe_cache_stats": (_I, [_P, _I, C.POINTER(moe_cache_counters)]),
     "moe_cache_event_log": (_I, [_P, _I, C.POINTER(moe_cache_event), _I, C.POINTER(_I)]),
     "moe_debug_inject_transfer_failure": (_I, [_P, _I, _I]),
+    "moe_debug_delay_copies": (_I, [_P, _I]),
     "moe_timer_enable": (_I, [_P, _I]),
     "moe_timer_read": (_I, [_P, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
     "moe_fused_phase_stamps": (_I, [_P, _P, C.c_int64, C.POINTER(_I), C.POINTER(_I), C.POINTER(_I)]),

@@ -19,6 +19,7 @@
 #include <string.h>
 
 #include <condition_variable>
+#include <cstdlib>
 #include <memory>
 #include <mutex>
 #include <string>
@@ -186,6 +187,8 @@ struct moe_ctx {
   uint16_t* xbuf = nullptr;
   uint32_t* err = nullptr;
   hipStream_t side = nullptr;
+  int copy_delay_us = 0;       // test hook: wait before every host-to-device blob copy
+  bool sync_each = false;      // MOE_SYNC_EACH_CALL=1 at creation
   std::string last_error;
   bool faulted = false;
   // fused decode path
@@ -345,6 +348,11 @@ void restore_rows(LayerState& L, RowState&& r) {
 // A blob comes straight from the pinned backing, or (staged transport) from
 // the pageable source through the next pinned staging buffer, after a host
 // wait until that buffer's previous transfer has completed.
+// Test hook: occupies the side stream for the set time before a blob copy.
+void delay_copy(moe_ctx* c) {
+  if (c->copy_delay_us > 0) launch_copy_delay(c->side, c->copy_delay_us);
+}
+
 bool enqueue_fills(moe_ctx* c, LayerState& L, const std::vector<PolicyEngine::Decision>& fills, hipStream_t s,
                    hipEvent_t t0, hipEvent_t t1, hipEvent_t done) {
   const int64_t blob = c->lay.total();
@@ -354,6 +362,7 @@ bool enqueue_fills(moe_ctx* c, LayerState& L, const std::vector<PolicyEngine::De
     good = good && hipEventRecord(t0, c->side) == hipSuccess;
     for (const auto& d : fills) {
       if (!good) break;
+      delay_copy(c);
       good = hipMemcpyAsync(L.store + (int64_t)d.slot * blob, L.backing + (int64_t)d.expert * blob,
                             (size_t)blob, hipMemcpyHostToDevice, c->side) == hipSuccess;
     }
@@ -387,11 +396,13 @@ bool enqueue_fills(moe_ctx* c, LayerState& L, const std::vector<PolicyEngine::De
         if (c->stage_used[si]) good = hipEventSynchronize(c->stage_ev[si]) == hipSuccess;
         if (!good) break;
         c->copier->copy(c->stage[si], L.backing + (int64_t)d.expert * blob, (size_t)blob);
+        delay_copy(c);
         good = hipMemcpyAsync(L.store + (int64_t)fr.row * blob, c->stage[si], (size_t)blob,
                               hipMemcpyHostToDevice, c->side) == hipSuccess;
         good = good && hipEventRecord(c->stage_ev[si], c->side) == hipSuccess;
         c->stage_used[si] = 1;
       } else {
+        delay_copy(c);
         good = hipMemcpyAsync(L.store + (int64_t)fr.row * blob, L.backing + (int64_t)d.expert * blob,
                               (size_t)blob, hipMemcpyHostToDevice, c->side) == hipSuccess;
       }
@@ -669,6 +680,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   }
   std::unique_ptr<moe_ctx> c(new moe_ctx());
   c->cfg = g;
+  if (const char* v = std::getenv("MOE_SYNC_EACH_CALL")) c->sync_each = std::string(v) == "1";
   const int64_t cb = (int64_t)g.inter * g.hidden / 2, sc = (int64_t)g.inter * g.hidden / 128;
   c->lay = BlobLayout{cb, sc * 2};
   const int64_t scb = (int64_t)g.shared_inter * g.hidden / 2, ssc = (int64_t)g.shared_inter * g.hidden / 128;
@@ -897,7 +909,7 @@ moe_status moe_register_layer(moe_ctx* c, int32_t layer, const uint16_t* router,
   return MOE_OK;
 }
 
-moe_status moe_route(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* forced_ids,
+static moe_status moe_route_call(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* forced_ids,
                      int32_t* ids, float* w, float* logits, void* stream) {
   if (moe_status st = check_ctx(c)) return st;
   if (moe_status st = check_layer(c, layer)) return st;
@@ -912,7 +924,7 @@ moe_status moe_route(moe_ctx* c, int32_t layer, const void* x, int32_t T, const 
   return MOE_OK;
 }
 
-moe_status moe_expert_forward(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* ids,
+static moe_status moe_expert_forward_call(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* ids,
                               const float* w, void* out, void* stream) {
   if (moe_status st = check_ctx(c)) return st;
   if (moe_status st = check_layer(c, layer)) return st;
@@ -923,7 +935,7 @@ moe_status moe_expert_forward(moe_ctx* c, int32_t layer, const void* x, int32_t 
                      (hipStream_t)stream, ctx_scratch(c));
 }
 
-moe_status moe_expert_forward_noalloc(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* ids,
+static moe_status moe_expert_forward_noalloc_call(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* ids,
                                       const float* w, void* out, void* stream) {
   if (moe_status st = check_ctx(c)) return st;
   if (moe_status st = check_layer(c, layer)) return st;
@@ -942,7 +954,7 @@ moe_status moe_expert_forward_noalloc(moe_ctx* c, int32_t layer, const void* x, 
                      false);
 }
 
-moe_status moe_stack_forward(moe_ctx* c, int32_t layer_begin, int32_t layer_end, float* h, int32_t T,
+static moe_status moe_stack_forward_call(moe_ctx* c, int32_t layer_begin, int32_t layer_end, float* h, int32_t T,
                              const int32_t* forced_ids, void* x_trace, int32_t* ids_trace,
                              float* w_trace, void* stream) {
   if (moe_status st = check_ctx(c)) return st;
@@ -1048,7 +1060,7 @@ moe_status moe_check_device_errors(moe_ctx* c, void* stream, uint32_t* bits) {
   return MOE_OK;
 }
 
-moe_status moe_cache_ensure(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n,
+static moe_status moe_cache_ensure_call(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n,
                             int32_t* slots, int32_t step, void* stream) {
   if (moe_status st = check_ctx(c)) return st;
   if (moe_status st = check_layer(c, layer)) return st;
@@ -1143,7 +1155,7 @@ moe_status moe_cache_ensure(moe_ctx* c, int32_t layer, const int32_t* experts, i
   return MOE_OK;
 }
 
-moe_status moe_cache_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int32_t step,
+static moe_status moe_cache_prefetch_call(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int32_t step,
                               void* stream) {
   if (moe_status st = check_ctx(c)) return st;
   if (moe_status st = check_layer(c, layer)) return st;
@@ -1206,7 +1218,7 @@ moe_status moe_cache_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts,
   return MOE_OK;
 }
 
-moe_status moe_cache_pin(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int32_t step,
+static moe_status moe_cache_pin_call(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int32_t step,
                          void* stream) {
   if (moe_status st = check_ctx(c)) return st;
   if (moe_status st = check_layer(c, layer)) return st;
@@ -1261,7 +1273,7 @@ moe_status moe_cache_pin(moe_ctx* c, int32_t layer, const int32_t* experts, int3
   return MOE_OK;
 }
 
-moe_status moe_stack_forward_pooled(moe_ctx* c, int32_t layer_begin, int32_t layer_end, float* h, int32_t T,
+static moe_status moe_stack_forward_pooled_call(moe_ctx* c, int32_t layer_begin, int32_t layer_end, float* h, int32_t T,
                                     int32_t prefetch, int32_t step, int32_t* ids_trace, int32_t* guess_trace,
                                     void* stream) {
   if (moe_status st = check_ctx(c)) return st;
@@ -1358,7 +1370,7 @@ moe_status moe_stack_forward_pooled(moe_ctx* c, int32_t layer_begin, int32_t lay
   return MOE_OK;
 }
 
-moe_status moe_rmsnorm(moe_ctx* c, const float* h, int32_t T, void* x, void* stream) {
+static moe_status moe_rmsnorm_call(moe_ctx* c, const float* h, int32_t T, void* x, void* stream) {
   if (moe_status st = check_ctx(c)) return st;
   if (!h || !x || T < 1 || T > c->cfg.max_tokens) return fail(c, MOE_E_ARG, "bad h/x/T");
   launch_rmsnorm(h, T, c->cfg.hidden, 1e-5f, reinterpret_cast<uint16_t*>(x), (hipStream_t)stream);
@@ -1437,6 +1449,75 @@ moe_status moe_debug_inject_transfer_failure(moe_ctx* c, int32_t layer, int32_t 
   if (layer < 0 || layer >= c->cfg.n_layers || mode < 0 || mode > 2)
     return fail(c, MOE_E_ARG, "bad layer or mode");
   c->layers[layer].inject = mode;
+  return MOE_OK;
+}
+
+// MOE_SYNC_EACH_CALL=1: every call that enqueues GPU work waits for its
+// stream and the side stream and reads the device error word, so that an
+// asynchronous error is reported by the call that caused it.
+moe_status sync_each_call(moe_ctx* c, void* stream, moe_status st, const char* what) {
+  if (st != MOE_OK || !c || !c->sync_each) return st;
+  HIPCHK(c, hipStreamSynchronize((hipStream_t)stream));
+  if (c->side) HIPCHK(c, hipStreamSynchronize(c->side));
+  uint32_t v = 0;
+  HIPCHK(c, hipMemcpy(&v, c->err, 4, hipMemcpyDeviceToHost));
+  if (v)
+    return fail(c, MOE_E_DEVICE, std::string(what) + ": device error word " + std::to_string(v) +
+                                     " (MOE_SYNC_EACH_CALL; moe_check_device_errors clears it)");
+  return MOE_OK;
+}
+
+moe_status moe_route(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* forced_ids,
+                     int32_t* ids, float* w, float* logits, void* stream) {
+  return sync_each_call(c, stream, moe_route_call(c, layer, x, T, forced_ids, ids, w, logits, stream), "moe_route");
+}
+
+moe_status moe_expert_forward(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* ids,
+                              const float* w, void* out, void* stream) {
+  return sync_each_call(c, stream, moe_expert_forward_call(c, layer, x, T, ids, w, out, stream), "moe_expert_forward");
+}
+
+moe_status moe_expert_forward_noalloc(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* ids,
+                                      const float* w, void* out, void* stream) {
+  return sync_each_call(c, stream, moe_expert_forward_noalloc_call(c, layer, x, T, ids, w, out, stream), "moe_expert_forward_noalloc");
+}
+
+moe_status moe_stack_forward(moe_ctx* c, int32_t layer_begin, int32_t layer_end, float* h, int32_t T,
+                             const int32_t* forced_ids, void* x_trace, int32_t* ids_trace,
+                             float* w_trace, void* stream) {
+  return sync_each_call(c, stream, moe_stack_forward_call(c, layer_begin, layer_end, h, T, forced_ids, x_trace, ids_trace, w_trace, stream), "moe_stack_forward");
+}
+
+moe_status moe_cache_ensure(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n,
+                            int32_t* slots, int32_t step, void* stream) {
+  return sync_each_call(c, stream, moe_cache_ensure_call(c, layer, experts, n, slots, step, stream), "moe_cache_ensure");
+}
+
+moe_status moe_cache_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int32_t step,
+                              void* stream) {
+  return sync_each_call(c, stream, moe_cache_prefetch_call(c, layer, experts, n, step, stream), "moe_cache_prefetch");
+}
+
+moe_status moe_cache_pin(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int32_t step,
+                         void* stream) {
+  return sync_each_call(c, stream, moe_cache_pin_call(c, layer, experts, n, step, stream), "moe_cache_pin");
+}
+
+moe_status moe_stack_forward_pooled(moe_ctx* c, int32_t layer_begin, int32_t layer_end, float* h, int32_t T,
+                                    int32_t prefetch, int32_t step, int32_t* ids_trace, int32_t* guess_trace,
+                                    void* stream) {
+  return sync_each_call(c, stream, moe_stack_forward_pooled_call(c, layer_begin, layer_end, h, T, prefetch, step, ids_trace, guess_trace, stream), "moe_stack_forward_pooled");
+}
+
+moe_status moe_rmsnorm(moe_ctx* c, const float* h, int32_t T, void* x, void* stream) {
+  return sync_each_call(c, stream, moe_rmsnorm_call(c, h, T, x, stream), "moe_rmsnorm");
+}
+
+moe_status moe_debug_delay_copies(moe_ctx* c, int32_t microseconds) {
+  if (!c) return MOE_E_ARG;
+  if (microseconds < 0 || microseconds > MOE_MAX_COPY_DELAY_US)
+    return fail(c, MOE_E_ARG, "the copy delay must be in [0, " + std::to_string(MOE_MAX_COPY_DELAY_US) + "] microseconds");
+  c->copy_delay_us = microseconds;
   return MOE_OK;
 }
 

@@ -68,6 +68,9 @@ int mfma_max_tiles(int T, int k, int E, int rows, int mode, int mfma_min);
 void launch_mfma_gateup(const MfmaArgs& a, int max_tiles, hipStream_t stream);
 void launch_mfma_down(const MfmaArgs& a, int max_tiles, hipStream_t stream);
 
+// Test support (debug.hip): a bounded wait of `microseconds` on `stream`.
+void launch_copy_delay(hipStream_t stream, int microseconds);
+
 struct ExpertArgs {
   const uint8_t* blobs;       // expert storage of the layer (slot-indexed)
   int64_t blob_stride;        // bytes per slot
