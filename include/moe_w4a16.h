@@ -356,6 +356,23 @@ moe_status moe_fused_phase_stamps(moe_ctx* ctx, uint64_t* dev_buf, int64_t count
 
 /* ---- expert-slot pool (partial residency) ------------------------------------ */
 
+/* Several consumer streams on one pooled context ("Horizon RunMap -
+ * Architecture, Results and Public Evaluation", "Partial-residency contract:
+ * immutable authority and miss lifecycle": a request captures a generation and
+ * acquires its routed group; prior-generation consumers keep their leases and
+ * victim storage is reused only after they retire; the first contract
+ * serialises miss transactions).  Every call of a pooled context that enqueues
+ * GPU work may use its own stream.  Those calls run on the GPU one after
+ * another in the order the host made them: each makes its stream wait for the
+ * end of the previous one, whatever its stream, and records its own end after
+ * its work.  A request -- its moe_cache_ensure calls and the compute call
+ * after them, with no call of another request in between -- reads the
+ * generation its ensures published.  Transfers run on the side stream
+ * beside the compute of other streams: a miss lands in a row (a spare row, or
+ * with in-place slots the victim's slot) only after every earlier reader of
+ * that row on any stream has retired.  The host calls themselves must not
+ * overlap (one thread at a time per context). */
+
 /* ensure() of the slot pool of `layer` for one routed group ("F51 Nitro /
  * Nitro-MoE", "Layer 1 - expert persistence cache": lookup, evict, copy host
  * to device, return the slot; "Horizon RunMap - Architecture, Results and

@@ -558,3 +558,60 @@ def test_sync_each_call_reports_device_errors_at_the_call(moe, olmoe_layers, mon
         ctx.close()
     monkeypatch.delenv("MOE_SYNC_EACH_CALL")
     assert torch.equal(outs["0"], outs["1"])
+
+
+# ---- two consumer streams ----------------------------------------------------------
+@pytest.mark.parametrize("mode", ["in_place", "spare", "staged"])
+def test_pool_two_consumer_streams_delayed_readers(moe, olmoe_layers, h0s, mode):
+    """Two request streams on one pooled context ("Partial-residency contract:
+    immutable authority and miss lifecycle": prior-generation consumers keep
+    their leases; victim storage is reused only after they retire).  Requests
+    alternate A, B; every A request starts with a ~1 ms spin on its stream, so
+    its reads run late while B's ensures already transfer; copies are delayed
+    too; with 12 slots for two groups of 8, B's misses evict experts that the
+    pending A request reads.  Each stream's outputs equal a fully resident run
+    of its own routing, bit for bit, and the decisions equal the oracle's over
+    the interleaved groups."""
+    say(f"test_pool_two_consumer_streams mode={mode}")
+    # C < 2k: a B request's misses must evict experts of the A request just
+    # before it, whose delayed reads are still pending
+    steps, E, k, C = 24, fx.OLMOE.n_experts, fx.OLMOE.top_k, 12
+    tr = {"A": fx.zipf_trace("pool-two-A", steps, L, E, k, s=1.1),
+          "B": fx.zipf_trace("pool-two-B", steps, L, E, k, s=1.1)}
+    res = _ctx(moe, olmoe_layers)
+    ref = {n: _run(res, tr[n], h0s, pooled=False, steps=steps) for n in "AB"}
+    res.close()
+    kw = {"in_place": {}, "spare": SPARE, "staged": STAGED}[mode]
+    ctx = _ctx(moe, olmoe_layers, policy="lru", slots=C, **kw)
+    ctx.delay_copies(100)
+    streams = {"A": torch.cuda.Stream(), "B": torch.cuda.Stream()}
+    ftr = {n: torch.from_numpy(tr[n][:, :, None, :].copy()).cuda() for n in "AB"}
+    torch.cuda.synchronize()
+    outs = {"A": [], "B": []}
+    for s in range(steps):
+        for i, n in enumerate("AB"):
+            st = streams[n]
+            with torch.cuda.stream(st):
+                if n == "A":
+                    torch.cuda._sleep(2_000_000)
+                for l in range(L):
+                    ctx.cache_ensure(l, tr[n][s, l], step=2 * s + i, stream=st)
+                h = h0s[s % len(h0s)].clone()
+                ctx.stack_forward(h, forced_ids=ftr[n][s], stream=st)
+                outs[n].append(h)
+    torch.cuda.synchronize()
+    assert ctx.check_device_errors() == 0
+    for n in "AB":
+        assert torch.equal(torch.stack(outs[n]), ref[n]), f"stream {n} output changed ({mode})"
+    cross = 0  # B misses whose victim is an expert of the A request just before
+    for l in range(L):
+        sim = ora.CacheSim(ora.LRU, E, C, layer=l)
+        for s in range(steps):
+            sim.ensure(tr["A"][s, l].tolist(), 2 * s)
+            n0 = len(sim.events)
+            sim.ensure(tr["B"][s, l].tolist(), 2 * s + 1)
+            cross += sum(1 for e in sim.events[n0:] if e.victim in set(tr["A"][s, l].tolist()))
+        assert ctx.cache_events(l) == [e.as_tuple() for e in sim.events], f"layer {l}"
+    say(f"  B misses evicting the pending A request's experts: {cross}")
+    assert cross > 0
+    ctx.close()

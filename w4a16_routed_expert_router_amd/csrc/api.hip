@@ -188,6 +188,9 @@ struct moe_ctx {
   uint32_t* err = nullptr;
   hipStream_t side = nullptr;
   int copy_delay_us = 0;       // test hook: wait before every host-to-device blob copy
+  // slot pools: recorded after every call that publishes or reads the pool,
+  // on that call's stream; the next such call waits for it first
+  hipEvent_t pool_tail = nullptr;
   bool sync_each = false;      // MOE_SYNC_EACH_CALL=1 at creation
   std::string last_error;
   bool faulted = false;
@@ -348,6 +351,27 @@ void restore_rows(LayerState& L, RowState&& r) {
 // A blob comes straight from the pinned backing, or (staged transport) from
 // the pageable source through the next pinned staging buffer, after a host
 // wait until that buffer's previous transfer has completed.
+// Calls from several streams on a pooled context.  The calls that publish or
+// read the slot pool (and use the context's scratch) run on the GPU one after
+// another in the order they were made, whatever their streams: each first
+// makes its stream wait for the previous one's end (the wait takes that record
+// as it stands when the wait is enqueued; the next record comes after it).
+// Transfers still run on the side stream beside them.  A row's lease, recorded
+// on the stream of the call that vacates it after that wait, and each layer's
+// `retired` event, recorded by its latest reader, therefore cover every
+// earlier reader on every stream.
+moe_status pool_order_begin(moe_ctx* c, hipStream_t s) {
+  if (!pooled(c) || !c->pool_tail) return MOE_OK;
+  HIPCHK(c, hipStreamWaitEvent(s, c->pool_tail, 0));
+  return MOE_OK;
+}
+moe_status pool_order_end(moe_ctx* c, hipStream_t s) {
+  if (!pooled(c)) return MOE_OK;
+  if (!c->pool_tail) HIPCHK(c, hipEventCreateWithFlags(&c->pool_tail, hipEventDisableTiming));
+  HIPCHK(c, hipEventRecord(c->pool_tail, s));
+  return MOE_OK;
+}
+
 // Test hook: occupies the side stream for the set time before a blob copy.
 void delay_copy(moe_ctx* c) {
   if (c->copy_delay_us > 0) launch_copy_delay(c->side, c->copy_delay_us);
@@ -849,6 +873,7 @@ void moe_destroy(moe_ctx* c) {
   for (uint8_t* p : c->stage) (void)hipHostFree(p);
   for (hipEvent_t e : c->stage_ev) (void)hipEventDestroy(e);
   if (c->side) (void)hipStreamDestroy(c->side);
+  if (c->pool_tail) (void)hipEventDestroy(c->pool_tail);
   for (auto& p : c->timer_events) {
     (void)hipEventDestroy(p.first);
     (void)hipEventDestroy(p.second);
@@ -1452,6 +1477,9 @@ moe_status moe_debug_inject_transfer_failure(moe_ctx* c, int32_t layer, int32_t 
   return MOE_OK;
 }
 
+// Every call that enqueues GPU work: on a pooled context it first waits for
+// the previous such call (pool_order_begin) and records its own end after its
+// work (pool_order_end).
 // MOE_SYNC_EACH_CALL=1: every call that enqueues GPU work waits for its
 // stream and the side stream and reads the device error word, so that an
 // asynchronous error is reported by the call that caused it.
@@ -1469,48 +1497,84 @@ moe_status sync_each_call(moe_ctx* c, void* stream, moe_status st, const char* w
 
 moe_status moe_route(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* forced_ids,
                      int32_t* ids, float* w, float* logits, void* stream) {
-  return sync_each_call(c, stream, moe_route_call(c, layer, x, T, forced_ids, ids, w, logits, stream), "moe_route");
+  if (c && !c->faulted)
+    if (moe_status st = pool_order_begin(c, (hipStream_t)stream)) return st;
+  moe_status st = moe_route_call(c, layer, x, T, forced_ids, ids, w, logits, stream);
+  if (st == MOE_OK && c) st = pool_order_end(c, (hipStream_t)stream);
+  return sync_each_call(c, stream, st, "moe_route");
 }
 
 moe_status moe_expert_forward(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* ids,
                               const float* w, void* out, void* stream) {
-  return sync_each_call(c, stream, moe_expert_forward_call(c, layer, x, T, ids, w, out, stream), "moe_expert_forward");
+  if (c && !c->faulted)
+    if (moe_status st = pool_order_begin(c, (hipStream_t)stream)) return st;
+  moe_status st = moe_expert_forward_call(c, layer, x, T, ids, w, out, stream);
+  if (st == MOE_OK && c) st = pool_order_end(c, (hipStream_t)stream);
+  return sync_each_call(c, stream, st, "moe_expert_forward");
 }
 
 moe_status moe_expert_forward_noalloc(moe_ctx* c, int32_t layer, const void* x, int32_t T, const int32_t* ids,
                                       const float* w, void* out, void* stream) {
-  return sync_each_call(c, stream, moe_expert_forward_noalloc_call(c, layer, x, T, ids, w, out, stream), "moe_expert_forward_noalloc");
+  if (c && !c->faulted)
+    if (moe_status st = pool_order_begin(c, (hipStream_t)stream)) return st;
+  moe_status st = moe_expert_forward_noalloc_call(c, layer, x, T, ids, w, out, stream);
+  if (st == MOE_OK && c) st = pool_order_end(c, (hipStream_t)stream);
+  return sync_each_call(c, stream, st, "moe_expert_forward_noalloc");
 }
 
 moe_status moe_stack_forward(moe_ctx* c, int32_t layer_begin, int32_t layer_end, float* h, int32_t T,
                              const int32_t* forced_ids, void* x_trace, int32_t* ids_trace,
                              float* w_trace, void* stream) {
-  return sync_each_call(c, stream, moe_stack_forward_call(c, layer_begin, layer_end, h, T, forced_ids, x_trace, ids_trace, w_trace, stream), "moe_stack_forward");
+  if (c && !c->faulted)
+    if (moe_status st = pool_order_begin(c, (hipStream_t)stream)) return st;
+  moe_status st = moe_stack_forward_call(c, layer_begin, layer_end, h, T, forced_ids, x_trace, ids_trace, w_trace, stream);
+  if (st == MOE_OK && c) st = pool_order_end(c, (hipStream_t)stream);
+  return sync_each_call(c, stream, st, "moe_stack_forward");
 }
 
 moe_status moe_cache_ensure(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n,
                             int32_t* slots, int32_t step, void* stream) {
-  return sync_each_call(c, stream, moe_cache_ensure_call(c, layer, experts, n, slots, step, stream), "moe_cache_ensure");
+  if (c && !c->faulted)
+    if (moe_status st = pool_order_begin(c, (hipStream_t)stream)) return st;
+  moe_status st = moe_cache_ensure_call(c, layer, experts, n, slots, step, stream);
+  if (st == MOE_OK && c) st = pool_order_end(c, (hipStream_t)stream);
+  return sync_each_call(c, stream, st, "moe_cache_ensure");
 }
 
 moe_status moe_cache_prefetch(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int32_t step,
                               void* stream) {
-  return sync_each_call(c, stream, moe_cache_prefetch_call(c, layer, experts, n, step, stream), "moe_cache_prefetch");
+  if (c && !c->faulted)
+    if (moe_status st = pool_order_begin(c, (hipStream_t)stream)) return st;
+  moe_status st = moe_cache_prefetch_call(c, layer, experts, n, step, stream);
+  if (st == MOE_OK && c) st = pool_order_end(c, (hipStream_t)stream);
+  return sync_each_call(c, stream, st, "moe_cache_prefetch");
 }
 
 moe_status moe_cache_pin(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n, int32_t step,
                          void* stream) {
-  return sync_each_call(c, stream, moe_cache_pin_call(c, layer, experts, n, step, stream), "moe_cache_pin");
+  if (c && !c->faulted)
+    if (moe_status st = pool_order_begin(c, (hipStream_t)stream)) return st;
+  moe_status st = moe_cache_pin_call(c, layer, experts, n, step, stream);
+  if (st == MOE_OK && c) st = pool_order_end(c, (hipStream_t)stream);
+  return sync_each_call(c, stream, st, "moe_cache_pin");
 }
 
 moe_status moe_stack_forward_pooled(moe_ctx* c, int32_t layer_begin, int32_t layer_end, float* h, int32_t T,
                                     int32_t prefetch, int32_t step, int32_t* ids_trace, int32_t* guess_trace,
                                     void* stream) {
-  return sync_each_call(c, stream, moe_stack_forward_pooled_call(c, layer_begin, layer_end, h, T, prefetch, step, ids_trace, guess_trace, stream), "moe_stack_forward_pooled");
+  if (c && !c->faulted)
+    if (moe_status st = pool_order_begin(c, (hipStream_t)stream)) return st;
+  moe_status st = moe_stack_forward_pooled_call(c, layer_begin, layer_end, h, T, prefetch, step, ids_trace, guess_trace, stream);
+  if (st == MOE_OK && c) st = pool_order_end(c, (hipStream_t)stream);
+  return sync_each_call(c, stream, st, "moe_stack_forward_pooled");
 }
 
 moe_status moe_rmsnorm(moe_ctx* c, const float* h, int32_t T, void* x, void* stream) {
-  return sync_each_call(c, stream, moe_rmsnorm_call(c, h, T, x, stream), "moe_rmsnorm");
+  if (c && !c->faulted)
+    if (moe_status st = pool_order_begin(c, (hipStream_t)stream)) return st;
+  moe_status st = moe_rmsnorm_call(c, h, T, x, stream);
+  if (st == MOE_OK && c) st = pool_order_end(c, (hipStream_t)stream);
+  return sync_each_call(c, stream, st, "moe_rmsnorm");
 }
 
 moe_status moe_debug_delay_copies(moe_ctx* c, int32_t microseconds) {
