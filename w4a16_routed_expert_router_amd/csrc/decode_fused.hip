@@ -48,6 +48,7 @@
 // bit-identical results.  The grid is exactly 256 blocks (one per compute
 // unit, all resident together), each owning H / 256 = 8 residual rows.
 #include "fused_common.hpp"
+#include "topk_wave.hpp"
 
 namespace moe {
 
@@ -63,6 +64,9 @@ struct FusedSmem {
       int prank[kFW][kWave];                 // partial ranks of the waves
       int prank2[kFW][kWave];
       uint64_t key[kFW][kWave];              // per-wave (logit, id) sort keys
+      uint64_t cand[kFMaxCand];              // one-token candidates (keys)
+      uint64_t scr[2 * kWave];               // rank scratch of wave 0
+      uint64_t top[kFMaxP];                  // keys of ranks 0 .. k-1
     } sel;
     _Float16 hst[kFStageHalves];             // intermediates of every pair (down A operand)
     float hfull[kFStageHalves / 2];          // residual of every token (E1 staging)
@@ -222,56 +226,87 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
 
     // ---------------- selection: top-k by (logit desc, id asc) ----------------
     const int nch = E >> 6;
-    if (T == 1 && nch == 1 && !a.forced) {
-      // one token, 64 experts: every wave ranks, weighs and groups by itself
-      // (bit-identical results in every wave), so the phase needs no barrier;
-      // a wave's LDS accesses complete in order, so it reads back its own writes
+    if (T == 1 && nch <= kFW && !a.forced) {
+      // One token, at most 512 experts.  Lane l holds the keys of experts
+      // l + 64 j, ordered like (logit desc, id asc) by one unsigned compare.
+      // (1) The largest key of each lane; (2) the rank of each lane maximum
+      // among the 64, its 64 x 64 comparisons split over the waves (wave w
+      // takes lanes 8w .. 8w+7) and summed through LDS; (3) the lane maximum
+      // of rank k-1 bounds the k-th largest key from below (the k lanes above
+      // it hold k keys at least as large), so the keys at or above it -- at
+      // most k lanes x nch keys -- contain the top k, which wave 0 ranks
+      // exactly.  With 64 experts the lane maxima are the keys themselves and
+      // step (2) is the whole ranking.
       const float* lg = s.u.sel.logit;
-      const float v = lg[lane];
-      // 64-bit key ordered like (logit desc, id asc): the logit's bits mapped
-      // to an order-preserving unsigned integer, then the complemented id;
-      // rank = number of keys above this lane's (logits are never -0 or NaN)
-      const uint32_t vb = __builtin_bit_cast(uint32_t, v);
-      const uint32_t ob = (vb & 0x80000000u) ? ~vb : (vb | 0x80000000u);
-      const uint64_t key = ((uint64_t)ob << 32) | (uint32_t)(kWave - 1 - lane);
-      uint64_t* kw = s.u.sel.key[wv];
-      kw[lane] = key;
-      int r = 0;
+      uint64_t kj[kFW];
+      uint64_t m = 0;
 #pragma unroll
-      for (int j0 = 0; j0 < kWave; j0 += 8) {
-        uint64_t kj[8];
+      for (int j = 0; j < kFW; ++j) {
+        kj[j] = j < nch ? sel_key(lg[j * kWave + lane], j * kWave + lane) : 0ull;
+        m = kj[j] > m ? kj[j] : m;
+      }
+      constexpr int kLanesPerWave = kWave / kFW;
+      int pr = 0;
 #pragma unroll
-        for (int u = 0; u < 8; u += 2) {
-          const uint4 two = *reinterpret_cast<const uint4*>(kw + j0 + u);
-          kj[u] = ((uint64_t)two.y << 32) | two.x;
-          kj[u + 1] = ((uint64_t)two.w << 32) | two.z;
+      for (int i = 0; i < kLanesPerWave; ++i) {
+        const int src = wv * kLanesPerWave + i;
+        const uint64_t mo = ((uint64_t)rdlane((uint32_t)(m >> 32), src) << 32) | rdlane((uint32_t)m, src);
+        pr += (int)(mo > m);
+      }
+      s.u.sel.prank[wv][lane] = pr;
+      __syncthreads();
+      stamp(s, a, l, 10);
+      if (wv == 0) {
+        int r = 0;
+#pragma unroll
+        for (int w = 0; w < kFW; ++w) r += s.u.sel.prank[w][lane];
+        uint64_t* top = s.u.sel.top;
+        if (nch == 1) {
+          if (r < k) top[r] = m;
+        } else {
+          const int tl = __builtin_ctzll(__ballot(r == k - 1));  // exactly one lane
+          const uint64_t th = ((uint64_t)rdlane((uint32_t)(m >> 32), tl) << 32) | rdlane((uint32_t)m, tl);
+          const uint64_t below = (1ull << lane) - 1ull;
+          int n = 0;
+#pragma unroll
+          for (int j = 0; j < kFW; ++j) {
+            const bool c = kj[j] >= th;  // empty keys (0) never qualify
+            const uint64_t bal = __ballot(c);
+            if (c) s.u.sel.cand[n + __popcll(bal & below)] = kj[j];
+            n += __popcll(bal);
+          }
+          wave_top_cands(s.u.sel.cand, n, k, 0, s.u.sel.scr, top, lane);
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) r += (int)(kj[u] > key);
-      }
-      if (r < k) s.ids[r] = lane;
-      const float mx = lg[s.ids[0]];
-      const float sm = wave_sum(expf(v - mx));
-      const int ej = lane < k ? s.ids[lane] : 0;
-      float wj = lane < k ? expf(lg[ej] - mx) / sm : 0.0f;
-      if (a.renorm) wj = wj / wave_sum(wj);
-      if (lane < k) {
-        s.w[lane] = wj;
-        if (b == 0 && wv == 0 && a.ids_trace) a.ids_trace[(int64_t)l * P + lane] = ej;
-        if (b == 0 && wv == 0 && a.w_trace) a.w_trace[(int64_t)l * P + lane] = wj;
-        // unit u = rank u; pair u
-        int slot = L.map ? ldg<int32_t>(L.map + ej) : ej;
-        if (slot < 0) {
-          errs |= kErrNotResident;
-          slot = 0;
+        // softmax over all E logits, in the same order as for several tokens
+        const float mx = key_value(top[0]);
+        float sm = 0.0f;
+        for (int c = 0; c < nch; ++c) sm += expf(lg[c * kWave + lane] - mx);
+        sm = wave_sum(sm);
+        const uint64_t kt = lane < k ? top[lane] : 0ull;
+        const int ej = lane < k ? key_id(kt) : 0;
+        float wj = lane < k ? expf(key_value(kt) - mx) / sm : 0.0f;
+        if (a.renorm) wj = wj / wave_sum(wj);
+        stamp(s, a, l, 11);
+        if (lane < k) {
+          s.ids[lane] = ej;
+          s.w[lane] = wj;
+          if (b == 0 && a.ids_trace) a.ids_trace[(int64_t)l * P + lane] = ej;
+          if (b == 0 && a.w_trace) a.w_trace[(int64_t)l * P + lane] = wj;
+          // unit u = rank u; pair u
+          int slot = L.map ? ldg<int32_t>(L.map + ej) : ej;
+          if (slot < 0) {
+            errs |= kErrNotResident;
+            slot = 0;
+          }
+          s.unit_slot[lane] = slot;
+          s.pair_of[lane] = lane;
         }
-        s.unit_slot[lane] = slot;
-        s.pair_of[lane] = lane;
+        if (lane == 0) {
+          if (a.has_shared) s.pair_of[k] = P;
+          s.nunits = k;
+        }
       }
-      if (lane == 0) {
-        if (a.has_shared) s.pair_of[k] = P;
-        s.nunits = k;
-      }
+      __syncthreads();
     } else {
       if (a.forced) {
         if (wv == 0) {
@@ -465,8 +500,9 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
     auto unit_blob = [&](int u) -> const uint8_t* {
       return u < U ? L.store + (int64_t)s.unit_slot[u] * a.blob_stride : L.shared;
     };
+    static_assert(GH == 8, "one 16-byte load carries the 8 group scales of a half row");
     uint4 gq[GH];
-    uint16_t gs[GH];
+    uint4 gs;  // FP16 scales of the half row's GH groups
     auto load_gu = [&](int task) {
       const int g = task >> 1, half = task & 1;
       const int u = g / GPU, i0 = (g - u * GPU) * 8;
@@ -476,10 +512,10 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
       const uint8_t* cp = blob + a.lay.codes(mat) + (int64_t)row * (H / 2) + half * (H / 4) + q * 16;
       const uint16_t* sp = reinterpret_cast<const uint16_t*>(blob + a.lay.scales(mat)) + (int64_t)row * (H / 128) + half * GH;
 #pragma unroll
-      for (int g2 = 0; g2 < GH; ++g2) {
-        gq[g2] = ldg_u4(cp + g2 * 64);
-        gs[g2] = ldg<uint16_t>(sp + g2);
-      }
+      for (int g2 = 0; g2 < GH; ++g2) gq[g2] = ldg_u4(cp + g2 * 64);
+      // one 16-byte load for the scales: 2-byte loads cost the address unit
+      // about as much per instruction as a whole 16-byte-per-lane load
+      gs = ldg_u4(sp);
     };
     // down weights go straight to LDS: no registers are held for them while
     // gate/up runs and E3 completes.  Addresses are formed before any load of
@@ -533,7 +569,7 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
 #pragma unroll
           for (int st = 0; st < 4; ++st)
             ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[st], decode_h8(dword_of(gq[g2], st)), ag, 0, 0, 0);
-          acc += ag * half_bits_to_float(gs[g2]);
+          acc += ag * half_bits_to_float((uint16_t)(dword_of(gs, g2 >> 1) >> (16 * (g2 & 1))));
           // decode one group at a time: keeps the decoded operands of later
           // groups from being hoisted (and held in registers) early
           __builtin_amdgcn_sched_barrier(0);

@@ -30,9 +30,10 @@ __device__ __forceinline__ uint32_t rdlane(uint32_t v, int j) {
 
 // 64-bit selection key of expert `id` with logit v: ordered like (logit desc,
 // id asc) by one unsigned comparison (larger key = earlier rank); distinct
-// for distinct ids and never 0.
+// for distinct ids and never 0.  -0 is taken as +0, so that the two zeros
+// tie like equal values and the id decides.
 __device__ __forceinline__ uint64_t sel_key(float v, int id) {
-  return ((uint64_t)order_bits(v) << 32) | (uint32_t)(0xffffffffu - (uint32_t)id);
+  return ((uint64_t)order_bits(v + 0.0f) << 32) | (uint32_t)(0xffffffffu - (uint32_t)id);
 }
 __device__ __forceinline__ int key_id(uint64_t key) { return (int)(0xffffffffu - (uint32_t)key); }
 __device__ __forceinline__ float key_value(uint64_t key) { return unorder_bits((uint32_t)(key >> 32)); }
