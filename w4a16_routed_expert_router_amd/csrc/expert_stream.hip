@@ -14,6 +14,10 @@
 //     ring runs across item boundaries, so the weight stream never drains
 //     between items and no barrier stops it (a barrier is taken only when the
 //     next item belongs to another expert and its activations are loaded);
+//   * the FP16 scales of an item's rows come in one 16-byte load per lane and
+//     unit (2-byte loads cost the address unit about as much per instruction
+//     as 16-byte ones), and each step takes the scale of its group and row
+//     from the lane that holds it (ds_bpermute);
 //   * the tokens of the expert (<= 32, zero-padded to one or two 16-token
 //     sub-tiles; the second only when the expert has more than 16) are the A
 //     operand of v_mfma_f32_16x16x32_f16; INT4 codes are decoded in registers to the
@@ -35,8 +39,12 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ uint32_t word_of(const u4& v, int w) {
+  return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+}
+
 constexpr int kSW = 8;          // waves per block
-constexpr int kRing = 8;        // weight units in flight per wave
+constexpr int kRing = 3;        // weight units in flight per wave (deeper rings measured slower)
 constexpr int kTok = 32;        // tokens per expert handled here (two sub-tiles of 16)
 constexpr int kPad = 8;         // LDS row padding (halves)
 constexpr int kMaxList = 1024;  // experts per call
@@ -113,14 +121,17 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
 
   // ---- weight stream: unit v = (item lo + v / NG, scale group v % NG)
   // The unit loads are issued as inline assembly and waited for explicitly:
-  // every step issues exactly kUnitLoads loads (the tail re-reads the last
-  // unit), so the loads younger than unit v are always (kRing - 1) *
-  // kUnitLoads and "vmcnt <= that" means unit v has landed (loads return in
-  // order; stores and the activation-tile loads only make the wait longer).
-  // The compiler tracks none of these loads, so it never drains the ring.
-  constexpr int kUnitLoads = 4;
+  // every unit issues exactly kUnitLoads loads (its two code loads and the
+  // scale load of its item; the tail re-reads the last unit), so the loads
+  // younger than unit v are always (kRing - 1) * kUnitLoads and "vmcnt <=
+  // that" means unit v has landed (loads return in order; stores and the
+  // activation-tile loads only make the wait longer).  The compiler tracks
+  // none of these loads, so it never drains the ring.
+  constexpr int kUnitLoads = 3;
+  constexpr int SB = NG * 2;                   // scale bytes of one row
+  static_assert(SB == 32 || SB == 16 || SB == 8, "rows of 8 to 32 bytes of scales");
   u4 bq[kRing][2];
-  uint32_t bs[kRing][2];
+  u4 bsv[kRing];  // scales of the unit's item (used from its first unit)
   auto load_unit = [&](int v, int slot_) __attribute__((always_inline)) {
     const int it = lo + v / NG, g = v - (v / NG) * NG;
     const int se = it / ntn, nt = it - se * ntn;
@@ -133,14 +144,26 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
       const int mat = MODE == 0 ? j : 2;
       const int r = MODE == 0 ? nt * ROWS + wv * 16 + n : nt * ROWS + wv * 32 + j * 16 + n;
       const uint8_t* cp = blob + a.lay.codes(mat) + (int64_t)r * (K / 2) + q * 16 + g * 64;
-      const uint8_t* sp = blob + a.lay.scales(mat) + ((int64_t)r * NG + g) * 2;
       asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(bq[slot_][j]) : "v"(cp) : "memory");
-      asm volatile("global_load_ushort %0, %1, off" : "=v"(bs[slot_][j]) : "v"(sp) : "memory");
     }
+    // lane (n, q) holds the 16-byte aligned chunk of scales [8 (q & 1), +8)
+    // of row n of sub-tile q >> 1 (rows of 16 bytes: the lanes q & 1 == 1
+    // repeat the row's load; rows of 8 bytes: the chunk holds rows n & ~1 and
+    // n | 1).  The item's later units repeat its first unit's load, which
+    // keeps the count of loads per unit fixed and costs the address unit one
+    // instruction.  (Every ring register is a 16-byte vector: a ring slot of
+    // another width was seen copied at the loop's back edge while its load was
+    // in flight.)
+    const int j = q >> 1;
+    const int mat = MODE == 0 ? j : 2;
+    const int r = MODE == 0 ? nt * ROWS + wv * 16 + n : nt * ROWS + wv * 32 + j * 16 + n;
+    const int h = SB == 32 ? (q & 1) : 0;
+    const uint8_t* sp = blob + a.lay.scales(mat) + (((int64_t)r * SB) & ~(int64_t)15) + h * 16;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(bsv[slot_]) : "v"(sp) : "memory");
   };
   auto wait_unit = [&](int slot_) __attribute__((always_inline)) {
-    asm volatile("s_waitcnt vmcnt(%4)"
-                 : "+v"(bq[slot_][0]), "+v"(bq[slot_][1]), "+v"(bs[slot_][0]), "+v"(bs[slot_][1])
+    asm volatile("s_waitcnt vmcnt(%3)"
+                 : "+v"(bq[slot_][0]), "+v"(bq[slot_][1]), "+v"(bsv[slot_])
                  : "n"((kRing - 1) * kUnitLoads)
                  : "memory");
   };
@@ -202,13 +225,22 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   for (int m = 0; m < 2; ++m) acc[m][0] = acc[m][1] = f4{0.f, 0.f, 0.f, 0.f};
   uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u;
   asm("" : "+v"(mlo), "+v"(mhi));  // the decode masks live in VGPRs
+  u4 cs = {0u, 0u, 0u, 0u};  // scales of the current item (see load_unit)
+  // Every round runs all kRing steps, so that the count of loads between a
+  // unit's issue and its wait is the same on every path; the last round's
+  // steps past nv only keep that count (they load and wait, and compute and
+  // store nothing).
   auto step = [&](int v, auto uc) __attribute__((always_inline)) {
     constexpr int U = decltype(uc)::value;
-    const int it = lo + v / NG, g = v - (v / NG) * NG;
+    const bool live = v < nv;  // uniform
+    const int vl = live ? v : nv - 1;
+    const int it = lo + vl / NG, g = vl - (vl / NG) * NG;
     const int se = it / ntn;
-    if (g == 0 && se != cur) load_tile(se);  // uniform: same v sequence in every wave
+    if (live && g == 0 && se != cur) load_tile(se);  // uniform: same v sequence in every wave
     load_unit(min(v + kRing - 1, nv - 1), (U + kRing - 1) % kRing);
     wait_unit(U);
+    if (!live) return;
+    if (g == 0) cs = bsv[U];  // uniform
     f4 ag[2][2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) ag[m][0] = ag[m][1] = f4{0.f, 0.f, 0.f, 0.f};
@@ -231,7 +263,15 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
         ag[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, decode_unscaled(bq[U][1][st], mlo, mhi), ag[0][1], 0, 0, 0);
       }
     }
-    const float s0 = half_bits_to_float((uint16_t)bs[U][0]), s1 = half_bits_to_float((uint16_t)bs[U][1]);
+    // scale of group g, row n of sub-tile j: lane n + 16 (2 j + g / 8), 16-bit
+    // word g % 8 of its load (rows of 8 bytes: word g + 4 (n & 1))
+    const int w = (g & 7) >> 1;  // uniform
+    const uint32_t sw = SB == 8 ? ((n & 1) ? word_of(cs, w + 2) : word_of(cs, w)) : word_of(cs, w);
+    const int src = n + 16 * (g >> 3);
+    const uint32_t sv0 = (uint32_t)__shfl((int)sw, src, kWave);
+    const uint32_t sv1 = (uint32_t)__shfl((int)sw, src + 32, kWave);
+    const int sh = 16 * (g & 1);
+    const float s0 = half_bits_to_float((uint16_t)(sv0 >> sh)), s1 = half_bits_to_float((uint16_t)(sv1 >> sh));
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       acc[m][0] += ag[m][0] * s0;
@@ -267,7 +307,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   };
   for (int v0 = 0; v0 < nv; v0 += kRing) {
     [&]<int... Us>(std::integer_sequence<int, Us...>) {
-      ((v0 + Us < nv ? step(v0 + Us, std::integral_constant<int, Us>{}) : void()), ...);
+      (step(v0 + Us, std::integral_constant<int, Us>{}), ...);
     }(std::make_integer_sequence<int, kRing>{});
   }
 }
