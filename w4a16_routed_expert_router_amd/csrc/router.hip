@@ -21,6 +21,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "exact_dot.hpp"
+#include "topk_wave.hpp"
 
 namespace moe {
 
@@ -128,19 +129,30 @@ __global__ __launch_bounds__(64) void router_logits_kernel(const uint16_t* __res
   }
 }
 
-__device__ __forceinline__ uint64_t rank_key(float v, int id) {
-  uint32_t u = __float_as_uint(v + 0.0f);  // -0 -> +0
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)id);
-}
+constexpr int kTopkMaxK = 16;  // largest top-k a context accepts
+
+// LDS scratch of one wave's top-k (KV = ceil(E / 64) keys per lane).
+template <int KV>
+struct TopkScratch {
+  alignas(16) uint64_t scr[kWave];                  // lane maxima (rank scratch)
+  alignas(16) uint64_t cand[kTopkMaxK * KV + 2];    // keys at or above the bound
+  uint64_t top[kTopkMaxK];                          // keys of ranks 0 .. k-1
+};
 
 // Softmax + top-k (or the forced ids) of one token, by one wave.  lg holds the
 // token's E logits (global memory or LDS); KV = ceil(E / 64) logits per lane.
+// Selection: lane l holds the keys of experts l + 64 i (one 64-bit key per
+// expert, ordered like (logit desc, id asc) by one unsigned compare).  The
+// rank of each lane's largest key among the 64 lane maxima takes one pass of
+// comparisons; the lane maximum of rank k-1 bounds the k-th largest key from
+// below (the k lanes above it hold k keys at least as large), so the keys at
+// or above it -- at most k lanes x KV keys -- contain the top k, which are
+// ranked exactly.  With KV = 1 the lane maxima are the keys themselves.
 template <int KV>
 __device__ __forceinline__ void topk_token(const float* lg, int t, int E, int k, int renorm,
                                            const int32_t* __restrict__ forced,
                                            int32_t* __restrict__ ids, float* __restrict__ w,
-                                           uint32_t* __restrict__ err, int lane) {
+                                           uint32_t* __restrict__ err, TopkScratch<KV>& ts, int lane) {
   float v[KV];
   float mx = -INFINITY;
 #pragma unroll
@@ -173,22 +185,33 @@ __device__ __forceinline__ void topk_token(const float* lg, int t, int E, int k,
     }
     my_id = e;
   } else {
-    uint32_t removed = 0;
-    for (int r = 0; r < k; ++r) {
-      uint64_t best = 0;
+    uint64_t kv[KV];
+    uint64_t mk = 0;  // 0: a lane without experts (never selected, k <= E)
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int e = i * kWave + lane;
+      kv[i] = e < E ? sel_key(v[i], e) : 0ull;
+      mk = kv[i] > mk ? kv[i] : mk;
+    }
+    const int r = wave_rank64(mk, ts.scr, lane);
+    if (KV == 1) {
+      if (r < k) ts.top[r] = mk;
+    } else {
+      const int tl = __builtin_ctzll(__ballot(r == k - 1));  // exactly one lane
+      const uint64_t th = ((uint64_t)rdlane((uint32_t)(mk >> 32), tl) << 32) | rdlane((uint32_t)mk, tl);
+      const uint64_t below = (1ull << lane) - 1ull;
+      int n = 0;
 #pragma unroll
       for (int i = 0; i < KV; ++i) {
-        const int e = i * kWave + lane;
-        if (e < E && !((removed >> i) & 1u)) {
-          const uint64_t key = rank_key(v[i], e);
-          best = key > best ? key : best;
-        }
+        const bool c = kv[i] >= th;  // empty keys (0) never qualify
+        const uint64_t bal = __ballot(c);
+        if (c) ts.cand[n + __popcll(bal & below)] = kv[i];
+        n += __popcll(bal);
       }
-      best = wave_max_u64(best);  // DPP network: no LDS round trips
-      const int id = (int)(~(uint32_t)best);
-      if (lane == (id & (kWave - 1))) removed |= 1u << (id / kWave);
-      if (lane == r) my_id = id;
+      if (lane == 0) ts.cand[n] = 0ull;  // read (never counted) when n is odd
+      wave_top_list(ts.cand, n, k, ts.top, lane);
     }
+    if (lane < k) my_id = key_id(ts.top[lane]);
   }
   float my_w = 0.0f;
   if (lane < k) my_w = expf(lg[my_id] - mx) / s;
@@ -211,7 +234,8 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict
                                                          uint32_t* __restrict__ err) {
   (void)T;
   const int t = blockIdx.x;
-  topk_token<16>(logits + (int64_t)t * E, t, E, k, renorm, forced, ids, w, err, threadIdx.x);  // E <= 1024
+  __shared__ TopkScratch<16> ts;
+  topk_token<16>(logits + (int64_t)t * E, t, E, k, renorm, forced, ids, w, err, ts, threadIdx.x);  // E <= 1024
 }
 
 // ---- FP64 matrix-core logits -----------------------------------------------------
@@ -325,6 +349,7 @@ __global__ __launch_bounds__(KV * 64) void router_select_kernel(RouterArgs a, co
                                                                 const double* __restrict__ nrm_x,
                                                                 const double* __restrict__ nrm_w, int KB, int KR) {
   __shared__ float slg[KV * kWave];
+  __shared__ TopkScratch<KV> ts;
   const int t = blockIdx.x, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int T = a.T, E = a.E;
   const int e = wv * kWave + lane;
@@ -375,7 +400,7 @@ __global__ __launch_bounds__(KV * 64) void router_select_kernel(RouterArgs a, co
   }
   __syncthreads();
   if (e < E) a.logits[(int64_t)t * E + e] = slg[e];
-  if (wv == 0) topk_token<KV>(slg, t, E, a.k, a.renorm, a.forced, a.ids, a.w, a.err, lane);
+  if (wv == 0) topk_token<KV>(slg, t, E, a.k, a.renorm, a.forced, a.ids, a.w, a.err, ts, lane);
 }
 
 // K per wave of the matrix-core router (0: the shape does not take it).

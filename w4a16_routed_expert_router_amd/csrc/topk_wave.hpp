@@ -97,4 +97,24 @@ __device__ __forceinline__ void wave_top_cands(const uint64_t* cand, int n, int 
   if (lane + kWave < n && r1 >= skip && r1 < skip + k) out[r1 - skip] = k1;
 }
 
+// Ranks 0 .. k-1 of the n distinct keys list[0 .. n) (any n): out[r] = the
+// key of rank r.  Each lane ranks the keys of its slots lane + 64 c against
+// the whole list, read from LDS two keys at a time (list 16-byte aligned;
+// list[n] is read when n is odd and must exist: it is never counted).
+__device__ __forceinline__ void wave_top_list(const uint64_t* list, int n, int k, uint64_t* out, int lane) {
+#pragma unroll 1
+  for (int c0 = 0; c0 < n; c0 += kWave) {
+    const bool own = c0 + lane < n;
+    const uint64_t key = own ? list[c0 + lane] : 0ull;
+    int r = 0;
+#pragma unroll 4
+    for (int j = 0; j < n; j += 2) {
+      const uint4 two = *reinterpret_cast<const uint4*>(list + j);
+      const uint64_t x0 = ((uint64_t)two.y << 32) | two.x, x1 = ((uint64_t)two.w << 32) | two.z;
+      r += (int)(x0 > key) + (int)(j + 1 < n && x1 > key);
+    }
+    if (own && r < k) out[r] = key;
+  }
+}
+
 }  // namespace moe
