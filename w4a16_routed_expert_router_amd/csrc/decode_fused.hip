@@ -62,6 +62,7 @@ struct FusedSmem {
       float cval[kFMaxT][kFMaxCand];         // per-chunk candidates (E > 64)
       int cid[kFMaxT][kFMaxCand];
       int prank[kFW][kWave];                 // partial ranks of the waves
+      alignas(16) int prankT[kWave][kFW];    // the same by lane (one token)
       int prank2[kFW][kWave];
       uint64_t key[kFW][kWave];              // per-wave (logit, id) sort keys
       uint64_t cand[kFMaxCand];              // one-token candidates (keys)
@@ -253,16 +254,45 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         const uint64_t mo = ((uint64_t)rdlane((uint32_t)(m >> 32), src) << 32) | rdlane((uint32_t)m, src);
         pr += (int)(mo > m);
       }
-      s.u.sel.prank[wv][lane] = pr;
+      s.u.sel.prankT[lane][wv] = pr;  // a lane's partial ranks side by side: two reads
       __syncthreads();
       stamp(s, a, l, 10);
       if (wv == 0) {
-        int r = 0;
-#pragma unroll
-        for (int w = 0; w < kFW; ++w) r += s.u.sel.prank[w][lane];
+        const uint4 p0 = *reinterpret_cast<const uint4*>(&s.u.sel.prankT[lane][0]);
+        const uint4 p1 = *reinterpret_cast<const uint4*>(&s.u.sel.prankT[lane][4]);
+        const int r = (int)(((p0.x + p0.y) + (p0.z + p0.w)) + ((p1.x + p1.y) + (p1.z + p1.w)));
         uint64_t* top = s.u.sel.top;
         if (nch == 1) {
-          if (r < k) top[r] = m;
+          // every lane holds its own expert: the weights are formed where the
+          // logits are, in rank order only for the renormalisation's sum
+          const int l0 = __builtin_ctzll(__ballot(r == 0));
+          const float mx = key_value(((uint64_t)rdlane((uint32_t)(m >> 32), l0) << 32) | rdlane((uint32_t)m, l0));
+          const float v = key_value(m);
+          const float sm = wave_sum(expf(v - mx));
+          float wj = r < k ? expf(v - mx) / sm : 0.0f;
+          if (a.renorm) {
+            if (r < k) s.w[r] = wj;
+            const float wr = lane < k ? s.w[lane] : 0.0f;
+            wj = wj / wave_sum(wr);
+          }
+          stamp(s, a, l, 11);
+          if (r < k) {
+            s.ids[r] = lane;
+            s.w[r] = wj;
+            if (b == 0 && a.ids_trace) a.ids_trace[(int64_t)l * P + r] = lane;
+            if (b == 0 && a.w_trace) a.w_trace[(int64_t)l * P + r] = wj;
+            int slot = L.map ? ldg<int32_t>(L.map + lane) : lane;
+            if (slot < 0) {
+              errs |= kErrNotResident;
+              slot = 0;
+            }
+            s.unit_slot[r] = slot;
+            s.pair_of[r] = r;
+          }
+          if (lane == 0) {
+            if (a.has_shared) s.pair_of[k] = P;
+            s.nunits = k;
+          }
         } else {
           const int tl = __builtin_ctzll(__ballot(r == k - 1));  // exactly one lane
           const uint64_t th = ((uint64_t)rdlane((uint32_t)(m >> 32), tl) << 32) | rdlane((uint32_t)m, tl);
@@ -276,34 +306,37 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
             n += __popcll(bal);
           }
           wave_top_cands(s.u.sel.cand, n, k, 0, s.u.sel.scr, top, lane);
-        }
-        // softmax over all E logits, in the same order as for several tokens
-        const float mx = key_value(top[0]);
-        float sm = 0.0f;
-        for (int c = 0; c < nch; ++c) sm += expf(lg[c * kWave + lane] - mx);
-        sm = wave_sum(sm);
-        const uint64_t kt = lane < k ? top[lane] : 0ull;
-        const int ej = lane < k ? key_id(kt) : 0;
-        float wj = lane < k ? expf(key_value(kt) - mx) / sm : 0.0f;
-        if (a.renorm) wj = wj / wave_sum(wj);
-        stamp(s, a, l, 11);
-        if (lane < k) {
-          s.ids[lane] = ej;
-          s.w[lane] = wj;
-          if (b == 0 && a.ids_trace) a.ids_trace[(int64_t)l * P + lane] = ej;
-          if (b == 0 && a.w_trace) a.w_trace[(int64_t)l * P + lane] = wj;
-          // unit u = rank u; pair u
-          int slot = L.map ? ldg<int32_t>(L.map + ej) : ej;
-          if (slot < 0) {
-            errs |= kErrNotResident;
-            slot = 0;
+          // softmax over all E logits, in the same order as for several tokens
+          // (the logits are the keys' values; -0 is +0 there, same exponential)
+          const float mx = key_value(top[0]);
+          float sm = 0.0f;
+#pragma unroll
+          for (int c = 0; c < kFW; ++c)
+            if (c < nch) sm += expf(key_value(kj[c]) - mx);
+          sm = wave_sum(sm);
+          const uint64_t kt = lane < k ? top[lane] : 0ull;
+          const int ej = lane < k ? key_id(kt) : 0;
+          float wj = lane < k ? expf(key_value(kt) - mx) / sm : 0.0f;
+          if (a.renorm) wj = wj / wave_sum(wj);
+          stamp(s, a, l, 11);
+          if (lane < k) {
+            s.ids[lane] = ej;
+            s.w[lane] = wj;
+            if (b == 0 && a.ids_trace) a.ids_trace[(int64_t)l * P + lane] = ej;
+            if (b == 0 && a.w_trace) a.w_trace[(int64_t)l * P + lane] = wj;
+            // unit u = rank u; pair u
+            int slot = L.map ? ldg<int32_t>(L.map + ej) : ej;
+            if (slot < 0) {
+              errs |= kErrNotResident;
+              slot = 0;
+            }
+            s.unit_slot[lane] = slot;
+            s.pair_of[lane] = lane;
           }
-          s.unit_slot[lane] = slot;
-          s.pair_of[lane] = lane;
-        }
-        if (lane == 0) {
-          if (a.has_shared) s.pair_of[k] = P;
-          s.nunits = k;
+          if (lane == 0) {
+            if (a.has_shared) s.pair_of[k] = P;
+            s.nunits = k;
+          }
         }
       }
       __syncthreads();
