@@ -253,15 +253,21 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict
 // the squared norms of the token and expert rows over the same K range.
 //
 // router_select_kernel (one block per token, one wave per 64 experts): adds the partials of the K
-// blocks in order and certifies each logit.  An output is reached through at
-// most KR / 2 roundings in each of its wave's two chains (one per product),
-// the addition of the two chains, 3 additions in the block and KB - 1 over
-// the K blocks (together below KR + KB + 4), each with a relative error of at most 2^-53 of a partial sum
-// bounded by S = sum |x_i w_i|; by Cauchy-Schwarz S <= |x| |w|, from the
-// squared norms (their own relative error, below H * 2^-53, is covered by the
-// factor 1 + 2^-20).  The logit is certified when the interval of half-width
-// (KR + KB + 4) * 2^-52 * |x| |w| around the FP64 sum lies strictly between
-// the rounding midpoints of its FP32 rounding; the wave recomputes the others
+// blocks in order and certifies each logit.  Every rounding has an error of at
+// most 2^-53 of the sum it produces, which is at most the sum of |x_i w_i| over
+// that sum's terms.  A wave's two chains (one per product parity) take at most
+// KR / 2 roundings each over disjoint terms, so together at most
+// KR / 2 * 2^-53 * S_wave (S_wave: the sum of |x_i w_i| over the wave's K
+// range); the addition of the two chains, 3 additions in the block and KB - 1
+// over the K blocks add at most (1 + 3 + KB - 1) * 2^-53 * S, so the error is
+// below (KR / 2 + KB + 3) * 2^-53 * S (one more unit covers the second-order
+// growth of the partial sums), with S = sum |x_i w_i| <= |x| |w| by
+// Cauchy-Schwarz, from the squared norms (their own relative error, below
+// H * 2^-53, is covered by the factor 1 + 2^-20).  The logit is certified when
+// the interval of half-width (KR / 2 + KB + 4) * 2^-53 * |x| |w| around the
+// FP64 sum lies strictly between the rounding midpoints of its FP32 rounding
+// (a logit near zero, whose rounding step is small next to |x| |w|, is the
+// usual case that fails); the wave recomputes the others
 // with compensated FP64 sums (certified the same way against a bound about
 // 2^-52 times smaller) and, where that still fails (an exact sum on or next
 // to a midpoint), exactly.  Softmax and top-k follow.
@@ -375,7 +381,7 @@ __global__ __launch_bounds__(KV * 64) void router_select_kernel(RouterArgs a, co
     const float rr = (float)s;  // round to nearest even
     if (rr != 0.0f && isfinite(rr) && isfinite(s)) {
       const double bound = sqrt(nx) * sqrt(nw) * (1.0 + 0x1p-20);
-      const double eps = (double)(KR + KB + 4) * 0x1p-52 * bound;
+      const double eps = (double)(KR / 2 + KB + 4) * 0x1p-53 * bound;
       const double rd = (double)rr;
       const double m_lo = 0.5 * (rd + (double)nextafterf(rr, -INFINITY));
       const double m_hi = 0.5 * (rd + (double)nextafterf(rr, INFINITY));
