@@ -68,6 +68,9 @@ struct FusedSmem {
       uint64_t cand[kFMaxCand];              // one-token candidates (keys)
       uint64_t scr[2 * kWave];               // rank scratch of wave 0
       uint64_t top[kFMaxP];                  // keys of ranks 0 .. k-1
+      uint64_t candT[kFMaxT][kFMaxCand];     // the same per token (a few tokens)
+      uint64_t scrT[kFMaxT][2 * kWave];
+      uint64_t topT[kFMaxT][kFMaxP];
     } sel;
     _Float16 hst[kFStageHalves];             // intermediates of every pair (down A operand)
     float hfull[kFStageHalves / 2];          // residual of every token (E1 staging)
@@ -362,6 +365,42 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
           if (lane == 0 && badm) errs |= (bm ? kErrBadId : 0u) | (dm ? kErrDupId : 0u);
           if (valid) s.ids[p] = tok_bad ? (p - t * k) : e;
         }
+      } else if (nch <= kFW) {
+        // a few tokens, at most 512 experts: wave t selects token t by itself,
+        // as for one token but without the split over waves -- the rank of
+        // each lane's largest key among the 64 lane maxima, then the exact
+        // ranking of the keys at or above the k-th lane maximum
+        if (wv < T) {
+          const int t = wv;
+          const float* lg = s.u.sel.logit + t * E;
+          uint64_t kj[kFW];
+          uint64_t m = 0;
+#pragma unroll
+          for (int j = 0; j < kFW; ++j) {
+            kj[j] = j < nch ? sel_key(lg[j * kWave + lane], j * kWave + lane) : 0ull;
+            m = kj[j] > m ? kj[j] : m;
+          }
+          const int r = wave_rank64(m, s.u.sel.key[wv], lane);
+          if (nch == 1) {
+            if (r < k) s.ids[t * k + r] = lane;
+          } else {
+            const int tl = __builtin_ctzll(__ballot(r == k - 1));  // exactly one lane
+            const uint64_t th = ((uint64_t)rdlane((uint32_t)(m >> 32), tl) << 32) | rdlane((uint32_t)m, tl);
+            const uint64_t below = (1ull << lane) - 1ull;
+            uint64_t* cand = s.u.sel.candT[t];
+            int n = 0;
+#pragma unroll
+            for (int j = 0; j < kFW; ++j) {
+              const bool c = kj[j] >= th;  // empty keys (0) never qualify
+              const uint64_t bal = __ballot(c);
+              if (c) cand[n + __popcll(bal & below)] = kj[j];
+              n += __popcll(bal);
+            }
+            uint64_t* top = s.u.sel.topT[t];
+            wave_top_cands(cand, n, k, 0, s.u.sel.scrT[t], top, lane);
+            if (lane < k) s.ids[t * k + lane] = key_id(top[lane]);
+          }
+        }
       } else {
         // rank of every expert within its chunk of 64: `wpt` waves share one
         // (token, chunk) task, each comparing all 64 lanes against a slice of
@@ -493,10 +532,15 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         const int e = valid ? s.ids[p] : -1;
         int q0 = p;  // first pair naming the same expert (ids of one token are distinct)
         if (T > 1) {
-#pragma unroll 1
-          for (int qq = kWave - 1; qq >= 0; --qq) {
-            const int eq = qq < P ? s.ids[qq] : -2;
-            q0 = ((qq < p) & (eq == e)) ? qq : q0;
+          // once per distinct expert: the lowest pair not yet grouped leads,
+          // and every pair naming its expert takes it as its first
+          uint64_t rem = __ballot(valid);
+          while (rem) {
+            const int ld = __builtin_ctzll(rem);
+            const int ev = __builtin_amdgcn_readlane(e, ld);
+            const bool same = valid && e == ev;
+            if (same) q0 = ld;
+            rem &= ~__ballot(same);
           }
         }
         const bool first = valid && q0 == p;
