@@ -629,7 +629,10 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
     // one round: MFMA over the wave's K half, LDS sum of the halves, SwiGLU,
     // publication.  Round 0 runs outside the loop so that its loads are
     // waited for one group at a time.
-    auto gu_round = [&](int task, bool first) __attribute__((always_inline)) {
+    // `next`: the wave's task of the following round, whose weights are
+    // loaded as soon as this round's MFMAs have taken theirs (the registers
+    // are free then), so that their latency runs under the round's exchange
+    auto gu_round = [&](int task, bool first, int next) __attribute__((always_inline)) {
       const bool on = task < ntask_gu;
       if (on) {
         const int half = task & 1;
@@ -655,6 +658,7 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         for (int rr = 0; rr < 4; ++rr)
           if (4 * q + rr < T) s.red[wv][4 * q + rr][n16] = acc[rr];
       }
+      if (next < ntask_gu) load_gu(next);
       if (first && wv < ntask_d) load_d(d0);
       stamp(s, a, l, 13);
       __syncthreads();
@@ -679,12 +683,12 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
         }
       }
     };
-    gu_round(gu_task0, true);
+    constexpr int kGuStride = kFGrid * kFW;  // tasks per round
+    gu_round(gu_task0, true, nround_gu > 1 ? gu_task0 + kGuStride : ntask_gu);
     for (int r = 1; r < nround_gu; ++r) {
-      const int task = gu_task0 + r * kFGrid * kFW;
+      const int task = gu_task0 + r * kGuStride;
       __syncthreads();  // red is reused
-      if (task < ntask_gu) load_gu(task);
-      gu_round(task, false);
+      gu_round(task, false, r + 1 < nround_gu ? task + kGuStride : ntask_gu);
     }
     stamp(s, a, l, 6);
 
