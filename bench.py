@@ -189,7 +189,8 @@ def extra_single_layer(moe, fx, dev, stream, reps=100):
     over 4 replicas (830 MB > MALL).  Two entry points: the layer calls
     (moe_route + moe_expert_forward: FP16 x in, FP16 out) and a one-layer
     moe_stack_forward (the one-launch kernel: RMSNorm, the layer and the FP32
-    residual update).  Per-call median and p10/p90 of `reps` calls each."""
+    residual update, applied to the same residual call after call).  Per-call
+    median and p10/p90 of `reps` calls each."""
     import numpy as np
     import torch
     shape, T = fx.OLMOE, 4
@@ -213,9 +214,12 @@ def extra_single_layer(moe, fx, dev, stream, reps=100):
         ids, w = ctx.route(r, x, stream=stream)
         ctx.expert_forward(r, x, ids, w, out=out, stream=stream)
 
+    h.copy_(h0)
+
     def fused(i):
+        # the residual is updated in place from call to call (the timed region
+        # holds only the layer's launch; resetting it would add a copy kernel)
         r = i % N_REPLICAS
-        h.copy_(h0)
         ctx.stack_forward(h, layer_begin=r, layer_end=r + 1, stream=stream)
 
     res = {"tokens": T, "experts_touched_mean": used, "bytes_per_call": int(nbytes), "flops_per_call": flops}
