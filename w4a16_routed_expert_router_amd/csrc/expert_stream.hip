@@ -44,7 +44,13 @@ __device__ __forceinline__ uint32_t word_of(const u4& v, int w) {
 }
 
 constexpr int kSW = 8;          // waves per block
-constexpr int kRing = 3;        // weight units in flight per wave (deeper rings measured slower)
+// weight units per wave in the ring (one in use, the rest in flight): 4 for the
+// 2048- and 1024-wide K (3 to 4 measured 3 % faster, deeper rings slower); 3 for
+// K = 512, whose 4-slot ring the compiler built with a slot copied on the loop's
+// back edge while its load was in flight (tests/test_ring_asm.py checks every
+// instantiation)
+template <int K>
+constexpr int ring_units() { return K == 512 ? 3 : 4; }
 constexpr int kTok = 32;        // tokens per expert handled here (two sub-tiles of 16)
 constexpr int kPad = 8;         // LDS row padding (halves)
 constexpr int kMaxList = 1024;  // experts per call
@@ -130,6 +136,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   constexpr int kUnitLoads = 3;
   constexpr int SB = NG * 2;                   // scale bytes of one row
   static_assert(SB == 32 || SB == 16 || SB == 8, "rows of 8 to 32 bytes of scales");
+  constexpr int kRing = ring_units<K>();
   u4 bq[kRing][2];
   u4 bsv[kRing];  // scales of the unit's item (used from its first unit)
   auto load_unit = [&](int v, int slot_) __attribute__((always_inline)) {
