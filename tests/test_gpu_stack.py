@@ -83,8 +83,10 @@ def test_olmoe_stack_decode_teacher_forced(moe, fused):
     ctx.close()
 
 
-@pytest.mark.parametrize("T", [4, 8])
+@pytest.mark.parametrize("T", [2, 3, 4, 8])
 def test_olmoe_stack_batched_decode_fused(moe, T):
+    """2-4 tokens: the one-launch kernel (each token selected by a wave of its own);
+    8 tokens: the per-layer kernels."""
     say(f"test_olmoe_stack_batched_decode_fused T={T}")
     shape, L = fx.OLMOE, 16
     layers = stack_weights(shape, "stack-olmoe", L)
@@ -97,9 +99,9 @@ def test_olmoe_stack_batched_decode_fused(moe, T):
 @pytest.mark.parametrize("T", [1, 2, 4])
 def test_olmoe_stack_whole_call_equals_layer_by_layer(moe, T):
     """One launch over all layers gives the same bits as one launch per layer
-    (T = 1 takes the barrier-free one-token selection, T > 1 the block-wide
-    ranking); each per-layer launch is pinned to the oracle by the
-    teacher-forced tests."""
+    (T = 1 splits the one-token ranking over the block's waves, T > 1 gives each
+    token a wave of its own); each per-layer launch is pinned to the oracle by
+    the teacher-forced tests."""
     say(f"test_olmoe_stack_whole_call_equals_layer_by_layer T={T}")
     shape, L = fx.OLMOE, 16
     layers = stack_weights(shape, "stack-olmoe", L)
