@@ -258,22 +258,27 @@ inline uint32_t to_device_word(uint32_t c) {
 }
 
 // One expert's canonical (codes [3][cb], scales [3][sc]) -> device blob bytes.
-void repack_expert(const uint8_t* q, const uint16_t* s, int64_t cb, int64_t sc, uint8_t* dst) {
+// Canonical codes are row-major: gate and up [I][H/2], down [H][I/2]
+// (I = 2 * cb / H); on the device they go in blocks of 16 rows (code_offset).
+void repack_expert(const uint8_t* q, const uint16_t* s, int64_t cb, int64_t sc, int H, uint8_t* dst) {
+  const int I = (int)(2 * cb / H);
   for (int m = 0; m < 3; ++m) {
+    const int rows = m < 2 ? I : H, rb = m < 2 ? H / 2 : I / 2;
     const uint8_t* src = q + m * cb;
     uint8_t* d = dst + m * cb;
-    for (int64_t i = 0; i < cb; i += 4) {
-      uint32_t w;
-      memcpy(&w, src + i, 4);
-      w = to_device_word(w);
-      memcpy(d + i, &w, 4);
-    }
+    for (int r = 0; r < rows; ++r)
+      for (int b = 0; b < rb; b += 4) {
+        uint32_t w;
+        memcpy(&w, src + (int64_t)r * rb + b, 4);
+        w = to_device_word(w);
+        memcpy(d + code_offset(r, b, rb), &w, 4);
+      }
   }
   memcpy(dst + 3 * cb, s, 3 * sc * sizeof(uint16_t));
 }
 
 // Repack E experts with a few host threads.
-void repack_many(const uint8_t* q, const uint16_t* s, int n, int64_t cb, int64_t sc,
+void repack_many(const uint8_t* q, const uint16_t* s, int n, int64_t cb, int64_t sc, int H,
                  uint8_t* dst, int64_t blob) {
   unsigned nt = std::thread::hardware_concurrency();
   nt = nt == 0 ? 1 : (nt > 16 ? 16 : nt);
@@ -282,7 +287,7 @@ void repack_many(const uint8_t* q, const uint16_t* s, int n, int64_t cb, int64_t
   for (unsigned t = 0; t < nt; ++t)
     th.emplace_back([=] {
       for (int e = (int)t; e < n; e += (int)nt)
-        repack_expert(q + (int64_t)e * 3 * cb, s + (int64_t)e * 3 * sc, cb, sc, dst + e * blob);
+        repack_expert(q + (int64_t)e * 3 * cb, s + (int64_t)e * 3 * sc, cb, sc, H, dst + e * blob);
     });
   for (auto& x : th) x.join();
 }
@@ -896,7 +901,7 @@ moe_status moe_register_layer(moe_ctx* c, int32_t layer, const uint16_t* router,
   HIPCHK(c, hipMemcpy(L.router, router, (size_t)g.n_experts * g.hidden * 2, hipMemcpyHostToDevice));
   std::vector<int32_t> map(g.n_experts);
   if (pooled(c)) {
-    repack_many(q, s, g.n_experts, cb, sc, L.backing, blob);
+    repack_many(q, s, g.n_experts, cb, sc, g.hidden, L.backing, blob);
     for (int e = 0; e < g.n_experts; ++e) map[e] = -1;
     L.policy.reset(new PolicyEngine(g.policy, g.n_experts, g.slots_per_layer, layer));
     L.stats = moe_cache_counters{};
@@ -913,7 +918,7 @@ moe_status moe_register_layer(moe_ctx* c, int32_t layer, const uint16_t* router,
     hipError_t err = hipSuccess;
     for (int e0 = 0; e0 < g.n_experts && err == hipSuccess; e0 += chunk) {
       const int n = std::min(chunk, g.n_experts - e0);
-      repack_many(q + (int64_t)e0 * 3 * cb, s + (int64_t)e0 * 3 * sc, n, cb, sc, stage, blob);
+      repack_many(q + (int64_t)e0 * 3 * cb, s + (int64_t)e0 * 3 * sc, n, cb, sc, g.hidden, stage, blob);
       err = hipMemcpy(L.store + (int64_t)e0 * blob, stage, (size_t)n * blob, hipMemcpyHostToDevice);
     }
     (void)hipHostFree(stage);
@@ -924,7 +929,7 @@ moe_status moe_register_layer(moe_ctx* c, int32_t layer, const uint16_t* router,
   if (g.shared_inter) {
     const int64_t scb = c->shared_lay.code_bytes, ssc = c->shared_lay.scale_bytes / 2;
     std::vector<uint8_t> tmp((size_t)c->shared_lay.total());
-    repack_expert(shared_q, shared_s, scb, ssc, tmp.data());
+    repack_expert(shared_q, shared_s, scb, ssc, g.hidden, tmp.data());
     HIPCHK(c, hipMemcpy(L.shared, tmp.data(), tmp.size(), hipMemcpyHostToDevice));
   }
   // full residency: slot = expert, the fused path skips the map lookup

@@ -29,6 +29,19 @@ struct ActiveExpert {
 // Byte offsets of the parts of one expert blob in HBM (device layout):
 //   [gate codes I*H/2][up codes I*H/2][down codes H*I/2]
 //   [gate scales I*H/128 fp16][up scales][down scales]
+// Scales are row-major.  Codes come in blocks of 16 rows; inside a block the
+// 64 bytes of scale group g of row n sit at g * 1024 + n * 64, so the 16 rows'
+// bytes of one group (what one MFMA B fragment load of a wave takes) are one
+// contiguous 1 KiB run, and a row block's groups follow one another.
+constexpr int kCodeRowBlock = 16;
+constexpr int kCodeGroupBytes = kGroup / 2;                            // 64
+constexpr int kCodeGroupStride = kCodeRowBlock * kCodeGroupBytes;      // 1024
+// Offset of byte `b` of row `row`'s codes in a matrix with `row_bytes` (= K/2)
+// code bytes per row.
+__host__ __device__ __forceinline__ int64_t code_offset(int row, int b, int row_bytes) {
+  return (int64_t)(row / kCodeRowBlock) * kCodeRowBlock * row_bytes + (b / kCodeGroupBytes) * kCodeGroupStride +
+         (row % kCodeRowBlock) * kCodeGroupBytes + (b % kCodeGroupBytes);
+}
 struct BlobLayout {
   int64_t code_bytes;   // one matrix
   int64_t scale_bytes;  // one matrix

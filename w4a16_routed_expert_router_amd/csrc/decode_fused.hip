@@ -586,10 +586,10 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
       const uint8_t* blob = unit_blob(u);
       const int mat = n16 >> 3;  // columns 0-7 gate rows, 8-15 up rows
       const int row = i0 + (n16 & 7);
-      const uint8_t* cp = blob + a.lay.codes(mat) + (int64_t)row * (H / 2) + half * (H / 4) + q * 16;
+      const uint8_t* cp = blob + a.lay.codes(mat) + code_offset(row, half * (H / 4) + q * 16, H / 2);
       const uint16_t* sp = reinterpret_cast<const uint16_t*>(blob + a.lay.scales(mat)) + (int64_t)row * (H / 128) + half * GH;
 #pragma unroll
-      for (int g2 = 0; g2 < GH; ++g2) gq[g2] = ldg_u4(cp + g2 * 64);
+      for (int g2 = 0; g2 < GH; ++g2) gq[g2] = ldg_u4(cp + g2 * kCodeGroupStride);
       // one 16-byte load for the scales: 2-byte loads cost the address unit
       // about as much per instruction as a whole 16-byte-per-lane load
       gs = ldg_u4(sp);
@@ -606,13 +606,13 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
       const int u = min(cg * 2 + (n16 >> 3), UU - 1);  // a dead column re-reads a live row
       const uint8_t* blob = unit_blob(u);
       const int row = r0 + (n16 & 7);
-      return DPtr{blob + a.lay.codes(2) + (int64_t)row * (I / 2) + kp * (I / 2 / ks) + q * 16,
+      return DPtr{blob + a.lay.codes(2) + code_offset(row, kp * (I / 2 / ks) + q * 16, I / 2),
                   reinterpret_cast<const uint16_t*>(blob + a.lay.scales(2)) + (int64_t)row * GDM + kp * ngd + 2 * q};
     };
     auto load_d = [&](const DPtr& d) {
 #pragma unroll
       for (int g2 = 0; g2 < GDM; ++g2)
-        if (g2 < ngd) dma_lds16(d.cp + g2 * 64, lds_addr(&s.dpre[wv][g2][0]));
+        if (g2 < ngd) dma_lds16(d.cp + g2 * kCodeGroupStride, lds_addr(&s.dpre[wv][g2][0]));
       // lane (n, q) fetches the scales of groups 2q, 2q+1 of column n
       if (2 * q < ngd) dma_lds4(d.sp, lds_addr(&s.dsc[wv][0]));
     };

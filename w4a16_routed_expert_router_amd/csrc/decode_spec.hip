@@ -431,10 +431,10 @@ __global__ __launch_bounds__(kFT) void spec_decode_kernel(FusedArgs a) {
         const uint8_t* blob = blob_of(LL, e);
         const int mat = n16 >> 3;  // columns 0-7 gate rows, 8-15 up rows
         const int row = i0 + (n16 & 7);
-        const uint8_t* cp = blob + a.lay.codes(mat) + (int64_t)row * (H / 2) + q * 16;
+        const uint8_t* cp = blob + a.lay.codes(mat) + code_offset(row, q * 16, H / 2);
         const uint16_t* sp = reinterpret_cast<const uint16_t*>(blob + a.lay.scales(mat)) + (int64_t)row * (H / 128) + 2 * q;
 #pragma unroll 1
-        for (int g = 0; g < GK; ++g) dma_lds16(cp + g * 64, lds_addr(&s.gw[mw][g][0]));
+        for (int g = 0; g < GK; ++g) dma_lds16(cp + g * kCodeGroupStride, lds_addr(&s.gw[mw][g][0]));
         dma_lds4(sp, lds_addr(&s.gsc[mw][0][0]));
         dma_lds4(sp + GK / 2, lds_addr(&s.gsc[mw][1][0]));
       };
@@ -443,13 +443,13 @@ __global__ __launch_bounds__(kFT) void spec_decode_kernel(FusedArgs a) {
         const int cg = slot / ks, kp = slot - cg * ks;
         const uint8_t* blob = blob_of(LL, (n16 >> 3) ? e1 : e0);
         const int row = r0 + (n16 & 7);
-        const uint8_t* cp = blob + a.lay.codes(2) + (int64_t)row * (I / 2) + kp * (I / 2 / ks) + q * 16;
+        const uint8_t* cp = blob + a.lay.codes(2) + code_offset(row, kp * (I / 2 / ks) + q * 16, I / 2);
         // lanes with 2q >= ngd have no scales of their own: they re-read lane
         // group 0's (never used), which keeps every read inside the row
         const int qs = 2 * q < ngd ? q : 0;
         const uint16_t* sp = reinterpret_cast<const uint16_t*>(blob + a.lay.scales(2)) + (int64_t)row * GDM + kp * ngd + 2 * qs;
 #pragma unroll 1
-        for (int g2 = 0; g2 < ngd; ++g2) dma_lds16(cp + g2 * 64, lds_addr(&s.dw[slot][g2][0]));
+        for (int g2 = 0; g2 < ngd; ++g2) dma_lds16(cp + g2 * kCodeGroupStride, lds_addr(&s.dw[slot][g2][0]));
         dma_lds4(sp, lds_addr(&s.dsc[slot][0]));
       };
       // expert pair of down slot `slot` for unit experts ue(u), as one key

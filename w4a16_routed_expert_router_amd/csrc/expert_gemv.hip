@@ -81,9 +81,9 @@ __global__ __launch_bounds__(256) void gateup_gemv_kernel(ExpertArgs a) {
   const int kc = lane % CPR;
   const int rsub = lane / CPR;
   const int row0 = tile * RT;
-  const int64_t row_bytes = H / 2;
-  const uint8_t* gc = blob + a.lay.codes(0) + row0 * row_bytes;
-  const uint8_t* uc = blob + a.lay.codes(1) + row0 * row_bytes;
+  const int row_bytes = H / 2;
+  const uint8_t* gc = blob + a.lay.codes(0);
+  const uint8_t* uc = blob + a.lay.codes(1);
   const uint16_t* gs = reinterpret_cast<const uint16_t*>(blob + a.lay.scales(0));
   const uint16_t* us = reinterpret_cast<const uint16_t*>(blob + a.lay.scales(1));
   const int ngroups = H / kGroup;
@@ -92,9 +92,9 @@ __global__ __launch_bounds__(256) void gateup_gemv_kernel(ExpertArgs a) {
   float gsc[kLoads], usc[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
-    gq[i] = *reinterpret_cast<const uint4*>(gc + (int64_t)(i * kWave + lane) * 16);
-    uq[i] = *reinterpret_cast<const uint4*>(uc + (int64_t)(i * kWave + lane) * 16);
     const int r = row0 + i * RPL + rsub;
+    gq[i] = *reinterpret_cast<const uint4*>(gc + code_offset(r, kc * 16, row_bytes));
+    uq[i] = *reinterpret_cast<const uint4*>(uc + code_offset(r, kc * 16, row_bytes));
     gsc[i] = half_bits_to_float(gs[(int64_t)r * ngroups + (kc >> 2)]);
     usc[i] = half_bits_to_float(us[(int64_t)r * ngroups + (kc >> 2)]);
   }
@@ -148,8 +148,8 @@ __global__ __launch_bounds__(256) void down_gemv_kernel(ExpertArgs a) {
   const int kc = lane % CPR;
   const int rsub = lane / CPR;
   const int row0 = tile * RT;
-  const int64_t row_bytes = I / 2;
-  const uint8_t* dc = blob + a.lay.codes(2) + row0 * row_bytes;
+  const int row_bytes = I / 2;
+  const uint8_t* dc = blob + a.lay.codes(2);
   const uint16_t* ds = reinterpret_cast<const uint16_t*>(blob + a.lay.scales(2));
   const int ngroups = I / kGroup;
 
@@ -157,8 +157,8 @@ __global__ __launch_bounds__(256) void down_gemv_kernel(ExpertArgs a) {
   float dsc[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
-    dq[i] = *reinterpret_cast<const uint4*>(dc + (int64_t)(i * kWave + lane) * 16);
     const int r = row0 + i * RPL + rsub;
+    dq[i] = *reinterpret_cast<const uint4*>(dc + code_offset(r, kc * 16, row_bytes));
     dsc[i] = half_bits_to_float(ds[(int64_t)r * ngroups + (kc >> 2)]);
   }
   h2 dw[kLoads][16];

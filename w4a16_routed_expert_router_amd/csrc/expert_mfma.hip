@@ -122,15 +122,15 @@ struct WaveTiles {
       const int mat = MODE == 0 ? (j & 1) : 2;
       const int r0 = base + 16 * (MODE == 0 ? (j >> 1) : j);
       row[j] = r0 + n;
-      code[j] = wave_uniform(blob + a.lay.codes(mat) + (int64_t)r0 * (K / 2));
+      code[j] = wave_uniform(blob + a.lay.codes(mat) + code_offset(r0, 0, K / 2));  // r0 % 16 == 0
       scale[j] = wave_uniform(blob + a.lay.scales(mat) + (int64_t)r0 * ng * 2);
     }
-    lane_code = (uint32_t)(n * (K / 2) + q * 16);
+    lane_code = (uint32_t)(n * kCodeGroupBytes + q * 16);
     lane_scale = (uint32_t)(n * ng * 2);
   }
   // global (not flat) loads: flat loads would also hold up every LDS wait
   __device__ __forceinline__ u4 codes(int j, int g) const {
-    return ldg<u4>(code[j] + (lane_code + (uint32_t)g * 64u));
+    return ldg<u4>(code[j] + (lane_code + (uint32_t)(g * kCodeGroupStride)));
   }
   __device__ __forceinline__ uint32_t scale_of(int j, int g) const {
     return ldg<uint16_t>(scale[j] + (lane_scale + (uint32_t)g * 2u));

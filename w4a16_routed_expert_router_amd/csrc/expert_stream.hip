@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
     for (int j = 0; j < 2; ++j) {
       const int mat = MODE == 0 ? j : 2;
       const int r = MODE == 0 ? nt * ROWS + wv * 16 + n : nt * ROWS + wv * 32 + j * 16 + n;
-      const uint8_t* cp = blob + a.lay.codes(mat) + (int64_t)r * (K / 2) + q * 16 + g * 64;
+      const uint8_t* cp = blob + a.lay.codes(mat) + code_offset(r, g * kCodeGroupBytes + q * 16, K / 2);
       asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(bq[slot_][j]) : "v"(cp) : "memory");
     }
     // lane (n, q) holds the 16-byte aligned chunk of scales [8 (q & 1), +8)
