@@ -305,6 +305,33 @@ def test_layer_crowded_experts_stream(moe, olmoe_layer):
     ctx.close()
 
 
+@pytest.mark.parametrize("case", ["ids_in_global", "masks_beyond_lds"])
+def test_grouping_general_kernel_equals_one_pass(moe, case):
+    """Batches too large for the one-pass grouping (more pairs than fit in LDS,
+    or more (64-token chunk, expert) masks than fit) take the general grouping
+    kernel.  A token's expert outputs do not depend on the other tokens of its
+    tile, so the whole batch must equal its two halves (each grouped in one
+    pass) bit for bit, on the grouped GEMM for both."""
+    say(f"test_grouping_general_kernel_equals_one_pass {case}")
+    if case == "ids_in_global":
+        shape, T = SMALL, 4200  # 16,800 pairs
+    else:
+        shape, T = fx.MoEShape(hidden=256, n_experts=512, inter=256, top_k=8, renorm=False), 1024  # 16 x 512 masks
+    wts = gpu_layer(shape, "gpu-group-general", 0)
+    ctx = moe.MoEContext(shape, n_layers=1, max_tokens=T, flags=moe.MOE_FLAG_FORCE_MFMA)
+    ctx.register_layer(0, wts)
+    xg = to_gpu(fx.activations(("group-general", case), T, shape.hidden).numpy())
+    ids, w = ctx.route(0, xg)
+    whole = ctx.expert_forward(0, xg, ids, w).clone()
+    h = T // 2
+    first = ctx.expert_forward(0, xg[:h].contiguous(), ids[:h].contiguous(), w[:h].contiguous()).clone()
+    second = ctx.expert_forward(0, xg[h:].contiguous(), ids[h:].contiguous(), w[h:].contiguous()).clone()
+    torch.cuda.synchronize()
+    assert ctx.check_device_errors() == 0
+    assert torch.equal(whole, torch.cat([first, second]))
+    ctx.close()
+
+
 @pytest.mark.parametrize("T", [17, 32])
 def test_layer_shared_expert_two_subtiles(moe, T):
     """A shared expert that sees every token of a 17- or 32-token batch runs

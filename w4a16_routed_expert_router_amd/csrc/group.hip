@@ -51,6 +51,140 @@ __device__ void block_exclusive_scan(const int (&v)[N], int (&excl)[N], int (&to
   __syncthreads();
 }
 
+// Validates the k ids of token t: an id out of range or repeated within the
+// token flags the call (errbits) and the token gets ids 0..k-1 (valid and
+// distinct) instead.
+__device__ __forceinline__ void validate_token(const int (&rv)[kMaxK], int k, int E, int (&out)[kMaxK],
+                                               uint32_t& errbits) {
+  bool bad = false, dup = false;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      bad |= rv[j] < 0 || rv[j] >= E;
+#pragma unroll
+      for (int jj = 0; jj < j; ++jj) dup |= rv[jj] == rv[j];
+    }
+  }
+  if (bad) errbits |= kErrBadId;
+  if (dup) errbits |= kErrDupId;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) out[j] = (bad || dup) ? j : rv[j];
+}
+
+// The call's plan from the per-expert token counts (c of thread e < E):
+// positions of each expert's first pair (ascending expert id), the active
+// list, the MFMA token-tile offsets and the few-token kernel's list.  Every
+// thread of the block calls it (barriers inside); base[e] is set on return.
+struct ListPlan {
+  int c, slot, off, moff, mtotal, act, nact, sidx, nsmall, nchunk;
+};
+__device__ ListPlan plan_lists(const GroupArgs& a, int c, int slot_pre, int* base, int (*sh_warp)[16], int* sh_tot) {
+  const int tid = threadIdx.x, E = a.E;
+  ListPlan L;
+  L.c = c;
+  const int mtiles = c >= a.mfma_min ? (c + kMfmaTileTokens - 1) / kMfmaTileTokens : 0;
+  // entries of the few-token kernel's list: one for an expert with at most
+  // kStreamTokens tokens below the MFMA threshold, or (chunk_all) one per
+  // chunk of kStreamTokens tokens of every active expert
+  L.nchunk = a.chunk_all ? (c + kStreamTokens - 1) / kStreamTokens
+                         : (c > 0 && c <= kStreamTokens && c < a.mfma_min ? 1 : 0);
+  const int sv[4] = {c, mtiles, c > 0 ? 1 : 0, L.nchunk};
+  int sx[4], st[4];
+  block_exclusive_scan<4>(sv, sx, st, sh_warp, sh_tot);
+  L.off = sx[0];
+  L.moff = sx[1];
+  L.mtotal = st[1];
+  L.act = sx[2];
+  L.nact = st[2];
+  L.sidx = sx[3];
+  L.nsmall = st[3];
+  L.slot = 0;
+  if (tid < E) {
+    base[tid] = L.off;
+    if (c > 0) {
+      L.slot = slot_pre;
+      if (L.slot < 0) {
+        atomic_or_err(a.err, kErrNotResident);
+        L.slot = 0;
+      }
+    }
+  }
+  return L;
+}
+
+// The plan's global lists (thread e writes expert e's entries).
+__device__ void store_lists(const GroupArgs& a, const ListPlan& L) {
+  const int tid = threadIdx.x;
+  if (L.c > 0) {
+    a.mtile_off[L.act] = L.moff;
+    a.active[L.act] = ActiveExpert{tid, L.slot, L.c, L.off};
+  }
+  for (int i = 0; i < L.nchunk; ++i)
+    a.small[L.sidx + i] =
+        ActiveExpert{tid, L.slot, min(kStreamTokens, L.c - i * kStreamTokens), L.off + i * kStreamTokens};
+  if (tid == 0) {
+    a.mtile_off[L.nact] = L.mtotal;
+    *a.n_active = L.nact;
+    *a.n_small = L.nsmall;
+  }
+}
+
+// One pass over the pairs, for calls whose (64-token chunk, expert) bit masks
+// and validated ids fit in LDS.  Each thread validates whole tokens as their
+// ids arrive and sets the token's bit in the mask of each of its experts; an
+// expert's count and its pairs in earlier chunks then come from one walk over
+// its masks, and a pair's position is its expert's base + the expert's pairs
+// in earlier chunks + the expert's earlier tokens in the pair's own chunk.
+constexpr int kOnePassMaskWords = 4096;
+__global__ __launch_bounds__(kGroupThreads) void group_onepass_kernel(GroupArgs a) {
+  __shared__ unsigned long long mask[kOnePassMaskWords];  // [chunk][expert]
+  __shared__ int cum[kOnePassMaskWords];                  // [chunk][expert]: pairs in earlier chunks
+  __shared__ int base[kMaxExperts];
+  __shared__ int sh_warp[4][16];
+  __shared__ int sh_tot[4];
+  __shared__ int16_t sid[kLdsPairs];  // validated ids by pair
+  const int tid = threadIdx.x;
+  const int T = a.T, k = a.k, E = a.E;
+  const int P = T * k, NC = (T + kChunk - 1) / kChunk;
+  // the slot map is loaded first: its latency overlaps everything up to the lists
+  const int slot_pre = tid < E && a.slot_map ? a.slot_map[tid] : tid;
+  for (int i = tid; i < NC * E; i += kGroupThreads) mask[i] = 0ull;
+  __syncthreads();
+  uint32_t errbits = 0;
+  for (int t = tid; t < T; t += kGroupThreads) {
+    int rv[kMaxK], v[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) rv[j] = j < k ? a.ids_in[(int64_t)t * k + j] : -1;
+    validate_token(rv, k, E, v, errbits);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k) break;
+      sid[t * k + j] = (int16_t)v[j];
+      atomicOr(&mask[(t / kChunk) * E + v[j]], 1ull << (t % kChunk));
+    }
+  }
+  if (errbits) atomic_or_err(a.err, errbits);
+  __syncthreads();
+  int c = 0;
+  if (tid < E)
+    for (int ch = 0; ch < NC; ++ch) {
+      cum[ch * E + tid] = c;
+      c += __popcll(mask[ch * E + tid]);
+    }
+  const ListPlan L = plan_lists(a, c, slot_pre, base, sh_warp, sh_tot);
+  __syncthreads();
+  for (int p = tid; p < P; p += kGroupThreads) {
+    const int t = p / k, e = sid[p];
+    const int ch = t / kChunk, tl = t % kChunk;
+    const int pos = base[e] + cum[ch * E + e] + __popcll(mask[ch * E + e] & ((1ull << tl) - 1ull));
+    a.perm_tok[pos] = t;
+    a.pos_of[p] = pos;
+  }
+  store_lists(a, L);
+}
+
+// General form (any T and E): ids stay in LDS up to kLdsPairs pairs, else in
+// the global scratch, and the placement runs in rounds of chunks.
 // One block of 1024 threads.
 __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
   __shared__ int cnt[kMaxExperts];
@@ -84,29 +218,18 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
   // validate each token's ids; a bad token gets ids 0..k-1 (valid, distinct)
   uint32_t errbits = 0;
   for (int t = tid; t < T; t += kGroupThreads) {
-    int rv[kMaxK];
+    int rv[kMaxK], v[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
       rv[j] = j < k ? (lds_ids ? (int)sid[t * k + j] : a.ids_in[(int64_t)t * k + j]) : -1;
-    bool bad = false, dup = false;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < k) {
-        bad |= rv[j] < 0 || rv[j] >= E;
-#pragma unroll
-        for (int jj = 0; jj < j; ++jj) dup |= rv[jj] == rv[j];
-      }
-    }
-    if (bad) errbits |= kErrBadId;
-    if (dup) errbits |= kErrDupId;
+    validate_token(rv, k, E, v, errbits);
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
       if (j >= k) break;
-      const int v = (bad || dup) ? j : rv[j];
       if (lds_ids)
-        sid[t * k + j] = (int16_t)v;
+        sid[t * k + j] = (int16_t)v[j];
       else
-        a.ids_s[(int64_t)t * k + j] = v;
+        a.ids_s[(int64_t)t * k + j] = v[j];
     }
   }
   if (errbits) atomic_or_err(a.err, errbits);
@@ -116,28 +239,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
 
   // offsets and the active list (ascending expert id); E <= 1024 = one per thread
   const int c = (tid < E) ? cnt[tid] : 0;
-  const int mtiles = c >= a.mfma_min ? (c + kMfmaTileTokens - 1) / kMfmaTileTokens : 0;
-  // entries of the few-token kernel's list: one for an expert with at most
-  // kStreamTokens tokens below the MFMA threshold, or (chunk_all) one per
-  // chunk of kStreamTokens tokens of every active expert
-  const int nchunk = a.chunk_all ? (c + kStreamTokens - 1) / kStreamTokens
-                                 : (c > 0 && c <= kStreamTokens && c < a.mfma_min ? 1 : 0);
-  const int sv[4] = {c, mtiles, c > 0 ? 1 : 0, nchunk};
-  int sx[4], st[4];
-  block_exclusive_scan<4>(sv, sx, st, sh_warp, sh_tot);
-  const int off = sx[0], moff = sx[1], mtotal = st[1], act = sx[2], nact = st[2];
-  const int sidx = sx[3], nsmall = st[3];
-  int slot = 0;
-  if (tid < E) {
-    base[tid] = off;
-    if (c > 0) {
-      slot = a.slot_map ? a.slot_map[tid] : tid;
-      if (slot < 0) {
-        atomic_or_err(a.err, kErrNotResident);
-        slot = 0;
-      }
-    }
-  }
+  const ListPlan L = plan_lists(a, c, tid < E && a.slot_map ? a.slot_map[tid] : tid, base, sh_warp, sh_tot);
   for (int i = tid; i < kRounds * kMaxExperts; i += kGroupThreads) (&mask[0][0])[i] = 0ull;
   __syncthreads();
 
@@ -189,21 +291,15 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
       a.pos_of[p] = spos[p];
     }
   }
-  if (c > 0) {
-    a.mtile_off[act] = moff;
-    a.active[act] = ActiveExpert{tid, slot, c, off};
-  }
-  for (int i = 0; i < nchunk; ++i)
-    a.small[sidx + i] = ActiveExpert{tid, slot, min(kStreamTokens, c - i * kStreamTokens), off + i * kStreamTokens};
-  if (tid == 0) {
-    a.mtile_off[nact] = mtotal;
-    *a.n_active = nact;
-    *a.n_small = nsmall;
-  }
+  store_lists(a, L);
 }
 
 void launch_group(const GroupArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), 0, stream, a);
+  const int64_t nc = (a.T + kChunk - 1) / kChunk;
+  if ((int64_t)a.T * a.k <= kLdsPairs && nc * a.E <= kOnePassMaskWords)
+    hipLaunchKernelGGL(group_onepass_kernel, dim3(1), dim3(kGroupThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), 0, stream, a);
 }
 
 }  // namespace moe
