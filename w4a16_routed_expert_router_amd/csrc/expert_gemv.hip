@@ -212,35 +212,50 @@ void launch_down_gemv(const ExpertArgs& a, hipStream_t stream) {
 
 // out[t] = sum_j w[t,j] * y[pos_of[t,j]] (+ yshared[t]), summed in rank order
 // in FP32.  grid (ceil(H/1024), T), block 256, 4 columns per thread.
+constexpr int kCombineMaxK = 16;  // largest top-k a context accepts
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.y;
   const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (n >= a.H) return;
+  // every independent load first: the pairs' positions and weights, the
+  // shared expert's row and the residual, then the k expert rows; the sum
+  // runs in rank order afterwards
+  int p[kCombineMaxK];
+  float wj[kCombineMaxK];
+#pragma unroll
+  for (int j = 0; j < kCombineMaxK; ++j)
+    if (j < a.k) {
+      p[j] = a.pos_of[(int64_t)t * a.k + j];
+      wj[j] = a.w[(int64_t)t * a.k + j];
+    }
+  float4 ys = make_float4(0.f, 0.f, 0.f, 0.f), rv = ys;
+  if (a.yshared) ys = *reinterpret_cast<const float4*>(a.yshared + (int64_t)t * a.H + n);
+  if (a.resid) rv = *reinterpret_cast<const float4*>(a.resid + (int64_t)t * a.H + n);
+  float4 y[kCombineMaxK];
+#pragma unroll
+  for (int j = 0; j < kCombineMaxK; ++j)
+    if (j < a.k) y[j] = *reinterpret_cast<const float4*>(a.ybuf + (int64_t)p[j] * a.H + n);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < a.k; ++j) {
-    const int p = a.pos_of[(int64_t)t * a.k + j];
-    const float wj = a.w[(int64_t)t * a.k + j];
-    const float4 y = *reinterpret_cast<const float4*>(a.ybuf + (int64_t)p * a.H + n);
-    acc.x += wj * y.x;
-    acc.y += wj * y.y;
-    acc.z += wj * y.z;
-    acc.w += wj * y.w;
-  }
+#pragma unroll
+  for (int j = 0; j < kCombineMaxK; ++j)
+    if (j < a.k) {
+      acc.x += wj[j] * y[j].x;
+      acc.y += wj[j] * y[j].y;
+      acc.z += wj[j] * y[j].z;
+      acc.w += wj[j] * y[j].w;
+    }
   if (a.yshared) {
-    const float4 y = *reinterpret_cast<const float4*>(a.yshared + (int64_t)t * a.H + n);
-    acc.x += y.x;
-    acc.y += y.y;
-    acc.z += y.z;
-    acc.w += y.w;
+    acc.x += ys.x;
+    acc.y += ys.y;
+    acc.z += ys.z;
+    acc.w += ys.w;
   }
   if (a.resid) {
-    float4* r = reinterpret_cast<float4*>(a.resid + (int64_t)t * a.H + n);
-    float4 v = *r;
-    v.x += acc.x;
-    v.y += acc.y;
-    v.z += acc.z;
-    v.w += acc.w;
-    *r = v;
+    rv.x += acc.x;
+    rv.y += acc.y;
+    rv.z += acc.z;
+    rv.w += acc.w;
+    *reinterpret_cast<float4*>(a.resid + (int64_t)t * a.H + n) = rv;
   } else {
     _Float16* o = reinterpret_cast<_Float16*>(a.out) + (int64_t)t * a.H + n;
     o[0] = (_Float16)acc.x;
@@ -255,21 +270,29 @@ void launch_combine(const CombineArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, a);
 }
 
-// x[t] = fp16(h[t] / sqrt(mean(h[t]^2) + eps)); grid T, block 256.
+// x[t] = fp16(h[t] / sqrt(mean(h[t]^2) + eps)); grid T, block 256, H <= 2048.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h, int H, float eps,
                                                       uint16_t* __restrict__ x) {
+  constexpr int kPer = 8;  // H <= 2048: at most 8 values per thread, held in registers
   __shared__ float part[4];
   const int t = blockIdx.x;
   const float* row = h + (int64_t)t * H;
+  float v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) v[j] = threadIdx.x + 256 * j < H ? row[threadIdx.x + 256 * j] : 0.0f;
   float ss = 0.0f;
-  for (int i = threadIdx.x; i < H; i += 256) ss += row[i] * row[i];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (threadIdx.x + 256 * j < H) ss += v[j] * v[j];
   ss = wave_sum_xor(ss, kWave);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float tot = (part[0] + part[1]) + (part[2] + part[3]);
   const float r = 1.0f / sqrtf(tot / (float)H + eps);
   _Float16* xo = reinterpret_cast<_Float16*>(x) + (int64_t)t * H;
-  for (int i = threadIdx.x; i < H; i += 256) xo[i] = (_Float16)(row[i] * r);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (threadIdx.x + 256 * j < H) xo[threadIdx.x + 256 * j] = (_Float16)(v[j] * r);
 }
 
 void launch_rmsnorm(const float* h, int T, int H, float eps, uint16_t* x, hipStream_t stream) {

@@ -9,6 +9,9 @@
 //   * one block per compute unit takes a contiguous run of work items
 //     (expert, tile of output rows), so consecutive items are mostly row tiles
 //     of the same expert and its activation tile stays in LDS;
+//   * at K = 2048 and 512 an item's scale groups are split between two waves
+//     on the same rows, which add their sums in LDS at the item's end (items
+//     of half the rows divide more evenly over the blocks; k_halves);
 //   * every wave streams "units" (one 128-wide scale group of its two 16-row
 //     weight sub-tiles, 2 KiB) through a ring of kRing units in registers; the
 //     ring runs across item boundaries, so the weight stream never drains
@@ -54,6 +57,17 @@ constexpr int ring_units() { return K == 512 ? 3 : 4; }
 constexpr int kTok = 32;        // tokens per expert handled here (two sub-tiles of 16)
 constexpr int kPad = 8;         // LDS row padding (halves)
 constexpr int kMaxList = 1024;  // experts per call
+// K halves per item.  With 2, waves w and w + kSW / 2 take the same rows of
+// an item, each one half of its scale groups, and add their sums in LDS at the
+// item's end: an item is half as many rows, so that the items of a call
+// divide more evenly over the blocks (the Qwen3-Next-like batch of 16 has 140
+// experts x 4 items of 128 gate/up rows for 256 blocks: 3 items on the busiest
+// block against 2.2 on average; with 64-row items 5 against 4.4; measured
+// gate/up 45.6 -> 41.5 us, down at K = 512 25.8 -> 24.8 us).  The down
+// projection at K = 1024 keeps whole rows per wave: the OLMoE-shaped batch of
+// 64 already divides evenly, and there the split measured 21.4 -> 22.9 us.
+template <int K>
+constexpr int k_halves() { return K == 1024 ? 1 : 2; }
 
 // 8 INT4 codes -> (q - 8) as FP16 (exact); the group scale is applied to the
 // FP32 MFMA result of the group instead (one FMA per output, fewer VALU
@@ -70,6 +84,7 @@ __device__ __forceinline__ h8 decode_unscaled(uint32_t d, uint32_t mlo, uint32_t
 template <int K>
 struct StreamSmem {
   alignas(16) _Float16 a[kTok * (K + kPad)];  // activation tile of the current expert
+  f4 red[k_halves<K>() == 2 ? kSW / 2 : 1][4][kWave];  // second K half's sums: [row wave][sub-tile pair][lane]
   int slot[kMaxList];             // small experts of the call: blob slot, count, offset
   int count[kMaxList];
   int offset[kMaxList];
@@ -87,9 +102,13 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   __shared__ StreamSmem<K> s;
   constexpr int LD = K + kPad;
   constexpr int NG = K / kGroup;
-  constexpr int ROWS = MODE == 0 ? kSW * 16 : kSW * 32;
-  static_assert(NG % 2 == 0 || NG == 1, "scale groups per row");
+  constexpr int KS = k_halves<K>();
+  constexpr int RW = kSW / KS;  // waves per K half
+  constexpr int ROWS = MODE == 0 ? RW * 16 : RW * 32;
+  constexpr int NGW = NG / KS;  // scale groups of a wave per item
+  static_assert(NG % KS == 0, "scale groups per K half");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wr = wv % RW, kh = wv / RW;  // row wave, K half
   const int n = lane & 15, q = lane >> 4;
   const int N = MODE == 0 ? a.I : a.H;
   const int ntn = N / ROWS;
@@ -106,7 +125,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   const int lo = blockIdx.x * per;
   const int hi = min(items, lo + per);
   if (lo >= hi) return;  // uniform over the block
-  const int nv = (hi - lo) * NG;  // units of every wave
+  const int nv = (hi - lo) * NGW;  // units of every wave
   const int se0 = lo / ntn;       // first expert of the block (list index)
   if (tid <= (hi - 1) / ntn - se0) {
     if (a.fixed_blob) {
@@ -125,7 +144,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
     }
   }
 
-  // ---- weight stream: unit v = (item lo + v / NG, scale group v % NG)
+  // ---- weight stream: unit v = (item lo + v / NGW, scale group kh * NGW + v % NGW)
   // The unit loads are issued as inline assembly and waited for explicitly:
   // every unit issues exactly kUnitLoads loads (its two code loads and the
   // scale load of its item; the tail re-reads the last unit), so the loads
@@ -140,7 +159,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   u4 bq[kRing][2];
   u4 bsv[kRing];  // scales of the unit's item (used from its first unit)
   auto load_unit = [&](int v, int slot_) __attribute__((always_inline)) {
-    const int it = lo + v / NG, g = v - (v / NG) * NG;
+    const int it = lo + v / NGW, g = kh * NGW + (v - (v / NGW) * NGW);
     const int se = it / ntn, nt = it - se * ntn;
     const int sl = s.slot[se - se0];
     const uint8_t* blob = a.fixed_blob ? a.fixed_blob
@@ -149,7 +168,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int mat = MODE == 0 ? j : 2;
-      const int r = MODE == 0 ? nt * ROWS + wv * 16 + n : nt * ROWS + wv * 32 + j * 16 + n;
+      const int r = MODE == 0 ? nt * ROWS + wr * 16 + n : nt * ROWS + wr * 32 + j * 16 + n;
       const uint8_t* cp = blob + a.lay.codes(mat) + code_offset(r, g * kCodeGroupBytes + q * 16, K / 2);
       asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(bq[slot_][j]) : "v"(cp) : "memory");
     }
@@ -163,7 +182,7 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
     // in flight.)
     const int j = q >> 1;
     const int mat = MODE == 0 ? j : 2;
-    const int r = MODE == 0 ? nt * ROWS + wv * 16 + n : nt * ROWS + wv * 32 + j * 16 + n;
+    const int r = MODE == 0 ? nt * ROWS + wr * 16 + n : nt * ROWS + wr * 32 + j * 16 + n;
     const int h = SB == 32 ? (q & 1) : 0;
     const uint8_t* sp = blob + a.lay.scales(mat) + (((int64_t)r * SB) & ~(int64_t)15) + h * 16;
     asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(bsv[slot_]) : "v"(sp) : "memory");
@@ -241,13 +260,13 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
     constexpr int U = decltype(uc)::value;
     const bool live = v < nv;  // uniform
     const int vl = live ? v : nv - 1;
-    const int it = lo + vl / NG, g = vl - (vl / NG) * NG;
+    const int it = lo + vl / NGW, gi = vl - (vl / NGW) * NGW, g = kh * NGW + gi;
     const int se = it / ntn;
-    if (live && g == 0 && se != cur) load_tile(se);  // uniform: same v sequence in every wave
+    if (live && gi == 0 && se != cur) load_tile(se);  // uniform: same v sequence in every wave
     load_unit(min(v + kRing - 1, nv - 1), (U + kRing - 1) % kRing);
     wait_unit(U);
     if (!live) return;
-    if (g == 0) cs = bsv[U];  // uniform
+    if (gi == 0) cs = bsv[U];  // uniform
     f4 ag[2][2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) ag[m][0] = ag[m][1] = f4{0.f, 0.f, 0.f, 0.f};
@@ -284,30 +303,50 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
       acc[m][0] += ag[m][0] * s0;
       acc[m][1] += ag[m][1] * s1;
     }
-    if (g == NG - 1) {
-      // item done: lane holds D[token 16m + 4q + r][row n] of both weight sub-tiles
-      const int nt = it - se * ntn;
-      const int cnt = s.count[se - se0], off = s.offset[se - se0];
-      const bool shared = s.slot[se - se0] < 0;  // uniform
-      _Float16* hout = reinterpret_cast<_Float16*>(shared ? a.shared_h : a.hbuf);
-      float* yout = shared ? a.shared_y : a.ybuf;
+    if (gi == NGW - 1) {
+      // item done: the second K half hands its sums to the first (the first
+      // barrier keeps the buffer until the last item's sums have been read)
+      if constexpr (KS == 2) {
+        __syncthreads();
+        if (kh == 1) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+          for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tr = 16 * m + 4 * q + r;
-          if (tr < cnt) {
-            const int64_t pos = off + tr;
-            if (MODE == 0) {
-              const int row = nt * ROWS + wv * 16 + n;
-              const float gv = acc[m][0][r], uv = acc[m][1][r];
-              hout[pos * a.I + row] = (_Float16)swiglu(gv, uv);
-            } else {
+            for (int j = 0; j < 2; ++j) s.red[wr][2 * m + j][lane] = acc[m][j];
+        }
+        __syncthreads();
+        if (kh == 0) {
 #pragma unroll
-              for (int j = 0; j < 2; ++j) yout[pos * a.H + nt * ROWS + wv * 32 + j * 16 + n] = acc[m][j][r];
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[m][j] += s.red[wr][2 * m + j][lane];
+        }
+      }
+      if (kh == 0) {
+        // lane holds D[token 16m + 4q + r][row n] of both weight sub-tiles
+        const int nt = it - se * ntn;
+        const int cnt = s.count[se - se0], off = s.offset[se - se0];
+        const bool shared = s.slot[se - se0] < 0;  // uniform
+        _Float16* hout = reinterpret_cast<_Float16*>(shared ? a.shared_h : a.hbuf);
+        float* yout = shared ? a.shared_y : a.ybuf;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tr = 16 * m + 4 * q + r;
+            if (tr < cnt) {
+              const int64_t pos = off + tr;
+              if (MODE == 0) {
+                const int row = nt * ROWS + wr * 16 + n;
+                const float gv = acc[m][0][r], uv = acc[m][1][r];
+                hout[pos * a.I + row] = (_Float16)swiglu(gv, uv);
+              } else {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) yout[pos * a.H + nt * ROWS + wr * 32 + j * 16 + n] = acc[m][j][r];
+              }
             }
           }
-        }
+      }
 #pragma unroll
       for (int m = 0; m < 2; ++m) acc[m][0] = acc[m][1] = f4{0.f, 0.f, 0.f, 0.f};
     }
@@ -320,7 +359,8 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
 }
 
 bool stream_supported(int mode, int K, int rows) {
-  const int per_item = mode == 0 ? kSW * 16 : kSW * 32;
+  const int ks = K == 1024 ? k_halves<1024>() : K == 512 ? k_halves<512>() : k_halves<2048>();
+  const int per_item = mode == 0 ? kSW / ks * 16 : kSW / ks * 32;
   if (rows % per_item) return false;
   return mode == 0 ? K == 2048 : (K == 1024 || K == 512);
 }
