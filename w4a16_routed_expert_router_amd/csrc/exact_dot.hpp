@@ -92,6 +92,47 @@ __device__ inline float exact_dot_wave(const uint16_t* a, const uint16_t* b, int
 
 
 
+// Exact partial dot product of FP16 rows a, b over [k0, k1) (k0, k1 multiples
+// of 8, 8-element chunks dealt over the lanes), as a 128-bit fixed-point
+// integer in units of 2^-48 summed over the wave: every lane returns it.  Exact
+// partial sums add exactly, so any split of a row over waves gives the same
+// total as exact_dot_wave.
+__device__ inline __int128 exact_partial_wave(const uint16_t* a, const uint16_t* b, int k0, int k1, int lane) {
+  constexpr int kAhead = 4;
+  __int128 acc = 0;
+  for (int kb = k0 + lane * 8; kb < k1; kb += kAhead * kWave * 8) {
+    uint4 av[kAhead], bv[kAhead];
+#pragma unroll
+    for (int c = 0; c < kAhead; ++c) {
+      const int k = kb + c * kWave * 8;
+      av[c] = k < k1 ? *reinterpret_cast<const uint4*>(a + k) : make_uint4(0u, 0u, 0u, 0u);
+      bv[c] = k < k1 ? ldg_u4(b + k) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int c = 0; c < kAhead; ++c) {
+      const uint32_t aw[4] = {av[c].x, av[c].y, av[c].z, av[c].w};
+      const uint32_t bw[4] = {bv[c].x, bv[c].y, bv[c].z, bv[c].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int32_t ma, sa, mb, sb;
+        f16_fixed((uint16_t)(aw[i >> 1] >> (16 * (i & 1))), ma, sa);
+        f16_fixed((uint16_t)(bw[i >> 1] >> (16 * (i & 1))), mb, sb);
+        acc += ((__int128)(ma * mb)) << (sa + sb);  // a zero chunk adds zero
+      }
+    }
+  }
+  uint64_t lo = (uint64_t)acc;
+  int64_t hi = (int64_t)(acc >> 64);
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const uint64_t lo2 = __shfl_xor(lo, o, kWave);
+    const int64_t hi2 = __shfl_xor(hi, o, kWave);
+    const uint64_t nlo = lo + lo2;
+    hi = hi + hi2 + (nlo < lo ? 1 : 0);
+    lo = nlo;
+  }
+  return (((__int128)hi) << 64) | (__int128)lo;
+}
+
 // exact_dot_wave with one chunk of each row in flight and no unrolling: the
 // same exact sum (so the same result) for a caller with little register room,
 // where the exact tier is a rare fallback.
@@ -124,74 +165,6 @@ __device__ inline float exact_dot_wave_lean(const uint16_t* a, const uint16_t* b
   }
   const __int128 S = (((__int128)hi) << 64) | (__int128)lo;
   return round_i128_to_f32(S, -48);
-}
-
-// Compensated tier between the FP64 sum and the exact one.  Each product is
-// exact in FP64; they are added with TwoSum (Knuth), which returns the rounded
-// sum and its exact rounding error, the errors being summed separately, first
-// within a lane and then over the lanes' tree.  The pair (s, c) then differs
-// from the exact sum only by the rounding of the error sum: at most
-// (depth + 2) 2^-53 * sum|e| with sum|e| <= (H + 64) 2^-53 * S (one error
-// per product and per tree addition, each at most half an ulp of a partial
-// sum bounded by S), where S bounds
-// sum |x_i w_i| (the caller's `S`).  The FP32 rounding of s + c is returned
-// with *ok set when the exact sum, so bounded, lies strictly inside that
-// value's rounding interval; every lane returns the same result.
-__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
-  s = a + b;
-  const double bp = s - a;
-  e = (a - (s - bp)) + (b - bp);
-}
-__device__ inline float compensated_dot_wave(const uint16_t* a, const uint16_t* b, int H, int lane, double S,
-                                             bool* ok) {
-  constexpr int kAhead = 4;
-  double s = 0.0, c = 0.0;
-  int n_local = 0;
-  for (int k0 = lane * 8; k0 < H; k0 += kAhead * kWave * 8) {
-    uint4 av[kAhead], bv[kAhead];
-#pragma unroll
-    for (int q = 0; q < kAhead; ++q) {
-      const int k = k0 + q * kWave * 8;
-      av[q] = k < H ? *reinterpret_cast<const uint4*>(a + k) : make_uint4(0u, 0u, 0u, 0u);
-      bv[q] = k < H ? ldg_u4(b + k) : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int q = 0; q < kAhead; ++q) {
-      const uint32_t aw[4] = {av[q].x, av[q].y, av[q].z, av[q].w};
-      const uint32_t bw[4] = {bv[q].x, bv[q].y, bv[q].z, bv[q].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double x = (double)half_bits_to_float((uint16_t)(aw[i >> 1] >> (16 * (i & 1))));
-        const double y = (double)half_bits_to_float((uint16_t)(bw[i >> 1] >> (16 * (i & 1))));
-        double e;
-        two_sum(s, x * y, s, e);  // x * y exact: 22 significant bits
-        c += e;
-      }
-    }
-    n_local += kAhead * 8;
-  }
-  // xor butterfly: every lane ends with the same (s, c)
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const double s2 = __shfl_xor(s, o, kWave);
-    const double c2 = __shfl_xor(c, o, kWave);
-    double e;
-    two_sum(s, s2, s, e);
-    c = (c + c2) + e;
-  }
-  const int depth = n_local + 2 * 6;  // additions any error term went through
-  const double eps = (double)(depth + 2) * 0x1p-53 * ((double)(H + 64) * 0x1p-53 * S) * (1.0 + 0x1p-20);
-  const double sd = s + c;
-  const float r = (float)sd;
-  *ok = false;
-  if (r != 0.0f && isfinite(r) && isfinite(sd)) {
-    const double rd = (double)r;
-    const double m_lo = 0.5 * (rd + (double)nextafterf(r, -INFINITY));
-    const double m_hi = 0.5 * (rd + (double)nextafterf(r, INFINITY));
-    // distances to the midpoints, each off by a few roundings of itself at
-    // most: demand twice the bound
-    *ok = ((s - m_lo) + c) > 2.0 * eps && ((m_hi - s) - c) > 2.0 * eps;
-  }
-  return r;
 }
 
 }  // namespace moe

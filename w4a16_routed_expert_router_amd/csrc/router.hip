@@ -10,20 +10,29 @@
 // real dot product of the FP16 inputs, so the selected experts do not depend on
 // summation order.  It is reached in two tiers:
 //   1. every FP16 x FP16 product is exact in FP32 (and FP64); products are
-//      summed in FP64 together with a bound on sum |p| (the sum itself, or the
-//      product of the two rows' norms), which bounds the FP64 error; the FP64
-//      sum is rounded to FP32 and accepted when the whole error interval
+//      summed in FP64 together with S = sum |p|.  Every product, and so every
+//      partial sum, is an integer multiple of 2^-48, and every partial sum is
+//      at most S in magnitude: with S below 2^5 = 2^53 * 2^-48 no FP64
+//      addition rounds, the FP64 sum is the exact sum and its FP32 rounding is
+//      the logit (kExactSumBound).  Otherwise S bounds the FP64 error, and the
+//      FP32 rounding of the FP64 sum is accepted when the whole error interval
 //      rounds to the same FP32 value (it lies strictly between that value's
 //      two rounding midpoints).  Shapes with a multiple of 16 experts run this
 //      tier on the FP64 matrix cores;
-//   2. otherwise (about one logit in 10^6) the wave recomputes the sum exactly
-//      as a 128-bit fixed-point integer (unit 2^-48) and rounds it once.
+//   2. otherwise the sum is recomputed exactly as a 128-bit fixed-point
+//      integer (unit 2^-48) and rounded once.
 #include "common.hpp"
 #include "launch.hpp"
 #include "exact_dot.hpp"
 #include "topk_wave.hpp"
 
 namespace moe {
+
+// Below this S = sum |x_i w_i| an FP64 sum of FP16 products is exact (every
+// partial sum is a multiple of 2^-48 and below 2^5 in magnitude).  Had the
+// exact S reached 2^5, a computed S (relative error below 2^-16) would exceed
+// 2^5 (1 - 2^-16), so the computed S is tested against 31.
+constexpr double kExactSumBound = 31.0;
 
 constexpr int kRtTok = 4;  // tokens per logits work item
 constexpr int kRtExp = 4;  // experts per logits work item
@@ -107,11 +116,11 @@ __global__ __launch_bounds__(64) void router_logits_kernel(const uint16_t* __res
     const int depth = 8 * ((H + 511) / 512) + 6;
     const double eps = (double)(depth + 2) * 0x1p-52 * asum;
     const float r = (float)s;  // round to nearest even
-    if (r != 0.0f && isfinite(r) && isfinite(s)) {
+    if (r != 0.0f && isfinite(r) && isfinite(s) && isfinite(asum)) {
       const double rd = (double)r;
       const double m_lo = 0.5 * (rd + (double)nextafterf(r, -INFINITY));
       const double m_hi = 0.5 * (rd + (double)nextafterf(r, INFINITY));
-      if (s - eps > m_lo && s + eps < m_hi) {
+      if (asum < kExactSumBound || (s - eps > m_lo && s + eps < m_hi)) {
         certified = true;
         logits[(int64_t)t * E + e] = r;
       }
@@ -250,38 +259,47 @@ __global__ __launch_bounds__(64) void router_topk_kernel(const float* __restrict
 // lane group q for both operands, so A and B see the same permutation of K
 // and the tile is the plain dot product.  The four wave tiles are added in
 // LDS in wave order and written as the block's FP64 partial, together with
-// the squared norms of the token and expert rows over the same K range.
+// the partial of |x_i| |w_i| (FP16 matrix cores, FP32 accumulation: every
+// product is exact and every rounding of these positive sums is below 2^-24
+// of the sum, so the partial is within a relative 2^-16 of the exact one).
 //
-// router_select_kernel (one block per token, one wave per 64 experts): adds the partials of the K
-// blocks in order and certifies each logit.  Every rounding has an error of at
-// most 2^-53 of the sum it produces, which is at most the sum of |x_i w_i| over
-// that sum's terms.  A wave's two chains (one per product parity) take at most
-// KR / 2 roundings each over disjoint terms, so together at most
-// KR / 2 * 2^-53 * S_wave (S_wave: the sum of |x_i w_i| over the wave's K
-// range); the addition of the two chains, 3 additions in the block and KB - 1
-// over the K blocks add at most (1 + 3 + KB - 1) * 2^-53 * S, so the error is
-// below (KR / 2 + KB + 3) * 2^-53 * S (one more unit covers the second-order
-// growth of the partial sums), with S = sum |x_i w_i| <= |x| |w| by
-// Cauchy-Schwarz, from the squared norms (their own relative error, below
-// H * 2^-53, is covered by the factor 1 + 2^-20).  The logit is certified when
-// the interval of half-width (KR / 2 + KB + 4) * 2^-53 * |x| |w| around the
-// FP64 sum lies strictly between the rounding midpoints of its FP32 rounding
-// (a logit near zero, whose rounding step is small next to |x| |w|, is the
-// usual case that fails); the wave recomputes the others
-// with compensated FP64 sums (certified the same way against a bound about
-// 2^-52 times smaller) and, where that still fails (an exact sum on or next
-// to a midpoint), exactly.  Softmax and top-k follow.
+// router_select_kernel (one block per token, one wave per 64 experts, at
+// least 4 waves): adds the partials of the K blocks in order and certifies
+// each logit with S = sum |x_i w_i| (the added |x| |w| partials):
+//   * every FP16 value is an integer multiple of 2^-24, so every product is
+//     one of 2^-48, and so is every partial sum.  While a partial sum stays
+//     below 2^53 * 2^-48 = 2^5 in magnitude it is representable in FP64, so
+//     no addition rounds; every partial sum of either chain is bounded by the
+//     sum of |x_i w_i| over its terms.  So when S < 2^5 both FP64 sums are
+//     exact, and the FP32 rounding of the logit's sum is the logit
+//     (kExactSumBound).
+//   * otherwise every rounding has an error of at most 2^-53 of the sum it
+//     produces, which is at most the sum of |x_i w_i| over that sum's terms.
+//     A wave's two chains (one per product parity) take at most KR / 2
+//     roundings each over disjoint terms, so together at most
+//     KR / 2 * 2^-53 * S_wave (S_wave: the sum of |x_i w_i| over the wave's K
+//     range); the addition of the two chains, 3 additions in the block and
+//     KB - 1 over the K blocks add at most (1 + 3 + KB - 1) * 2^-53 * S, so
+//     the error is below (KR / 2 + KB + 3) * 2^-53 * S (one more unit covers
+//     the second-order growth of the partial sums; the factor 1 + 2^-12 covers
+//     the error of the computed S).  The logit is certified when the interval of
+//     half-width (KR / 2 + KB + 4) * 2^-53 * S around the FP64 sum lies
+//     strictly between the rounding midpoints of its FP32 rounding.
+// The block's waves then compute each logit that neither test certifies
+// exactly, every wave the 128-bit fixed-point sum of one K slice, added
+// exactly and rounded once.  Softmax and top-k follow.
 typedef double d4 __attribute__((ext_vector_type(4)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 constexpr int kRmTile = 16;  // tokens and experts per MFMA tile
 constexpr int kRmWaves = 4;  // K parts per block
 constexpr int kRmMaxKB = 8;  // K blocks
 
 template <int KR>
 __global__ __launch_bounds__(kRmWaves * kWave) void router_partial_kernel(RouterArgs a, double* __restrict__ part,
-                                                                          double* __restrict__ nrm_x,
-                                                                          double* __restrict__ nrm_w) {
+                                                                          double* __restrict__ pabs) {
   __shared__ double sp[kRmWaves][kRmTile * kRmTile];
-  __shared__ double sn[kRmWaves][2 * kRmTile];  // token norms, then expert norms
+  __shared__ double sa[kRmWaves][kRmTile * kRmTile];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, q = lane >> 4;
   const int T = a.T, E = a.E, H = a.H;
@@ -299,7 +317,10 @@ __global__ __launch_bounds__(kRmWaves * kWave) void router_partial_kernel(Router
   }
   // two independent accumulation chains (even and odd e), added at the end
   d4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
-  double sx = 0.0, sw = 0.0;
+  // sum of |x| |w| on the FP16 matrix cores (lane (r, q) holds K 32c + 8q + e
+  // of token row r and expert row r, which is the A and B fragment layout of
+  // v_mfma_f32_16x16x32_f16; subnormal inputs are kept)
+  f4v sab = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const uint32_t au[4] = {av[c].x, av[c].y, av[c].z, av[c].w};
@@ -308,104 +329,123 @@ __global__ __launch_bounds__(kRmWaves * kWave) void router_partial_kernel(Router
     for (int e = 0; e < 8; ++e) {
       const double xv = (double)half_bits_to_float((uint16_t)(au[e >> 1] >> (16 * (e & 1))));
       const double wvv = (double)half_bits_to_float((uint16_t)(bu[e >> 1] >> (16 * (e & 1))));
-      sx = fma(xv, xv, sx);
-      sw = fma(wvv, wvv, sw);
       if (e & 1)
         acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(xv, wvv, acc1, 0, 0, 0);
       else
         acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(xv, wvv, acc0, 0, 0, 0);
     }
+    const uint4 xa_abs = make_uint4(av[c].x & 0x7fff7fffu, av[c].y & 0x7fff7fffu, av[c].z & 0x7fff7fffu,
+                                    av[c].w & 0x7fff7fffu);
+    const uint4 wb_abs = make_uint4(bv[c].x & 0x7fff7fffu, bv[c].y & 0x7fff7fffu, bv[c].z & 0x7fff7fffu,
+                                    bv[c].w & 0x7fff7fffu);
+    sab = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8v, xa_abs), __builtin_bit_cast(h8v, wb_abs),
+                                                  sab, 0, 0, 0);
   }
   const d4 acc = acc0 + acc1;
-  // squared norms of the wave's K range: sum over the four lane groups
-  sx += __shfl_xor(sx, 16, kWave);
-  sx += __shfl_xor(sx, 32, kWave);
-  sw += __shfl_xor(sw, 16, kWave);
-  sw += __shfl_xor(sw, 32, kWave);
-  if (q == 0) {
-    sn[wv][r] = sx;
-    sn[wv][kRmTile + r] = sw;
-  }
-  // lane holds D[token q + 4i][expert r] (the FP64 layout; the FP16 MFMAs
-  // put rows 4q + i in a lane instead)
+  // lane holds D[token q + 4i][expert r] of the FP64 MFMA and D[token 4q + i]
+  // [expert r] of the FP16 one
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sp[wv][(q + 4 * i) * kRmTile + r] = acc[i];
+  for (int i = 0; i < 4; ++i) {
+    sp[wv][(q + 4 * i) * kRmTile + r] = acc[i];
+    sa[wv][(4 * q + i) * kRmTile + r] = (double)sab[i];
+  }
   __syncthreads();
   // one output per thread: tid = 16 * token + expert
-  {
-    const int ti = tid >> 4, ei = tid & 15;
-    const double s = ((sp[0][tid] + sp[1][tid]) + sp[2][tid]) + sp[3][tid];
-    if (t0 + ti < T) part[((int64_t)kb * T + t0 + ti) * E + e0 + ei] = s;
-  }
-  if (tid < kRmTile) {
-    const double nx = ((sn[0][tid] + sn[1][tid]) + sn[2][tid]) + sn[3][tid];
-    if (blockIdx.x == 0 && t0 + tid < T) nrm_x[(int64_t)kb * T + t0 + tid] = nx;
-  } else if (tid < 2 * kRmTile) {
-    const int i = tid - kRmTile;
-    const double nw = ((sn[0][tid] + sn[1][tid]) + sn[2][tid]) + sn[3][tid];
-    if (blockIdx.y == 0) nrm_w[(int64_t)kb * E + e0 + i] = nw;
+  const int ti = tid >> 4, ei = tid & 15;
+  if (t0 + ti < T) {
+    const int64_t o = ((int64_t)kb * T + t0 + ti) * E + e0 + ei;
+    part[o] = ((sp[0][tid] + sp[1][tid]) + sp[2][tid]) + sp[3][tid];
+    pabs[o] = ((sa[0][tid] + sa[1][tid]) + sa[2][tid]) + sa[3][tid];
   }
 }
 
-// grid T, block 64 * ceil(E / 64): wave w certifies experts 64w .. 64w + 63 of
-// the token, then wave 0 does softmax and top-k over all of them (KV =
-// ceil(E / 64) logits per lane there).
+// grid T, block 64 * max(ceil(E / 64), 4): wave w < KV = ceil(E / 64)
+// certifies experts 64w .. 64w + 63 of the token; the logits it cannot
+// certify are then computed exactly by all waves of the block together (each
+// one K slice, exact integer partial sums added in LDS); then wave 0 does
+// softmax and top-k over all of them (KV logits per lane there).
 template <int KV>
-__global__ __launch_bounds__(KV * 64) void router_select_kernel(RouterArgs a, const double* __restrict__ part,
-                                                                const double* __restrict__ nrm_x,
-                                                                const double* __restrict__ nrm_w, int KB, int KR) {
+constexpr int select_waves() { return KV < 4 ? 4 : KV; }
+template <int KV>
+__global__ __launch_bounds__(select_waves<KV>() * 64) void router_select_kernel(RouterArgs a,
+                                                                              const double* __restrict__ part,
+                                                                              const double* __restrict__ pabs,
+                                                                              int KB, int KR) {
+  constexpr int NW = select_waves<KV>();
   __shared__ float slg[KV * kWave];
   __shared__ TopkScratch<KV> ts;
+  __shared__ uint64_t unc[KV];     // per certifying wave: lanes whose logit was not certified
+  __shared__ uint64_t xlo[NW], xhi[NW];  // exact partial sums of one logit, per wave
   const int t = blockIdx.x, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int T = a.T, E = a.E;
-  const int e = wv * kWave + lane;
-  const int ec = min(e, E - 1);
-  // every partial is loaded before any is added (at most kRmMaxKB of each)
-  double pv[kRmMaxKB], sv[kRmMaxKB], wn[kRmMaxKB];
+  if (wv < KV) {
+    const int e = wv * kWave + lane;
+    const int ec = min(e, E - 1);
+    // every partial is loaded before any is added (at most kRmMaxKB of each)
+    double sv[kRmMaxKB], av[kRmMaxKB];
 #pragma unroll
-  for (int kb = 0; kb < kRmMaxKB; ++kb) {
-    pv[kb] = kb < KB ? nrm_x[(int64_t)kb * T + t] : 0.0;
-    sv[kb] = kb < KB ? part[((int64_t)kb * T + t) * E + ec] : 0.0;
-    wn[kb] = kb < KB ? nrm_w[(int64_t)kb * E + ec] : 0.0;
-  }
-  double nx = 0.0, s = 0.0, nw = 0.0;
+    for (int kb = 0; kb < kRmMaxKB; ++kb) {
+      sv[kb] = kb < KB ? part[((int64_t)kb * T + t) * E + ec] : 0.0;
+      av[kb] = kb < KB ? pabs[((int64_t)kb * T + t) * E + ec] : 0.0;
+    }
+    double s = 0.0, sab = 0.0;
 #pragma unroll
-  for (int kb = 0; kb < kRmMaxKB; ++kb)
-    if (kb < KB) {  // fixed order
-      nx += pv[kb];
-      s += sv[kb];
-      nw += wn[kb];
+    for (int kb = 0; kb < kRmMaxKB; ++kb)
+      if (kb < KB) {  // fixed order
+        s += sv[kb];
+        sab += av[kb];
+      }
+    bool certified = false;
+    if (e < E) {
+      const float rr = (float)s;  // round to nearest even
+      if (rr != 0.0f && isfinite(rr) && isfinite(s) && isfinite(sab)) {
+        if (sab < kExactSumBound) {
+          certified = true;  // the FP64 sum is the exact sum: rr is its FP32 rounding
+        } else {
+          const double eps = (double)(KR / 2 + KB + 4) * 0x1p-53 * (sab * (1.0 + 0x1p-12));
+          const double rd = (double)rr;
+          const double m_lo = 0.5 * (rd + (double)nextafterf(rr, -INFINITY));
+          const double m_hi = 0.5 * (rd + (double)nextafterf(rr, INFINITY));
+          certified = s - eps > m_lo && s + eps < m_hi;
+        }
+      }
+      if (certified) slg[e] = rr;
     }
-  bool certified = false;
-  if (e < E) {
-    const float rr = (float)s;  // round to nearest even
-    if (rr != 0.0f && isfinite(rr) && isfinite(s)) {
-      const double bound = sqrt(nx) * sqrt(nw) * (1.0 + 0x1p-20);
-      const double eps = (double)(KR / 2 + KB + 4) * 0x1p-53 * bound;
-      const double rd = (double)rr;
-      const double m_lo = 0.5 * (rd + (double)nextafterf(rr, -INFINITY));
-      const double m_hi = 0.5 * (rd + (double)nextafterf(rr, INFINITY));
-      certified = s - eps > m_lo && s + eps < m_hi;
-    }
-    if (certified) slg[e] = rr;
-  }
-  // compensated, then exact tier for the wave's logits that were not certified
-  uint64_t m = __ballot(e < E && !certified);
-  const double bnd_x = sqrt(nx);
-  while (m) {
-    const int l = __builtin_ctzll(m);
-    m &= m - 1;
-    const int ee = wv * kWave + l;
-    const double nwe = __shfl(nw, l, kWave);
-    const uint16_t* xr = a.x + (int64_t)t * a.H;
-    const uint16_t* wr = a.wr + (int64_t)ee * a.H;
-    bool ok;
-    float rr = compensated_dot_wave(xr, wr, a.H, lane, bnd_x * sqrt(nwe) * (1.0 + 0x1p-20), &ok);
-    if (!ok) rr = exact_dot_wave(xr, wr, a.H, lane);
-    if (lane == 0) slg[ee] = rr;
+    const uint64_t m = __ballot(e < E && !certified);
+    if (lane == 0) unc[wv] = m;
   }
   __syncthreads();
-  if (e < E) a.logits[(int64_t)t * E + e] = slg[e];
+  // the uncertified logits, one at a time (block-uniform loop): wave w adds
+  // the exact products of its K slice, and thread 0 adds the waves' sums
+  {
+    const int H = a.H;
+    const int ks = ((H / 8 + NW - 1) / NW) * 8;  // K slice per wave (multiple of 8)
+    const int k0 = min(H, wv * ks), k1 = min(H, k0 + ks);
+    const uint16_t* xr = a.x + (int64_t)t * H;
+    for (int w = 0; w < KV; ++w) {
+      uint64_t m = unc[w];
+      while (m) {
+        const int ee = w * kWave + __builtin_ctzll(m);
+        m &= m - 1;
+        const __int128 ps = exact_partial_wave(xr, a.wr + (int64_t)ee * H, k0, k1, lane);
+        if (lane == 0) {
+          xlo[wv] = (uint64_t)ps;
+          xhi[wv] = (uint64_t)(ps >> 64);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          __int128 S = 0;
+          for (int i = 0; i < NW; ++i) S += (__int128)(((unsigned __int128)xhi[i] << 64) | (unsigned __int128)xlo[i]);
+          slg[ee] = round_i128_to_f32(S, -48);
+        }
+        __syncthreads();
+      }
+    }
+  }
+  if (wv < KV) {
+    const int e = wv * kWave + lane;
+    if (e < E) a.logits[(int64_t)t * E + e] = slg[e];
+  }
   if (wv == 0) topk_token<KV>(slg, t, E, a.k, a.renorm, a.forced, a.ids, a.w, a.err, ts, lane);
 }
 
@@ -421,7 +461,7 @@ size_t router_scratch_bytes(int max_tokens, int E, int H) {
   const int kr = mfma_router_kr(H, E);
   if (!kr) return 0;
   const int64_t KB = H / (kRmWaves * kr);
-  return (size_t)(KB * ((int64_t)max_tokens * E + max_tokens + E) * 8);
+  return (size_t)(2 * KB * (int64_t)max_tokens * E * 8);
 }
 
 // Logits + softmax/top-k.  Returns false (nothing launched) when the shape
@@ -431,25 +471,29 @@ bool launch_router(const RouterArgs& a, double* scratch, hipStream_t stream) {
   if (a.exact_always || !kr || !scratch) return false;
   const int KB = a.H / (kRmWaves * kr);
   double* part = scratch;
-  double* nrm_x = part + (int64_t)KB * a.T * a.E;
-  double* nrm_w = nrm_x + (int64_t)KB * a.T;
+  double* pabs = part + (int64_t)KB * a.T * a.E;
   dim3 g(a.E / kRmTile, (a.T + kRmTile - 1) / kRmTile, KB);
   if (kr == 128)
-    hipLaunchKernelGGL((router_partial_kernel<128>), g, dim3(kRmWaves * kWave), 0, stream, a, part, nrm_x, nrm_w);
+    hipLaunchKernelGGL((router_partial_kernel<128>), g, dim3(kRmWaves * kWave), 0, stream, a, part, pabs);
   else
-    hipLaunchKernelGGL((router_partial_kernel<64>), g, dim3(kRmWaves * kWave), 0, stream, a, part, nrm_x, nrm_w);
+    hipLaunchKernelGGL((router_partial_kernel<64>), g, dim3(kRmWaves * kWave), 0, stream, a, part, pabs);
   const int kv = (a.E + kWave - 1) / kWave;
-  const dim3 gs(a.T), bs(kWave * kv);
+  const dim3 gs(a.T);
   if (kv == 1)
-    hipLaunchKernelGGL((router_select_kernel<1>), gs, bs, 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+    hipLaunchKernelGGL((router_select_kernel<1>), gs, dim3(kWave * select_waves<1>()), 0, stream, a, part, pabs, KB,
+                       kr);
   else if (kv == 2)
-    hipLaunchKernelGGL((router_select_kernel<2>), gs, bs, 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+    hipLaunchKernelGGL((router_select_kernel<2>), gs, dim3(kWave * select_waves<2>()), 0, stream, a, part, pabs, KB,
+                       kr);
   else if (kv <= 4)
-    hipLaunchKernelGGL((router_select_kernel<4>), gs, bs, 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+    hipLaunchKernelGGL((router_select_kernel<4>), gs, dim3(kWave * select_waves<4>()), 0, stream, a, part, pabs, KB,
+                       kr);
   else if (kv <= 8)
-    hipLaunchKernelGGL((router_select_kernel<8>), gs, bs, 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+    hipLaunchKernelGGL((router_select_kernel<8>), gs, dim3(kWave * select_waves<8>()), 0, stream, a, part, pabs, KB,
+                       kr);
   else
-    hipLaunchKernelGGL((router_select_kernel<16>), gs, bs, 0, stream, a, part, nrm_x, nrm_w, KB, kr);
+    hipLaunchKernelGGL((router_select_kernel<16>), gs, dim3(kWave * select_waves<16>()), 0, stream, a, part,
+                       pabs, KB, kr);
   return true;
 }
 
