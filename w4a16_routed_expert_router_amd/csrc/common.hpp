@@ -12,6 +12,14 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kGroup = 128;  // INT4 quantisation group along K
 
+// Below this S = sum |x_i w_i| an FP64 sum of FP16 products x_i w_i is exact:
+// every FP16 value is an integer multiple of 2^-24, so every product and every
+// partial sum is one of 2^-48, and a partial sum (at most S in magnitude)
+// below 2^5 = 2^53 * 2^-48 is representable in FP64, so no addition rounds.
+// Had the exact S reached 2^5, a computed S (relative error below 2^-16)
+// would exceed 2^5 (1 - 2^-16), so the computed S is tested against 31.
+constexpr double kExactSumBound = 31.0;
+
 // Device error word bits (see moe_check_device_errors).
 constexpr uint32_t kErrBadId = 1u;
 constexpr uint32_t kErrDupId = 2u;

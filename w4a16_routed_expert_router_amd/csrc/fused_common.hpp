@@ -131,18 +131,20 @@ __device__ __forceinline__ void partial_dot(const _Float16* x, const uint4 (&q)[
   asum = wave_sum(asum);
 }
 
-// Certified rounding: the FP32 rounding of an FP64 sum whose error is at most
+// Certified rounding: an FP64 sum of FP16 products whose sum of magnitudes
+// asum is below kExactSumBound is exact, so its FP32 rounding is the logit;
+// otherwise the FP32 rounding of an FP64 sum whose error is at most
 // (depth + 2) * 2^-52 * asum equals the rounding of the exact sum when the
 // whole error interval lies strictly between the two rounding midpoints of
-// that value.  Returns false when that is not proven.
+// that value.  Returns false when neither is proven.
 __device__ __forceinline__ bool certify(double acc, double asum, int depth, float& out) {
   const double eps = (double)(depth + 2) * 0x1p-52 * asum;
   const float r = (float)acc;
-  if (r != 0.0f && isfinite(r) && isfinite(acc)) {
+  if (r != 0.0f && isfinite(r) && isfinite(acc) && isfinite(asum)) {
     const double rd = (double)r;
     const double m_lo = 0.5 * (rd + (double)nextafterf(r, -INFINITY));
     const double m_hi = 0.5 * (rd + (double)nextafterf(r, INFINITY));
-    if (acc - eps > m_lo && acc + eps < m_hi) {
+    if (asum < kExactSumBound || (acc - eps > m_lo && acc + eps < m_hi)) {
       out = r;
       return true;
     }

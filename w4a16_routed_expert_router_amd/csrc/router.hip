@@ -28,12 +28,6 @@
 
 namespace moe {
 
-// Below this S = sum |x_i w_i| an FP64 sum of FP16 products is exact (every
-// partial sum is a multiple of 2^-48 and below 2^5 in magnitude).  Had the
-// exact S reached 2^5, a computed S (relative error below 2^-16) would exceed
-// 2^5 (1 - 2^-16), so the computed S is tested against 31.
-constexpr double kExactSumBound = 31.0;
-
 constexpr int kRtTok = 4;  // tokens per logits work item
 constexpr int kRtExp = 4;  // experts per logits work item
 constexpr int kCombos = kRtTok * kRtExp;
