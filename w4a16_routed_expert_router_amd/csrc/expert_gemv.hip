@@ -212,50 +212,35 @@ void launch_down_gemv(const ExpertArgs& a, hipStream_t stream) {
 
 // out[t] = sum_j w[t,j] * y[pos_of[t,j]] (+ yshared[t]), summed in rank order
 // in FP32.  grid (ceil(H/1024), T), block 256, 4 columns per thread.
-constexpr int kCombineMaxK = 16;  // largest top-k a context accepts
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.y;
   const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (n >= a.H) return;
-  // every independent load first: the pairs' positions and weights, the
-  // shared expert's row and the residual, then the k expert rows; the sum
-  // runs in rank order afterwards
-  int p[kCombineMaxK];
-  float wj[kCombineMaxK];
-#pragma unroll
-  for (int j = 0; j < kCombineMaxK; ++j)
-    if (j < a.k) {
-      p[j] = a.pos_of[(int64_t)t * a.k + j];
-      wj[j] = a.w[(int64_t)t * a.k + j];
-    }
-  float4 ys = make_float4(0.f, 0.f, 0.f, 0.f), rv = ys;
-  if (a.yshared) ys = *reinterpret_cast<const float4*>(a.yshared + (int64_t)t * a.H + n);
-  if (a.resid) rv = *reinterpret_cast<const float4*>(a.resid + (int64_t)t * a.H + n);
-  float4 y[kCombineMaxK];
-#pragma unroll
-  for (int j = 0; j < kCombineMaxK; ++j)
-    if (j < a.k) y[j] = *reinterpret_cast<const float4*>(a.ybuf + (int64_t)p[j] * a.H + n);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int j = 0; j < kCombineMaxK; ++j)
-    if (j < a.k) {
-      acc.x += wj[j] * y[j].x;
-      acc.y += wj[j] * y[j].y;
-      acc.z += wj[j] * y[j].z;
-      acc.w += wj[j] * y[j].w;
-    }
+  for (int j = 0; j < a.k; ++j) {
+    const int p = a.pos_of[(int64_t)t * a.k + j];
+    const float wj = a.w[(int64_t)t * a.k + j];
+    const float4 y = *reinterpret_cast<const float4*>(a.ybuf + (int64_t)p * a.H + n);
+    acc.x += wj * y.x;
+    acc.y += wj * y.y;
+    acc.z += wj * y.z;
+    acc.w += wj * y.w;
+  }
   if (a.yshared) {
-    acc.x += ys.x;
-    acc.y += ys.y;
-    acc.z += ys.z;
-    acc.w += ys.w;
+    const float4 y = *reinterpret_cast<const float4*>(a.yshared + (int64_t)t * a.H + n);
+    acc.x += y.x;
+    acc.y += y.y;
+    acc.z += y.z;
+    acc.w += y.w;
   }
   if (a.resid) {
-    rv.x += acc.x;
-    rv.y += acc.y;
-    rv.z += acc.z;
-    rv.w += acc.w;
-    *reinterpret_cast<float4*>(a.resid + (int64_t)t * a.H + n) = rv;
+    float4* r = reinterpret_cast<float4*>(a.resid + (int64_t)t * a.H + n);
+    float4 v = *r;
+    v.x += acc.x;
+    v.y += acc.y;
+    v.z += acc.z;
+    v.w += acc.w;
+    *r = v;
   } else {
     _Float16* o = reinterpret_cast<_Float16*>(a.out) + (int64_t)t * a.H + n;
     o[0] = (_Float16)acc.x;
