@@ -171,7 +171,7 @@ struct moe_ctx {
   BlobLayout lay{}, shared_lay{};
   std::vector<LayerState> layers;
   float* logits = nullptr;
-  double* rscratch = nullptr;  // FP64 partial logits and norms of the matrix-core router
+  double* rscratch = nullptr;  // FP64 partial logits and sums of magnitudes of the matrix-core router
   int32_t* ids = nullptr;
   float* w = nullptr;
   int32_t* ids_s = nullptr;
