@@ -590,7 +590,17 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   GroupArgs ga{ids, T, g.top_k, g.n_experts, L.map, sc.ids_s, sc.active, sc.n_active,
                sc.perm_tok, sc.pos_of, c->err, mfma_min, sc.mtile_off,
                sc.active + g.n_experts, sc.n_active + 1, chunk_all ? 1 : 0};
-  {
+  // a shared expert of the routed experts' shape rides along in the streaming
+  // launches as one more list entry (one weight stream over the whole chip
+  // instead of two launches of its own)
+  const bool shared_in_stream = g.shared_inter == g.inter && !all_mfma && stream_gu && stream_dn &&
+                                T <= kStreamTokens;
+  // when every expert takes the streaming kernels, the gate/up kernel groups
+  // the pairs itself where that fits (no grouping launch, and its blocks start
+  // from LDS lists instead of reading them back)
+  const bool group_in_kernel =
+      chunk_all && stream_group_in_kernel_ok(T, g.top_k, g.n_experts, g.inter, c->ncu, shared_in_stream);
+  if (!group_in_kernel) {
     ScopedTimer tm(c, timed, kKindGroup, s);
     launch_group(ga, s);
   }
@@ -613,16 +623,15 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   ea.perm_tok = sc.perm_tok;
   ea.hbuf = sc.hbuf;
   ea.ybuf = sc.ybuf;
-  // a shared expert of the routed experts' shape rides along in the streaming
-  // launches as one more list entry (one weight stream over the whole chip
-  // instead of two launches of its own)
-  const bool shared_in_stream = g.shared_inter == g.inter && !all_mfma && stream_gu && stream_dn &&
-                                T <= kStreamTokens;
   if (shared_in_stream) {
     ea.shared_blob = L.shared;
     ea.shared_count = T;
     ea.shared_h = sc.hshared;
     ea.shared_y = sc.yshared;
+  }
+  if (group_in_kernel) {
+    ea.group_in_kernel = 1;
+    ea.grp = ga;
   }
   if (!all_mfma) {
     ScopedTimer tm(c, timed, kKindGateUp, s);
@@ -644,6 +653,7 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
   }
   if (g.shared_inter && !shared_in_stream) {
     ExpertArgs sa = ea;
+    sa.group_in_kernel = 0;  // one fixed expert: no list
     sa.shared_blob = nullptr;
     sa.lay = c->shared_lay;
     sa.fixed_blob = L.shared;

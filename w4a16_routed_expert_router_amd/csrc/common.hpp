@@ -247,4 +247,26 @@ __device__ __forceinline__ void atomic_or_err(uint32_t* err, uint32_t bits) {
   if (err) atomicOr(err, bits);
 }
 
+constexpr int kMaxTopK = 16;  // largest top-k a context accepts
+
+// Validates the k ids of token t: an id out of range or repeated within the
+// token flags the call (errbits) and the token gets ids 0..k-1 (valid and
+// distinct) instead.
+__device__ __forceinline__ void validate_token(const int (&rv)[kMaxTopK], int k, int E, int (&out)[kMaxTopK],
+                                               uint32_t& errbits) {
+  bool bad = false, dup = false;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k) {
+      bad |= rv[j] < 0 || rv[j] >= E;
+#pragma unroll
+      for (int jj = 0; jj < j; ++jj) dup |= rv[jj] == rv[j];
+    }
+  }
+  if (bad) errbits |= kErrBadId;
+  if (dup) errbits |= kErrDupId;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) out[j] = (bad || dup) ? j : rv[j];
+}
+
 }  // namespace moe

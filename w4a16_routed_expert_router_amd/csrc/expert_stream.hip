@@ -29,6 +29,7 @@
 // MFMA operand layout (gfx950): lane l holds A[l%16][8*(l/16)+e],
 // B[8*(l/16)+e][l%16], D[4*(l/16)+r][l%16]; the K index of step st, lane group
 // q, element e is 128g + 32q + 8st + e for both operands.
+#include <algorithm>
 #include <utility>
 
 #include "common.hpp"
@@ -57,6 +58,8 @@ constexpr int ring_units() { return K == 512 ? 3 : 4; }
 constexpr int kTok = 32;        // tokens per expert handled here (two sub-tiles of 16)
 constexpr int kPad = 8;         // LDS row padding (halves)
 constexpr int kMaxList = 1024;  // experts per call
+constexpr int kBlockEntries = 8;  // list entries a block keeps when it groups the call itself
+constexpr int kGroupScans = 4;    // values scanned over the experts by that grouping
 // K halves per item.  With 2, waves w and w + kSW / 2 take the same rows of
 // an item, each one half of its scale groups, and add their sums in LDS at the
 // item's end: an item is half as many rows, so that the items of a call
@@ -91,9 +94,45 @@ struct StreamSmem {
   int tok[kTok];
   int ns;
   int scan[kSW];
+  int ptok[kBlockEntries][kTok];  // grouping in the kernel: tokens of the block's list entries
 };
 
 }  // namespace
+
+// Exclusive prefix sums of N values per thread over the block (thread order)
+// and their totals.  scratch: N x kSW ints, used once (no barrier after the
+// reads).
+template <int N>
+__device__ __forceinline__ void stream_block_scan(const int (&v)[N], int (&excl)[N], int (&tot)[N], int* scratch) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    incl[i] = wave_incl_scan(v[i]);
+    if (lane == 63) scratch[i * kSW + wv] = incl[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    int pre = 0, t = 0;
+#pragma unroll
+    for (int w = 0; w < kSW; ++w) {
+      const int x = scratch[i * kSW + w];
+      pre += w < wv ? x : 0;
+      t += x;
+    }
+    excl[i] = pre + incl[i] - v[i];
+    tot[i] = t;
+  }
+}
+
+// Bytes of the tile's LDS the in-kernel grouping takes: ids, (64-token chunk,
+// expert) masks and their prefix counts, four per-expert arrays, the scans'
+// scratch.
+__host__ __device__ inline size_t group_in_kernel_bytes(int T, int k, int E) {
+  const size_t P = (size_t)T * k, NC = ((size_t)T + 63) / 64;
+  return ((P * 4 + 7) & ~(size_t)7) + NC * E * 8 + NC * E * 4 + (size_t)E * 4 * 4 + (size_t)kGroupScans * kSW * 4;
+}
 
 // MODE 0: gate/up + SwiGLU (K = H, rows = I, 128 rows per item);
 // MODE 1: down (K = I, rows = H, 256 rows per item).
@@ -118,7 +157,123 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   // along; the block takes a contiguous run of items (expert, row tile) and
   // keeps the list entries of its experts in LDS (slot -1 marks the shared
   // expert)
-  const int nrouted = a.fixed_blob ? 1 : *a.n_small;
+  // With group_in_kernel (gate/up only) every block groups the call's pairs
+  // itself, the same way as the one-pass grouping kernel: ids validated per
+  // token, a bit per (64-token chunk, expert), per-expert counts, offsets and
+  // list entries (chunks of at most kStreamTokens tokens) by block scans; the
+  // arrays live in the activation tile's LDS until the first tile is loaded.
+  // Block 0 writes the grouping's outputs (positions, the permutation, the
+  // lists and their counts, errors) for the down kernel and the combine.
+  const bool gik = MODE == 0 && a.group_in_kernel;
+  const GroupArgs& g = a.grp;
+  const int gE = g.E, gT = g.T, gk = g.k, gP = gT * gk, gNC = (gT + 63) / 64;
+  uint8_t* gbase = reinterpret_cast<uint8_t*>(s.a);
+  int* gid = reinterpret_cast<int*>(gbase);                                                   // [P]
+  unsigned long long* gmask = reinterpret_cast<unsigned long long*>(gbase + ((gP * 4 + 7) & ~7));  // [NC][E]
+  int* gcum = reinterpret_cast<int*>(gmask + gNC * gE);  // [NC][E]: the expert's pairs in earlier chunks
+  int* ecnt = gcum + gNC * gE;
+  int* eoff = ecnt + gE;
+  int* esidx = eoff + gE;
+  int* eslot = esidx + gE;
+  int* escan = eslot + gE;  // [kGroupScans][kSW]
+  const int ept = (gE + kSW * kWave - 1) / (kSW * kWave);  // experts per thread (contiguous)
+  int nrouted;
+  if (gik) {
+    int slot_pre[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid * ept + i;
+      slot_pre[i] = (i < ept && e < gE && g.slot_map) ? g.slot_map[e] : e;
+    }
+    for (int i = tid; i < gNC * gE; i += kSW * kWave) gmask[i] = 0ull;
+    for (int p = tid; p < gP; p += kSW * kWave) gid[p] = g.ids_in[p];
+    __syncthreads();
+    uint32_t errbits = 0;
+    for (int t = tid; t < gT; t += kSW * kWave) {
+      int rv[kMaxTopK], v[kMaxTopK];
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) rv[j] = j < gk ? gid[t * gk + j] : -1;
+      validate_token(rv, gk, gE, v, errbits);
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (j >= gk) break;
+        gid[t * gk + j] = v[j];
+        atomicOr(&gmask[(t >> 6) * gE + v[j]], 1ull << (t & 63));
+      }
+    }
+    __syncthreads();
+    int c[2] = {0, 0}, vs[kGroupScans] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid * ept + i;
+      if (i < ept && e < gE) {
+        int cc = 0;
+        for (int ch = 0; ch < gNC; ++ch) {
+          gcum[ch * gE + e] = cc;
+          cc += __popcll(gmask[ch * gE + e]);
+        }
+        c[i] = cc;
+        vs[0] += cc;                                                               // positions
+        vs[1] += cc >= g.mfma_min ? (cc + kMfmaTileTokens - 1) / kMfmaTileTokens : 0;  // MFMA token tiles
+        vs[2] += cc > 0 ? 1 : 0;                                                   // active experts
+        vs[3] += (cc + kStreamTokens - 1) / kStreamTokens;                         // list entries
+      }
+    }
+    int ex[kGroupScans], tt[kGroupScans];
+    stream_block_scan<kGroupScans>(vs, ex, tt, escan);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid * ept + i;
+      if (i < ept && e < gE) {
+        const int cc = c[i];
+        int slot = 0;
+        if (cc > 0) {
+          slot = slot_pre[i];
+          if (slot < 0) {
+            errbits |= kErrNotResident;
+            slot = 0;
+          }
+        }
+        ecnt[e] = cc;
+        eoff[e] = ex[0];
+        esidx[e] = ex[3];
+        eslot[e] = slot;
+        if (blockIdx.x == 0) {
+          if (cc > 0) {
+            g.mtile_off[ex[2]] = ex[1];
+            g.active[ex[2]] = ActiveExpert{e, slot, cc, ex[0]};
+          }
+          for (int j = 0; j * kStreamTokens < cc; ++j)
+            g.small[ex[3] + j] =
+                ActiveExpert{e, slot, min(kStreamTokens, cc - j * kStreamTokens), ex[0] + j * kStreamTokens};
+        }
+        ex[0] += cc;
+        ex[1] += cc >= g.mfma_min ? (cc + kMfmaTileTokens - 1) / kMfmaTileTokens : 0;
+        ex[2] += cc > 0 ? 1 : 0;
+        ex[3] += (cc + kStreamTokens - 1) / kStreamTokens;
+      }
+    }
+    if (blockIdx.x == 0) {
+      if (errbits) atomic_or_err(g.err, errbits);
+      if (tid == 0) {
+        g.mtile_off[tt[2]] = tt[1];
+        *g.n_active = tt[2];
+        *g.n_small = tt[3];
+      }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int p = tid; p < gP; p += kSW * kWave) {
+        const int e = gid[p], t = p / gk, ch = t >> 6, tl = t & 63;
+        const int pos = eoff[e] + gcum[ch * gE + e] + __popcll(gmask[ch * gE + e] & ((1ull << tl) - 1ull));
+        g.perm_tok[pos] = t;
+        g.pos_of[p] = pos;
+      }
+    }
+    nrouted = tt[3];
+  } else {
+    nrouted = a.fixed_blob ? 1 : *a.n_small;
+  }
   const int ns = nrouted + (a.shared_blob ? 1 : 0);
   const int items = ns * ntn;
   const int per = (items + gridDim.x - 1) / gridDim.x;
@@ -127,7 +282,36 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
   if (lo >= hi) return;  // uniform over the block
   const int nv = (hi - lo) * NGW;  // units of every wave
   const int se0 = lo / ntn;       // first expert of the block (list index)
-  if (tid <= (hi - 1) / ntn - se0) {
+  if (gik) {
+    // the block's list entries (at most kBlockEntries) and their tokens
+    const int ne = (hi - 1) / ntn - se0 + 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid * ept + i;
+      if (i < ept && e < gE) {
+        const int cc = ecnt[e];
+        for (int j = 0; j * kStreamTokens < cc; ++j) {
+          const int idx = esidx[e] + j - se0;
+          if (idx >= 0 && idx < ne) {
+            s.slot[idx] = eslot[e];
+            s.count[idx] = min(kStreamTokens, cc - j * kStreamTokens);
+            s.offset[idx] = eoff[e] + j * kStreamTokens;
+          }
+        }
+      }
+    }
+    if (tid == 0 && a.shared_blob && nrouted - se0 >= 0 && nrouted - se0 < ne) {
+      s.slot[nrouted - se0] = -1;
+      s.count[nrouted - se0] = a.shared_count;
+      s.offset[nrouted - se0] = 0;
+    }
+    for (int p = tid; p < gP; p += kSW * kWave) {
+      const int e = gid[p], t = p / gk, ch = t >> 6, tl = t & 63;
+      const int r = gcum[ch * gE + e] + __popcll(gmask[ch * gE + e] & ((1ull << tl) - 1ull));
+      const int idx = esidx[e] + r / kStreamTokens - se0;
+      if (idx >= 0 && idx < ne) s.ptok[idx][r % kStreamTokens] = t;
+    }
+  } else if (tid <= (hi - 1) / ntn - se0) {
     if (a.fixed_blob) {
       s.slot[0] = 0;
       s.count[0] = a.fixed_count;
@@ -202,7 +386,11 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
     const bool shared = s.slot[se - se0] < 0;  // uniform
     if (tid < kTok) {
       int v = -1;
-      if (tid < cnt) v = (a.fixed_blob || shared) ? tid : (MODE == 0 ? a.perm_tok[off + tid] : off + tid);
+      if (tid < cnt)
+        v = (a.fixed_blob || shared) ? tid
+            : MODE == 1              ? off + tid
+            : gik                    ? s.ptok[se - se0][tid]
+                                     : a.perm_tok[off + tid];
       s.tok[tid] = v;
     }
     __syncthreads();
@@ -356,6 +544,20 @@ __global__ __launch_bounds__(kSW * kWave) void stream_expert_kernel(ExpertArgs a
       (step(v0 + Us, std::integral_constant<int, Us>{}), ...);
     }(std::make_integer_sequence<int, kRing>{});
   }
+}
+
+bool stream_group_in_kernel_ok(int T, int k, int E, int I, int grid, bool shared_rides) {
+  if (E > 2 * kSW * kWave || T <= 0) return false;
+  if (group_in_kernel_bytes(T, k, E) > sizeof(StreamSmem<2048>::a)) return false;
+  // list entries: every active expert in chunks of kStreamTokens tokens, at
+  // most min(E, P) + P / kStreamTokens of them, plus the shared expert; a run
+  // of `per` consecutive items spans at most ceil(per / ntn) + 1 entries
+  const int64_t P = (int64_t)T * k;
+  const int ntn = I / (kSW / k_halves<2048>() * 16);
+  if (ntn <= 0) return false;
+  const int64_t ns = std::min<int64_t>(E, P) + P / kStreamTokens + (shared_rides ? 1 : 0);
+  const int64_t per = (ns * ntn + grid - 1) / grid;
+  return (per + ntn - 1) / ntn + 1 <= kBlockEntries;
 }
 
 bool stream_supported(int mode, int K, int rows) {

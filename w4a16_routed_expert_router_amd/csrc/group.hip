@@ -15,7 +15,6 @@ constexpr int kGroupThreads = 1024;
 constexpr int kMaxExperts = 1024;
 constexpr int kChunk = 64;  // tokens per stable-placement round
 constexpr int kLdsPairs = 16384;  // validated ids are kept in LDS up to this many pairs
-constexpr int kMaxK = 16;         // largest top-k a context accepts
 constexpr int kRounds = 4;        // placement chunks per round at most
 
 // Exclusive prefix sums of N values per thread over the block (1024 threads =
@@ -49,26 +48,6 @@ __device__ void block_exclusive_scan(const int (&v)[N], int (&excl)[N], int (&to
     total[i] = sh_tot[i];
   }
   __syncthreads();
-}
-
-// Validates the k ids of token t: an id out of range or repeated within the
-// token flags the call (errbits) and the token gets ids 0..k-1 (valid and
-// distinct) instead.
-__device__ __forceinline__ void validate_token(const int (&rv)[kMaxK], int k, int E, int (&out)[kMaxK],
-                                               uint32_t& errbits) {
-  bool bad = false, dup = false;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k) {
-      bad |= rv[j] < 0 || rv[j] >= E;
-#pragma unroll
-      for (int jj = 0; jj < j; ++jj) dup |= rv[jj] == rv[j];
-    }
-  }
-  if (bad) errbits |= kErrBadId;
-  if (dup) errbits |= kErrDupId;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) out[j] = (bad || dup) ? j : rv[j];
 }
 
 // The call's plan from the per-expert token counts (c of thread e < E):
@@ -152,12 +131,12 @@ __global__ __launch_bounds__(kGroupThreads) void group_onepass_kernel(GroupArgs 
   __syncthreads();
   uint32_t errbits = 0;
   for (int t = tid; t < T; t += kGroupThreads) {
-    int rv[kMaxK], v[kMaxK];
+    int rv[kMaxTopK], v[kMaxTopK];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) rv[j] = j < k ? a.ids_in[(int64_t)t * k + j] : -1;
+    for (int j = 0; j < kMaxTopK; ++j) rv[j] = j < k ? a.ids_in[(int64_t)t * k + j] : -1;
     validate_token(rv, k, E, v, errbits);
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < kMaxTopK; ++j) {
       if (j >= k) break;
       sid[t * k + j] = (int16_t)v[j];
       atomicOr(&mask[(t / kChunk) * E + v[j]], 1ull << (t % kChunk));
@@ -218,13 +197,13 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(GroupArgs a) {
   // validate each token's ids; a bad token gets ids 0..k-1 (valid, distinct)
   uint32_t errbits = 0;
   for (int t = tid; t < T; t += kGroupThreads) {
-    int rv[kMaxK], v[kMaxK];
+    int rv[kMaxTopK], v[kMaxTopK];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
+    for (int j = 0; j < kMaxTopK; ++j)
       rv[j] = j < k ? (lds_ids ? (int)sid[t * k + j] : a.ids_in[(int64_t)t * k + j]) : -1;
     validate_token(rv, k, E, v, errbits);
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < kMaxTopK; ++j) {
       if (j >= k) break;
       if (lds_ids)
         sid[t * k + j] = (int16_t)v[j];

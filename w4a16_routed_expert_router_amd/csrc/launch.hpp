@@ -96,11 +96,22 @@ struct ExpertArgs {
   int shared_count;
   uint16_t* shared_h;         // [T, I] fp16
   float* shared_y;            // [T, H] fp32
+  // streaming gate/up kernel: 1 when every block groups the call's pairs
+  // itself from grp (stream_group_in_kernel_ok), block 0 writing the
+  // grouping's outputs for the later kernels; small / n_small then come from
+  // grp, and no grouping kernel runs
+  int group_in_kernel;
+  GroupArgs grp;
 };
 void launch_gateup_gemv(const ExpertArgs& a, hipStream_t stream);
 // Persistent weight-streaming expert kernel (expert_stream.hip) for experts with
 // at most kStreamTokens tokens (and below mfma_min); mode 0 gate/up, 1 down.
 constexpr int kStreamTokens = 32;
+// Whether a T-token call whose experts all take the streaming kernels can have
+// its pairs grouped inside the gate/up streaming kernel: the ids, bit masks
+// and per-expert lists fit in the kernel's LDS and no block's run of items can
+// span more list entries than it keeps.
+bool stream_group_in_kernel_ok(int T, int k, int E, int I, int grid, bool shared_rides);
 // with at least this many (token, expert) pairs per expert on average (a
 // prefill) every expert takes the grouped GEMM
 constexpr int kPrefillPairsPerExpert = 16;
