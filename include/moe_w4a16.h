@@ -317,6 +317,19 @@ moe_status moe_stack_forward(moe_ctx* ctx, int32_t layer_begin, int32_t layer_en
                              int32_t T, const int32_t* forced_ids, void* x_trace,
                              int32_t* ids_trace, float* w_trace, void* stream);
 
+/* The same residual stack ("Horizon RunMap", "The complete execution path"),
+ * its input read from h_in: h_in (dev FP32 [T,H], read only) is the first
+ * layer's residual and h (dev FP32 [T,H]) receives the result, as if h_in
+ * were copied into h and moe_stack_forward ran on h.  h_in may equal h (then
+ * it is moe_stack_forward); otherwise the two must not overlap
+ * (MOE_E_ARG).  The one-kernel path reads h_in directly (a decode step whose
+ * input sits in its own buffer needs no copy before the call); the per-layer
+ * path copies it into h on `stream` first.  Other arguments, errors and
+ * results as moe_stack_forward. */
+moe_status moe_stack_forward_into(moe_ctx* ctx, int32_t layer_begin, int32_t layer_end, const float* h_in,
+                                  float* h, int32_t T, const int32_t* forced_ids, void* x_trace,
+                                  int32_t* ids_trace, float* w_trace, void* stream);
+
 /* Synchronises `stream`, reads and clears the device error word.  Returns
  * MOE_OK if it was zero, else MOE_E_DEVICE with *bits (if non-NULL) set:
  * 1 = expert id out of range, 2 = expert repeated within a token,

@@ -124,9 +124,10 @@ def test_olmoe_stack_whole_call_equals_layer_by_layer(moe, T):
 
 
 def test_olmoe_stack_graph_replay_equals_direct_launch(moe):
-    """The benchmarked form -- batch 1, all 16 layers in one launch, replayed
-    from a captured HIP graph -- gives the same bits as a direct launch, on
-    every replay, with other work and synchronisations between replays."""
+    """The benchmarked form -- batch 1, all 16 layers in one launch reading the
+    input residual from its own buffer, replayed from a captured HIP graph --
+    gives the same bits as a direct in-place launch, on every replay, with other
+    work and synchronisations between replays."""
     say("test_olmoe_stack_graph_replay_equals_direct_launch")
     shape, L = fx.OLMOE, 16
     layers = stack_weights(shape, "stack-olmoe", L)
@@ -139,13 +140,13 @@ def test_olmoe_stack_graph_replay_equals_direct_launch(moe):
     src = h0s[0].clone()
     torch.cuda.synchronize()
     with torch.cuda.stream(s):
-        h.copy_(src)
-        ctx.stack_forward(h, stream=s)       # warm the path before capture
+        ctx.stack_forward(h, h_in=src, stream=s)       # warm the path before capture
     s.synchronize()
+    # the step as the bench times it: the stack reads the input residual from
+    # its own buffer (moe_stack_forward_into), one kernel per replay
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        h.copy_(src)
-        ctx.stack_forward(h, stream=s)
+        ctx.stack_forward(h, h_in=src, stream=s)
     for rep in range(6):
         i = rep % 3
         with torch.cuda.stream(s):
@@ -158,6 +159,37 @@ def test_olmoe_stack_graph_replay_equals_direct_launch(moe):
         assert torch.equal(got, ref), f"replay {rep} differs from a direct launch"
         torch.cuda.synchronize()
     assert ctx.check_device_errors(s) == 0
+    ctx.close()
+
+
+@pytest.mark.parametrize("T", [1, 2, 8])
+def test_stack_forward_into_equals_in_place(moe, T):
+    """moe_stack_forward_into (input residual in its own buffer) gives the bits
+    of moe_stack_forward on a copy, leaves the input untouched, accepts the
+    input as the output, and refuses partly overlapping buffers; T = 1 and 2
+    run the one-kernel path, T = 8 the per-layer kernels."""
+    say(f"test_stack_forward_into_equals_in_place T={T}")
+    shape, L = fx.OLMOE, 4
+    layers = stack_weights(shape, "stack-olmoe", 16)[:L]
+    ctx = make_ctx(moe, shape, layers, T)
+    h0 = torch.from_numpy(fx.activations(("into", T), T, shape.hidden).numpy().astype(np.float32)).cuda()
+    keep = h0.clone()
+    ref = h0.clone()
+    ctx.stack_forward(ref)
+    out = torch.full_like(h0, float("nan"))
+    ctx.stack_forward(out, h_in=h0)
+    same = h0.clone()
+    ctx.stack_forward(same, h_in=same)
+    torch.cuda.synchronize()
+    assert torch.equal(h0, keep)
+    assert torch.equal(out, ref)
+    assert torch.equal(same, ref)
+    if T > 1:
+        buf = torch.zeros((T + 1, shape.hidden), dtype=torch.float32, device="cuda")
+        with pytest.raises(moe.MoEError) as ei:
+            ctx.stack_forward(buf[1:], h_in=buf[:T])
+        assert ei.value.status == moe.capi.MOE_E_ARG
+    assert ctx.check_device_errors() == 0
     ctx.close()
 
 

@@ -145,8 +145,10 @@ class MoEContext:
         return out
 
     def stack_forward(self, h, layer_begin=0, layer_end=None, forced_ids=None, trace=False,
-                      stream=None):
-        """h: FP32 [T,H] CUDA tensor, updated in place.  forced_ids: int32 [L,T,k].
+                      stream=None, h_in=None):
+        """h: FP32 [T,H] CUDA tensor, updated in place; with h_in (FP32 [T,H],
+        read only) the stack starts from h_in and h receives the result
+        (moe_stack_forward_into).  forced_ids: int32 [L,T,k].
         With trace=True returns (x [L,T,H] fp16, ids [L,T,k], w [L,T,k])."""
         sh = self.shape
         T = h.shape[0]
@@ -159,12 +161,16 @@ class MoEContext:
             xs = torch.zeros((L, T, sh.hidden), dtype=torch.float16, device=h.device)
             ids = torch.full((L, T, sh.top_k), -1, dtype=torch.int32, device=h.device)
             ws = torch.zeros((L, T, sh.top_k), dtype=torch.float32, device=h.device)
-        self._check(_lib.moe_stack_forward(
-            self._h, layer_begin, layer_end, hp, T, fp,
-            None if xs is None else C.c_void_p(xs.data_ptr()),
-            None if ids is None else C.c_void_p(ids.data_ptr()),
-            None if ws is None else C.c_void_p(ws.data_ptr()),
-            _stream(stream, self.device)))
+        traces = (None if xs is None else C.c_void_p(xs.data_ptr()),
+                  None if ids is None else C.c_void_p(ids.data_ptr()),
+                  None if ws is None else C.c_void_p(ws.data_ptr()))
+        if h_in is None:
+            self._check(_lib.moe_stack_forward(self._h, layer_begin, layer_end, hp, T, fp, *traces,
+                                               _stream(stream, self.device)))
+        else:
+            hi = _dev(h_in, torch.float32, (T, sh.hidden), self.device, "h_in")
+            self._check(_lib.moe_stack_forward_into(self._h, layer_begin, layer_end, hi, hp, T, fp, *traces,
+                                                    _stream(stream, self.device)))
         return (xs, ids, ws) if trace else None
 
     def check_device_errors(self, stream=None):

@@ -71,6 +71,7 @@ SIGNATURES = {
     "moe_expert_forward": (_I, [_P, _I, _P, _I, _P, _P, _P, _P]),
     "moe_expert_forward_noalloc": (_I, [_P, _I, _P, _I, _P, _P, _P, _P]),
     "moe_stack_forward": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
+    "moe_stack_forward_into": (_I, [_P, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P]),
     "moe_check_device_errors": (_I, [_P, _P, C.POINTER(C.c_uint32)]),
     "moe_cache_ensure": (_I, [_P, _I, _P, _I, _P, _I, _P]),
     "moe_cache_prefetch": (_I, [_P, _I, _P, _I, _I, _P]),

@@ -994,9 +994,10 @@ static moe_status moe_expert_forward_noalloc_call(moe_ctx* c, int32_t layer, con
                      false);
 }
 
+// h_in: the first layer's input residual when it is not h (else null).
 static moe_status moe_stack_forward_call(moe_ctx* c, int32_t layer_begin, int32_t layer_end, float* h, int32_t T,
                              const int32_t* forced_ids, void* x_trace, int32_t* ids_trace,
-                             float* w_trace, void* stream) {
+                             float* w_trace, void* stream, const float* h_in = nullptr) {
   if (moe_status st = check_ctx(c)) return st;
   const moe_config& g = c->cfg;
   if (layer_begin < 0 || layer_end > g.n_layers || layer_begin >= layer_end)
@@ -1031,6 +1032,7 @@ static moe_status moe_stack_forward_call(moe_ctx* c, int32_t layer_begin, int32_
       while (fa.lg_sub < 4 && T * g.n_experts * fa.lg_sub * 2 <= waves) fa.lg_sub *= 2;
     }
     fa.h = h;
+    fa.h_in = h_in;
     fa.xh = c->xh;
     fa.xlg = c->xlg;
     fa.xhb = c->xhb;
@@ -1071,6 +1073,7 @@ static moe_status moe_stack_forward_call(moe_ctx* c, int32_t layer_begin, int32_
       for (int l = layer_begin; l < layer_end; ++l) HIPCHK(c, hipEventRecord(c->layers[l].retired, s));
     return MOE_OK;
   }
+  if (h_in) HIPCHK(c, hipMemcpyAsync(h, h_in, (size_t)th * sizeof(float), hipMemcpyDeviceToDevice, s));
   for (int l = layer_begin; l < layer_end; ++l) {
     uint16_t* x = x_trace ? (uint16_t*)x_trace + l * th : c->xbuf;
     int32_t* ids = ids_trace ? ids_trace + l * tk : c->ids;
@@ -1545,6 +1548,24 @@ moe_status moe_stack_forward(moe_ctx* c, int32_t layer_begin, int32_t layer_end,
   moe_status st = moe_stack_forward_call(c, layer_begin, layer_end, h, T, forced_ids, x_trace, ids_trace, w_trace, stream);
   if (st == MOE_OK && c) st = pool_order_end(c, (hipStream_t)stream);
   return sync_each_call(c, stream, st, "moe_stack_forward");
+}
+
+moe_status moe_stack_forward_into(moe_ctx* c, int32_t layer_begin, int32_t layer_end, const float* h_in,
+                                  float* h, int32_t T, const int32_t* forced_ids, void* x_trace,
+                                  int32_t* ids_trace, float* w_trace, void* stream) {
+  if (!h_in) return c ? fail(c, MOE_E_ARG, "h_in is required") : MOE_E_ARG;
+  if (c && !c->faulted) {
+    if (h_in != h && c->cfg.hidden > 0 && T > 0) {
+      const uintptr_t a0 = (uintptr_t)h_in, b0 = (uintptr_t)h;
+      const uintptr_t n = (uintptr_t)T * (uintptr_t)c->cfg.hidden * sizeof(float);
+      if (a0 < b0 + n && b0 < a0 + n) return fail(c, MOE_E_ARG, "h_in and h overlap without being equal");
+    }
+    if (moe_status st = pool_order_begin(c, (hipStream_t)stream)) return st;
+  }
+  moe_status st = moe_stack_forward_call(c, layer_begin, layer_end, h, T, forced_ids, x_trace, ids_trace, w_trace,
+                                         stream, h_in == h ? nullptr : h_in);
+  if (st == MOE_OK && c) st = pool_order_end(c, (hipStream_t)stream);
+  return sync_each_call(c, stream, st, "moe_stack_forward_into");
 }
 
 moe_status moe_cache_ensure(moe_ctx* c, int32_t layer, const int32_t* experts, int32_t n,

@@ -145,7 +145,8 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
 
     // ---------------- E1: residual -> RMSNorm -> x in LDS ----------------
     if (li == 0) {
-      for (int i = tid; i < T * H; i += kFT) s.u.hfull[i] = a.h[i];
+      const float* hin = a.h_in ? a.h_in : a.h;
+      for (int i = tid; i < T * H; i += kFT) s.u.hfull[i] = hin[i];
     } else {
       read_tagged(a.xh + (int64_t)(li & 1) * kFMaxT * H, T * H, tag - 1u, bail,
                   [&](int i, uint32_t v) { s.u.hfull[i] = __builtin_bit_cast(float, v); });

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kFT) void spec_decode_kernel(FusedArgs a) {
 
       // ---------------- E1: residual -> RMSNorm -> x ----------------
       if (li == 0) {
-        for (int i = tid; i < H; i += kPT) s.u.hfull[i] = a.h[i];
+        for (int i = tid; i < H; i += kPT) s.u.hfull[i] = (a.h_in ? a.h_in : a.h)[i];
       } else {
         // the staging buffer also holds the previous layer's intermediates:
         // every weight wave has finished its down projection

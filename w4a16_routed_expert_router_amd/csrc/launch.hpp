@@ -158,6 +158,7 @@ struct FusedArgs {
   BlobLayout lay;             // routed and shared blobs (shared inter == inter)
   int64_t blob_stride;
   float* h;                   // [T,H] residual, updated in place
+  const float* h_in;          // [T,H] the first layer's input residual (null: h)
   uint64_t* xh;               // [2][kFMaxT][H] tagged residual exchange
   uint64_t* xlg;              // [kFLogitReps][kFMaxTE] tagged logits
   uint64_t* xhb;              // [kFStageHalves/2] tagged FP16 pairs of intermediates
