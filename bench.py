@@ -214,13 +214,11 @@ def extra_single_layer(moe, fx, dev, stream, reps=100):
         ids, w = ctx.route(r, x, stream=stream)
         ctx.expert_forward(r, x, ids, w, out=out, stream=stream)
 
-    h.copy_(h0)
-
     def fused(i):
-        # the residual is updated in place from call to call (the timed region
-        # holds only the layer's launch; resetting it would add a copy kernel)
+        # the layer reads the input residual from its own buffer and writes h
+        # (moe_stack_forward_into: the timed region holds only the launch)
         r = i % N_REPLICAS
-        ctx.stack_forward(h, layer_begin=r, layer_end=r + 1, stream=stream)
+        ctx.stack_forward(h, layer_begin=r, layer_end=r + 1, h_in=h0, stream=stream)
 
     res = {"tokens": T, "experts_touched_mean": used, "bytes_per_call": int(nbytes), "flops_per_call": flops}
     for name, fn in (("layer_calls", layer_api), ("one_launch", fused)):
@@ -322,8 +320,7 @@ def extra_qwen(moe, fx, dev, stream, n_sets=8, n_layers=48, reps=50):
         nbytes = sum(u * shape.blob_bytes + blob_shared + router_b + 2 * T * shape.hidden * 4 for u in distinct)
 
         def step(i):
-            h.copy_(h0)
-            ctx.stack_forward(h, stream=stream)
+            ctx.stack_forward(h, h_in=h0, stream=stream)
 
         for i in range(5):
             step(i)

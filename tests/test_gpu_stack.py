@@ -180,10 +180,16 @@ def test_stack_forward_into_equals_in_place(moe, T):
     ctx.stack_forward(out, h_in=h0)
     same = h0.clone()
     ctx.stack_forward(same, h_in=same)
+    # one layer (the one-kernel path then skips its in-place read gate)
+    ref1 = h0.clone()
+    ctx.stack_forward(ref1, 1, 2)
+    out1 = torch.full_like(h0, float("nan"))
+    ctx.stack_forward(out1, 1, 2, h_in=h0)
     torch.cuda.synchronize()
     assert torch.equal(h0, keep)
     assert torch.equal(out, ref)
     assert torch.equal(same, ref)
+    assert torch.equal(out1, ref1)
     if T > 1:
         buf = torch.zeros((T + 1, shape.hidden), dtype=torch.float32, device="cuda")
         with pytest.raises(moe.MoEError) as ei:

@@ -152,9 +152,9 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
                   [&](int i, uint32_t v) { s.u.hfull[i] = __builtin_bit_cast(float, v); });
     }
     bail = block_any(bail);
-    // single-layer call: announce that this block has read the caller's
-    // residual (its loads have returned: their values are in LDS)
-    if (li == 0 && a.l1 - a.l0 == 1 && tid == 0) st_tag(a.xgate + b, tag, 0u);
+    // single-layer call in place: announce that this block has read the
+    // caller's residual (its loads have returned: their values are in LDS)
+    if (li == 0 && a.l1 - a.l0 == 1 && !a.h_in && tid == 0) st_tag(a.xgate + b, tag, 0u);
     if (tid < T * kFRows) s.hown[tid / kFRows][tid % kFRows] = s.u.hfull[(tid / kFRows) * H + r0 + tid % kFRows];
     for (int t = 0; t < T; ++t) {
       float ss = 0.0f;
@@ -794,9 +794,9 @@ __global__ __launch_bounds__(kFT) void fused_decode_kernel(FusedArgs a) {
 
     // ---------------- rank-ordered combine, residual update, E1 publication ----------------
     const bool last = l + 1 == a.l1;
-    if (last && li == 0) {
-      // single-layer call: the caller's residual is overwritten only after
-      // every block has read it
+    if (last && li == 0 && !a.h_in) {
+      // single-layer call in place: the caller's residual is overwritten only
+      // after every block has read it
       read_tagged(a.xgate, kFGrid, tag, bail, [&](int, uint32_t) {});
       bail = block_any(bail);
     }

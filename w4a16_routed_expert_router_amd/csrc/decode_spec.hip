@@ -224,8 +224,8 @@ __global__ __launch_bounds__(kFT) void spec_decode_kernel(FusedArgs a) {
         if (lane == 0) s.part[wv] = ss;
       }
       pbar(lane);
-      // single-layer call: announce that this block has read the caller's residual
-      if (li == 0 && a.l1 - a.l0 == 1 && tid == 0) st_tag(a.xgate + b, tag, 0u);
+      // single-layer call in place: announce that this block has read the caller's residual
+      if (li == 0 && a.l1 - a.l0 == 1 && !a.h_in && tid == 0) st_tag(a.xgate + b, tag, 0u);
       if (tid < kFRows) s.hown[tid] = s.u.hfull[r0 + tid];
       {
         float tot = 0.0f;
@@ -367,9 +367,9 @@ __global__ __launch_bounds__(kFT) void spec_decode_kernel(FusedArgs a) {
           if (!flag_wait(&s.f_down[w], l, &s.bailf, false)) bail = true;
         stamp(s, a, l, 8);
         const bool last = !has_next;
-        if (last && li == 0) {
-          // single-layer call: the caller's residual is overwritten only
-          // after every block has read it
+        if (last && li == 0 && !a.h_in) {
+          // single-layer call in place: the caller's residual is overwritten
+          // only after every block has read it
           read_tagged_n<kWave, kFGrid / kWave>(a.xgate, kFGrid, tag, bail, lane, [&](int, uint32_t) {});
         }
         const int ks = ((UU + 1) / 2 <= kFW / 2 && I >= 512) ? 2 : 1;
