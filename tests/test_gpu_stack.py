@@ -238,6 +238,36 @@ def test_olmoe_stack_free_running_vs_oracle(moe, T):
         ctx.close()
 
 
+@pytest.mark.parametrize("case", ["olmoe-8", "qwen-16"])
+def test_per_layer_stack_norm_from_combine_sums(moe, case):
+    """In a call over several layers on the per-layer kernels, every layer after
+    the first forms x in the router's partial-logit kernel from the residual and
+    the sums of squares the previous combine left.  The residual before layer l
+    is observable as the output of the call over the first l layers (calls are
+    deterministic, so the longer call computes the same residual); the longer
+    call's traced x_l must be within 1 FP16 ulp of the oracle's RMSNorm of it,
+    and its ids the oracle's routing of that x."""
+    say(f"test_per_layer_stack_norm_from_combine_sums {case}")
+    shape, T, L = (fx.OLMOE, 8, 4) if case == "olmoe-8" else (fx.QWEN_NEXT, 16, 3)
+    layers = stack_weights(shape, "stack-olmoe" if case == "olmoe-8" else "stack-qwen", 16 if case == "olmoe-8" else 8)[:L]
+    ctx = make_ctx(moe, shape, layers, T)
+    h0 = torch.from_numpy(fx.activations(("norm-sums", case), T, shape.hidden).numpy().astype(np.float32)).cuda()
+    for l in range(1, L):
+        hl = h0.clone()
+        ctx.stack_forward(hl, 0, l)
+        h = h0.clone()
+        xs, ids, _ = ctx.stack_forward(h, 0, l + 1, trace=True)
+        torch.cuda.synchronize()
+        x = xs[l].cpu().numpy()
+        xr = ora.rmsnorm_fp16(hl.cpu().numpy().astype(np.float64))
+        ulp = np.abs(x.astype(np.float32) - xr.astype(np.float32)) / np.spacing(np.abs(xr).astype(np.float16)).astype(np.float32)
+        assert ulp.max() <= 1.0, (l, ulp.max())
+        own, _, _ = ora.route(x, layers[l]["router"], shape.top_k, shape.renorm)
+        np.testing.assert_array_equal(ids[l].cpu().numpy(), own)
+    assert ctx.check_device_errors() == 0
+    ctx.close()
+
+
 @pytest.mark.parametrize("T", [1, 4])
 def test_qwen_stack_decode_teacher_forced(moe, T):
     """Qwen3-Next-style layers (512 experts, top-10 renormalised, shared expert),

@@ -185,6 +185,7 @@ struct moe_ctx {
   float* ybuf = nullptr;
   float* yshared = nullptr;
   uint16_t* xbuf = nullptr;
+  float* ssq = nullptr;        // [max_tokens][ceil(H/1024)] residual sums of squares (per-layer stack)
   uint32_t* err = nullptr;
   hipStream_t side = nullptr;
   int copy_delay_us = 0;       // test hook: wait before every host-to-device blob copy
@@ -561,7 +562,7 @@ size_t carve_scratch(const moe_config& g, int T, uint8_t* base, ExpertScratch* o
 // creates on first use); the allocation-free entry point passes false.
 moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const int32_t* ids,
                        const float* w, uint16_t* out, float* resid, hipStream_t s,
-                       const ExpertScratch& sc, bool timed = true) {
+                       const ExpertScratch& sc, bool timed = true, float* ssq = nullptr) {
   LayerState& L = c->layers[layer];
   const moe_config& g = c->cfg;
 
@@ -670,7 +671,7 @@ moe_status run_experts(moe_ctx* c, int layer, const uint16_t* x, int T, const in
     else launch_down_gemv(sa, s);
   }
   CombineArgs ca{sc.ybuf, g.shared_inter ? sc.yshared : nullptr, sc.pos_of, w, T, g.top_k,
-                 g.hidden, out, resid};
+                 g.hidden, out, resid, ssq};
   {
     ScopedTimer tm(c, timed, kKindCombine, s);
     launch_combine(ca, s);
@@ -808,6 +809,7 @@ moe_status moe_create(const moe_config* cfg, moe_ctx** out) {
   }
   ok = ok && dalloc((void**)&c->ybuf, (size_t)P * g.hidden * 4);
   ok = ok && dalloc((void**)&c->xbuf, (size_t)g.max_tokens * g.hidden * 2);
+  ok = ok && dalloc((void**)&c->ssq, (size_t)g.max_tokens * ((g.hidden + 1023) / 1024) * sizeof(float));
   ok = ok && dalloc((void**)&c->err, 4);
   if (g.shared_inter) {
     ok = ok && dalloc((void**)&c->hshared, (size_t)g.max_tokens * g.shared_inter * 2);
@@ -879,7 +881,7 @@ void moe_destroy(moe_ctx* c) {
     }
   }
   void* bufs[] = {c->logits, c->rscratch, c->ids,  c->w,    c->ids_s,   c->active,  c->n_active, c->perm_tok,
-                  c->pos_of, c->hbuf, c->ybuf, c->xbuf,    c->err,     c->hshared,  c->yshared,
+                  c->pos_of, c->hbuf, c->ybuf, c->xbuf,    c->ssq,     c->err,      c->hshared,  c->yshared,
                   c->dlayers, c->mtile_off, c->xh, c->xlg, c->xhb, c->xgate, c->epoch,
                   c->pool_x, c->pool_ids, c->pool_w, c->pool_gids, c->pool_cids};
   for (void* p : bufs) (void)hipFree(p);
@@ -1074,19 +1076,33 @@ static moe_status moe_stack_forward_call(moe_ctx* c, int32_t layer_begin, int32_
     return MOE_OK;
   }
   if (h_in) HIPCHK(c, hipMemcpyAsync(h, h_in, (size_t)th * sizeof(float), hipMemcpyDeviceToDevice, s));
+  // after the first layer, the combine leaves the residual's sums of squares
+  // and the matrix-core router's partial-logit kernel forms x itself (no
+  // RMSNorm launch)
+  const int exact_always = (int)(g.flags & MOE_FLAG_ROUTER_EXACT_ALWAYS);
+  const bool norm_in_router = router_takes_mfma(g.hidden, g.n_experts, exact_always);
+  const int nssq = (g.hidden + 1023) / 1024;
   for (int l = layer_begin; l < layer_end; ++l) {
     uint16_t* x = x_trace ? (uint16_t*)x_trace + l * th : c->xbuf;
     int32_t* ids = ids_trace ? ids_trace + l * tk : c->ids;
     float* w = w_trace ? w_trace + l * tk : c->w;
-    {
+    const bool fused_norm = norm_in_router && l > layer_begin;
+    if (!fused_norm) {
       ScopedTimer tm(c, kKindNorm, s);
       launch_rmsnorm(h, T, g.hidden, 1e-5f, x, s);
     }
     RouterArgs ra{x, c->layers[l].router, T, g.n_experts, g.hidden, g.top_k, g.renorm, c->logits,
-                  forced_ids ? forced_ids + l * tk : nullptr, ids, w, c->err,
-                  (int)(g.flags & MOE_FLAG_ROUTER_EXACT_ALWAYS)};
+                  forced_ids ? forced_ids + l * tk : nullptr, ids, w, c->err, exact_always};
+    if (fused_norm) {
+      ra.hres = h;
+      ra.ssq = c->ssq;
+      ra.nssq = nssq;
+      ra.xw = x;
+    }
     run_router(c, ra, s);
-    if (moe_status st = run_experts(c, l, x, T, ids, w, nullptr, h, s, ctx_scratch(c))) return st;
+    if (moe_status st = run_experts(c, l, x, T, ids, w, nullptr, h, s, ctx_scratch(c), true,
+                                    norm_in_router && l + 1 < layer_end ? c->ssq : nullptr))
+      return st;
   }
   return MOE_OK;
 }

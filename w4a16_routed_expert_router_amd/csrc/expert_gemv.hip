@@ -211,42 +211,54 @@ void launch_down_gemv(const ExpertArgs& a, hipStream_t stream) {
 }
 
 // out[t] = sum_j w[t,j] * y[pos_of[t,j]] (+ yshared[t]), summed in rank order
-// in FP32.  grid (ceil(H/1024), T), block 256, 4 columns per thread.
+// in FP32.  grid (ceil(H/1024), T), block 256, 4 columns per thread.  Stack
+// mode (resid): resid[t] += that, and with ssq each block also writes the sum
+// of squares of its 1024 updated columns (for the next layer's RMSNorm).
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.y;
   const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
-  if (n >= a.H) return;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < a.k; ++j) {
-    const int p = a.pos_of[(int64_t)t * a.k + j];
-    const float wj = a.w[(int64_t)t * a.k + j];
-    const float4 y = *reinterpret_cast<const float4*>(a.ybuf + (int64_t)p * a.H + n);
-    acc.x += wj * y.x;
-    acc.y += wj * y.y;
-    acc.z += wj * y.z;
-    acc.w += wj * y.w;
+  float ss = 0.0f;  // this thread's part of the new residual's sum of squares
+  if (n < a.H) {    // H is a multiple of 256: a wave is wholly in or out
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < a.k; ++j) {
+      const int p = a.pos_of[(int64_t)t * a.k + j];
+      const float wj = a.w[(int64_t)t * a.k + j];
+      const float4 y = *reinterpret_cast<const float4*>(a.ybuf + (int64_t)p * a.H + n);
+      acc.x += wj * y.x;
+      acc.y += wj * y.y;
+      acc.z += wj * y.z;
+      acc.w += wj * y.w;
+    }
+    if (a.yshared) {
+      const float4 y = *reinterpret_cast<const float4*>(a.yshared + (int64_t)t * a.H + n);
+      acc.x += y.x;
+      acc.y += y.y;
+      acc.z += y.z;
+      acc.w += y.w;
+    }
+    if (a.resid) {
+      float4* r = reinterpret_cast<float4*>(a.resid + (int64_t)t * a.H + n);
+      float4 v = *r;
+      v.x += acc.x;
+      v.y += acc.y;
+      v.z += acc.z;
+      v.w += acc.w;
+      *r = v;
+      ss = ((v.x * v.x + v.y * v.y) + v.z * v.z) + v.w * v.w;
+    } else {
+      _Float16* o = reinterpret_cast<_Float16*>(a.out) + (int64_t)t * a.H + n;
+      o[0] = (_Float16)acc.x;
+      o[1] = (_Float16)acc.y;
+      o[2] = (_Float16)acc.z;
+      o[3] = (_Float16)acc.w;
+    }
   }
-  if (a.yshared) {
-    const float4 y = *reinterpret_cast<const float4*>(a.yshared + (int64_t)t * a.H + n);
-    acc.x += y.x;
-    acc.y += y.y;
-    acc.z += y.z;
-    acc.w += y.w;
-  }
-  if (a.resid) {
-    float4* r = reinterpret_cast<float4*>(a.resid + (int64_t)t * a.H + n);
-    float4 v = *r;
-    v.x += acc.x;
-    v.y += acc.y;
-    v.z += acc.z;
-    v.w += acc.w;
-    *r = v;
-  } else {
-    _Float16* o = reinterpret_cast<_Float16*>(a.out) + (int64_t)t * a.H + n;
-    o[0] = (_Float16)acc.x;
-    o[1] = (_Float16)acc.y;
-    o[2] = (_Float16)acc.z;
-    o[3] = (_Float16)acc.w;
+  if (a.ssq) {  // uniform
+    __shared__ float part[4];
+    ss = wave_sum_xor(ss, kWave);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) a.ssq[(int64_t)t * gridDim.x + blockIdx.x] = (part[0] + part[1]) + (part[2] + part[3]);
   }
 }
 

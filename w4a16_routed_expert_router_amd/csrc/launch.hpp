@@ -18,12 +18,22 @@ struct RouterArgs {
   float* w;               // [T,k] out
   uint32_t* err;
   int exact_always;
+  // stack layers after the first, on the matrix-core router: x is formed in
+  // the partial-logit kernel as fp16(RMSNorm(hres)) from the residual's sums
+  // of squares ssq ([T][nssq] blocks of it, written by the previous layer's
+  // combine) and written to xw (= x); hres null: x is given
+  const float* hres;
+  const float* ssq;
+  int nssq;
+  uint16_t* xw;
 };
 void launch_router_logits(const RouterArgs& a, hipStream_t stream);
 // logits + softmax/top-k on the FP64 matrix cores, using `scratch` of
 // router_scratch_bytes(); returns false, launching nothing, when the shape or
 // the flags do not take that path (then launch_router_logits + _topk)
 bool launch_router(const RouterArgs& a, double* scratch, hipStream_t stream);
+// whether launch_router takes the matrix-core path for this shape and flag
+bool router_takes_mfma(int H, int E, int exact_always);
 size_t router_scratch_bytes(int max_tokens, int E, int H);
 void launch_router_topk(const RouterArgs& a, hipStream_t stream);
 
@@ -127,6 +137,9 @@ struct CombineArgs {
   int T, k, H;
   uint16_t* out;              // [T,H] fp16 (if resid == null)
   float* resid;               // [T,H] fp32: resid += combined (stack mode)
+  // stack mode: [T][ceil(H/1024)] sums of squares of the updated residual,
+  // one per block of 1024 columns (for the next layer's RMSNorm), or null
+  float* ssq;
 };
 void launch_combine(const CombineArgs& a, hipStream_t stream);
 

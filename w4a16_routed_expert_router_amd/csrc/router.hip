@@ -304,10 +304,41 @@ __global__ __launch_bounds__(kRmWaves * kWave) void router_partial_kernel(Router
   const uint16_t* wb = a.wr + (int64_t)(e0 + r) * H + k0 + 8 * q;
   constexpr int NC = KR / 32;  // 32-wide K chunks, all loaded up front
   uint4 av[NC], bv[NC];
+  if (a.hres) {
+    // x = fp16(RMSNorm(h)) of the lane's chunks, from the residual and its
+    // sums of squares; the blocks of expert tile 0 write x for the later
+    // kernels (every (token, K chunk) once)
+    const float* hr = a.hres + (int64_t)tr * H + k0 + 8 * q;
+    float4 hv[NC][2];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    av[c] = *reinterpret_cast<const uint4*>(xa + 32 * c);
-    bv[c] = ldg_u4(wb + 32 * c);
+    for (int c = 0; c < NC; ++c) {
+      hv[c][0] = *reinterpret_cast<const float4*>(hr + 32 * c);
+      hv[c][1] = *reinterpret_cast<const float4*>(hr + 32 * c + 4);
+      bv[c] = ldg_u4(wb + 32 * c);
+    }
+    float tot = 0.0f;
+    for (int i = 0; i < a.nssq; ++i) tot += a.ssq[(int64_t)tr * a.nssq + i];
+    const float rr = 1.0f / sqrtf(tot / (float)H + 1e-5f);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const float f[8] = {hv[c][0].x, hv[c][0].y, hv[c][0].z, hv[c][0].w,
+                          hv[c][1].x, hv[c][1].y, hv[c][1].z, hv[c][1].w};
+      uint32_t w4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const _Float16 lo = (_Float16)(f[2 * e] * rr), hi = (_Float16)(f[2 * e + 1] * rr);
+        w4[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      av[c] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      if (blockIdx.x == 0 && t0 + r < T)
+        *reinterpret_cast<uint4*>(a.xw + (int64_t)tr * H + k0 + 8 * q + 32 * c) = av[c];
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      av[c] = *reinterpret_cast<const uint4*>(xa + 32 * c);
+      bv[c] = ldg_u4(wb + 32 * c);
+    }
   }
   // two independent accumulation chains (even and odd e), added at the end
   d4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
@@ -457,6 +488,8 @@ size_t router_scratch_bytes(int max_tokens, int E, int H) {
   const int64_t KB = H / (kRmWaves * kr);
   return (size_t)(2 * KB * (int64_t)max_tokens * E * 8);
 }
+
+bool router_takes_mfma(int H, int E, int exact_always) { return !exact_always && mfma_router_kr(H, E) != 0; }
 
 // Logits + softmax/top-k.  Returns false (nothing launched) when the shape
 // does not take the matrix-core router.
