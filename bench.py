@@ -33,9 +33,9 @@ REL_L2_TOL = 2e-3    # layer-output tolerance, applied to the final residual
 # the kernel sources they were taken on (sha256 prefixes below); a changed
 # kernel reports traffic = null until the counters are taken again.
 COUNTED_TRAFFIC = {
-    "bytes": 460_548_824,
-    "sources": {"decode_fused.hip": "b5955115a673ce4a", "common.hpp": "f2de7d1c2d57c861",
-                "launch.hpp": "563606838230d76d", "fused_common.hpp": "a23f31d44a7efb9f",
+    "bytes": 460_588_992,
+    "sources": {"decode_fused.hip": "f3ac3570b7aa0ff2", "common.hpp": "bbd12f2f5f254678",
+                "launch.hpp": "3d80c9ff07a13432", "fused_common.hpp": "a23f31d44a7efb9f",
                 "exact_dot.hpp": "dd7ddc2f23467800", "topk_wave.hpp": "d6d1cd76583c6732"},
 }
 
